@@ -1,0 +1,108 @@
+"""Pins for oracle/formats.py: e4m3fn, int4 and bf16 decoding."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats
+
+
+def test_e4m3_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = formats.e4m3_to_f32(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_e4m3_closed_form_points():
+    v = formats.e4m3_to_f32(np.array([0x7E, 0x01, 0x07, 0x08, 0x38, 0xB8, 0x00, 0x80, 0x40], np.uint8))
+    assert v[0] == 448.0                       # largest finite: 1.75 * 2^8
+    assert v[1] == 2.0 ** -9                   # smallest subnormal
+    assert v[2] == 7 * 2.0 ** -9
+    assert v[3] == 2.0 ** -6                   # smallest normal
+    assert v[4] == 1.0 and v[5] == -1.0
+    assert v[6] == 0.0 and np.signbit(v[7])
+    assert v[8] == 2.0
+
+
+def test_e4m3_encoder_roundtrip_and_vs_torch():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = formats.e4m3_to_f32(codes)
+    assert np.array_equal(synth.e4m3_from_f32(vals), codes)
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(100000) * 60).astype(np.float32)
+    x = np.clip(x, -440, 440)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(synth.e4m3_from_f32(x), ref)
+
+
+def test_f16_encoder_vs_numpy():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(50000).astype(np.float32) * s for s in (1e-6, 1e-3, 1.0, 1e3, 1e5)])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(synth.f16_from_f32(x), ref)
+
+
+def test_bf16_decode_vs_torch():
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 65536, 10000, dtype=np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]        # finite only
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(formats.bf16_to_f32(bits), ref)
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -1.0 - 2 ** -8], np.float32)
+    got = formats.bf16_to_f32(synth.round_bf16(x))
+    assert np.array_equal(got, np.array([1.0, 1.0 + 2 ** -6, 1.0, -1.0], np.float32))
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_int4_unpack_vs_bit_extraction():
+    rng = np.random.default_rng(4)
+    qp = rng.integers(0, 256, (3, 64), dtype=np.uint8)
+    q = formats.unpack_int4(qp)
+    for r in range(3):
+        for c in range(128):
+            byte = int(qp[r, c // 2])
+            nib = (byte >> (4 * (c % 2))) & 0xF
+            assert q[r, c] == nib
+
+
+def test_int4_dequant_error_within_half_step():
+    wl = synth.workload("decode_int4_k26_b4", hidden=256, inter=128)
+    f13, f2 = synth.expert_draws(wl.hidden, wl.inter, 0, 1)
+    q13, q2, s13, s2 = synth.expert_tensors(wl, 0, 1)
+    for f, q, s in ((f13, q13, s13), (f2, q2, s2)):
+        w = formats.dequant_int4_g128(q, s)
+        step = np.repeat(formats.f16_to_f32(s), 128, axis=1)
+        assert np.all(np.abs(w - f) <= step / 2 * (1 + 1e-6))
+        assert formats.unpack_int4(q).min() >= 1        # symmetric: -8 is never used
+
+
+def test_fp8_dequant_error_within_rounding():
+    wl = synth.workload("decode_fp8_k40_b4", hidden=256, inter=128)
+    f13, f2 = synth.expert_draws(wl.hidden, wl.inter, 0, 1)
+    q13, q2, s13, s2 = synth.expert_tensors(wl, 0, 1)
+    for f, q, s in ((f13, q13, s13), (f2, q2, s2)):
+        w = formats.dequant_fp8_b128(q, s)
+        sc = np.repeat(np.repeat(s, 128, 0), 128, 1)
+        # e4m3 keeps 3 mantissa bits: relative error <= 2^-4 for normals, absolute <= 2^-10*s below 2^-6
+        assert np.all(np.abs(w - f) <= np.maximum(np.abs(f) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6))
+        # every block's largest magnitude maps to 448
+        blk = np.abs(formats.e4m3_to_f32(q)).reshape(q.shape[0] // 128, 128, q.shape[1] // 128, 128).max(axis=(1, 3))
+        assert np.all(blk == 448.0)
+
+
+def test_dequant_expert_shapes():
+    for name in ("decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4"):
+        wl = synth.workload(name, hidden=256, inter=128)
+        w13, w2 = formats.dequant_expert(wl.wtype, *synth.expert_tensors(wl, 1, 2))
+        assert w13.shape == (256, 256) and w2.shape == (256, 128)
+        assert w13.dtype == np.float32
+        assert 0.015 < w13.std() < 0.025
