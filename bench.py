@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Paged-MoE decode benchmark on one MI355X.
+
+A step is one decode token batch through every MoE layer of the workload
+(48 layers, E=128, top-8 by default): per layer the device LRU planner, the
+page-in of missing experts from pinned host memory, the SwiGLU expert GEMVs
+and the fixed-order top-k sum.  Device-planned workloads (tokens x top_k <= K)
+are captured as one hipGraph per step (48 layers) and replayed; host-planned
+workloads run eagerly.  Inputs (hidden states, routed ids and weights of every
+step) are resident in HBM before the timed region; the timed region starts
+from an empty slot table (pe_reset_lru) so the roofline covers the same
+window.
+
+Output: one JSON line with tok/s, the HBM + host-link roofline of the window
+(D*S / 8 TB/s + M*S / measured link rate, D and M counted by the library),
+the page-in kernel's achieved link rate, the gate/up GEMV's HBM rate, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PCIE5_X16_GBS = 32.0 * 16 * 128 / 130 / 8   # 63.0 GB/s per direction
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="decode_bf16_k40_b1")
+    ap.add_argument("--cpu-samples", type=int, default=None, help="decode steps the CPU oracle runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing-pass", action="store_true")
+    ap.add_argument("--dma", action="store_true", help="host-planned page-in with hipMemcpyAsync")
+    ap.add_argument("--repeats", type=int, default=2, help="timed repetitions (best and median reported)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this method keeps its slot tables and LRU state on one GPU, "
+              "and multi-GPU runs are out of scope; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import harness
+    import synth
+    import host_paged_expert_amd as pe
+
+    base = synth.WORKLOADS[args.workload]
+    steps = args.steps or base.steps
+    warmup = max(0, args.warmup)
+    wl = synth.workload(args.workload, steps=max(steps, warmup, base.steps))
+    dev = "cuda:0"
+    torch.cuda.init()
+    flags = pe.PE_FLAG_PAGEIN_DMA if args.dma else 0
+    captured = wl.batch * wl.top_k <= wl.resident
+
+    t0 = time.time()
+    m = harness.make_moe(wl, flags=flags)
+    log("context: %d layers x %d experts, K=%d, %s; pinned store ready in %.1fs" %
+        (wl.layers, wl.experts, wl.resident, wl.wtype, time.time() - t0))
+    t0 = time.time()
+    harness.load_store(m, wl, progress=wl.layers * wl.experts // 8)
+    log("host store filled in %.1fs" % (time.time() - t0))
+
+    link_dma = pe.pe_link_probe(m.ctx, 1 << 30, 0, 5)
+    link_kernel = pe.pe_link_probe(m.ctx, 1 << 30, 1, 5)
+    link = max(link_dma, link_kernel)
+    log("host->device link: DMA %.2f GB/s, mapped-read kernel %.2f GB/s" % (link_dma, link_kernel))
+
+    routing = synth.routing_for(wl)
+    x_all, ids_all, w_all = harness.decode_inputs(wl, routing, dev)
+    L, B, H = wl.layers, wl.batch, wl.hidden
+    out = torch.empty((L, B, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    graph = None
+    sidx = torch.zeros(1, dtype=torch.long, device=dev)
+    if captured:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                xs = torch.index_select(x_all, 0, sidx)[0]
+                ids_s = torch.index_select(ids_all, 0, sidx)[0]
+                w_s = torch.index_select(w_all, 0, sidx)[0]
+                cs = torch.cuda.current_stream()
+                for l in range(L):
+                    m.forward(l, xs, ids_s[l], w_s[l], out[l], stream=cs)
+                sidx.add_(1)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        log("captured one %d-layer decode step as a hipGraph" % L)
+
+    def run(n):
+        if captured:
+            for _ in range(n):
+                graph.replay()
+        else:
+            for s in range(n):
+                for l in range(L):
+                    m.forward(l, x_all[s], ids_all[s, l], w_all[s, l], out[l], stream=stream)
+
+    def cold():
+        torch.cuda.synchronize()
+        m.reset_lru(-1, stream)
+        sidx.zero_()
+        torch.cuda.synchronize()
+        m.reset_stats()
+
+    # warm-up (untimed), then timed repetitions from a cold slot table
+    cold()
+    run(warmup)
+    torch.cuda.synchronize()
+    times = []
+    stats = None
+    for rep in range(max(1, args.repeats)):
+        cold()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        run(steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        times.append(ms)
+        st = m.stats()
+        if stats is None:
+            stats = st
+        elif st["page_ins"] != stats["page_ins"] or st["distinct"] != stats["distinct"]:
+            raise RuntimeError("repetitions planned differently: %r vs %r" % (st, stats))
+        log("rep %d: %d steps in %.1f ms (%.2f tok/s), %d page-ins, %d distinct" %
+            (rep, steps, ms, steps * B / (ms / 1e3), st["page_ins"], st["distinct"]))
+    best_ms = min(times)
+    med_ms = sorted(times)[len(times) // 2]
+    value = steps * B / (best_ms / 1e3)
+
+    S_alg, S_copy = pe.pe_expert_bytes(wl.wtype, wl.hidden, wl.inter)
+    D, M = stats["distinct"], stats["page_ins"]
+    t_roof = D * S_alg / (HBM_PEAK_GBS * 1e9) + M * S_alg / (link * 1e9)
+    roof_tok_s = steps * B / t_roof
+
+    # Per-kernel timing pass: the same window, eager, each stage bracketed by hipEvents.
+    kernel = {}
+    sample_steps = []
+    samples = {}
+    if not args.no_cpu_baseline:
+        n_samp = args.cpu_samples or (4 if B == 1 else 2)
+        sample_steps = sorted(set(int(round(v)) for v in np.linspace(0, steps - 1, n_samp)))
+    if not args.no_timing_pass:
+        cold()
+        m.set_timing(1)
+        for s in range(steps):
+            for l in range(L):
+                m.forward(l, x_all[s], ids_all[s, l], w_all[s, l], out[l], stream=stream)
+            if s in sample_steps:
+                samples[s] = harness.bf16_bits(out)
+        tm = m.timing()
+        m.set_timing(0)
+        st2 = m.stats()
+        if st2["page_ins"] != M or st2["distinct"] != D:
+            raise RuntimeError("timing pass planned differently from the timed run")
+        w13b = 2 * wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5}[wl.wtype]
+        s13b = {"bf16": 0, "fp8": (2 * wl.inter // 128) * (wl.hidden // 128) * 4,
+                "int4": 2 * wl.inter * (wl.hidden // 128) * 2}[wl.wtype]
+        n_pi, ms_pi = tm["page_in"]
+        n_gu, ms_gu = tm["gate_up"]
+        kernel = {
+            "page_in": {"launches": n_pi, "avg_us": 1e3 * ms_pi / max(n_pi, 1),
+                        "bytes_per_launch": M * S_alg / max(n_pi, 1),
+                        "gbs": (M * S_alg / 1e9) / (ms_pi / 1e3) if ms_pi > 0 else None},
+            "gate_up": {"launches": n_gu, "avg_us": 1e3 * ms_gu / max(n_gu, 1),
+                        "bytes_per_launch": D * (w13b + s13b) / max(n_gu, 1),
+                        "gbs": (D * (w13b + s13b) / 1e9) / (ms_gu / 1e3) if ms_gu > 0 else None},
+            "stages_ms": {k: v[1] for k, v in tm.items()},
+        }
+        log("stage totals (ms): %s" % ", ".join("%s %.1f" % (k, v[1]) for k, v in tm.items()))
+
+    result = {
+        "metric": "paged-MoE decode tok/s, 48-layer 128-expert top-8; HBM & page-in GB/s % peak",
+        "value": round(value, 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(best_ms / steps, 4),
+        "ms_per_step_median": round(med_ms / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x", "int4": "int4-w/bf16-x"}[wl.wtype],
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "experts": wl.experts, "top_k": wl.top_k,
+                   "resident": wl.resident, "hidden": H, "inter": wl.inter, "wtype": wl.wtype,
+                   "batch": B, "path": "captured" if captured else "host-planned",
+                   "pagein": "dma" if (args.dma and not captured) else "kernel"},
+        "window": {"distinct": D, "page_ins": M, "expert_bytes": S_alg,
+                   "miss_rate": M / max(stats["entries"], 1)},
+        "roofline_path": {"model": "D*S/HBM + M*S/link", "hbm_gbs": HBM_PEAK_GBS, "link_gbs": round(link, 2),
+                          "link_dma_gbs": round(link_dma, 2), "link_kernel_gbs": round(link_kernel, 2),
+                          "roof_tok_s": round(roof_tok_s, 2), "frac": round(value / roof_tok_s, 4)},
+    }
+    if kernel:
+        pi = kernel["page_in"]
+        result["roofline"] = {"kernel": "page_in_kernel", "bound": "link",
+                              "achieved": round(pi["gbs"], 2) if pi["gbs"] else None,
+                              "peak": round(PCIE5_X16_GBS, 2), "unit": "GB/s",
+                              "frac": round(pi["gbs"] / PCIE5_X16_GBS, 4) if pi["gbs"] else None,
+                              "traffic": None, "avg_launch_us": round(pi["avg_us"], 2),
+                              "launches": pi["launches"], "bytes_per_launch": round(pi["bytes_per_launch"])}
+        gu = kernel["gate_up"]
+        result["roofline_hbm"] = {"kernel": "gemv_gate_up_kernel", "bound": "hbm",
+                                  "achieved": round(gu["gbs"], 2) if gu["gbs"] else None,
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gu["gbs"] / HBM_PEAK_GBS, 4) if gu["gbs"] else None,
+                                  "traffic": None, "avg_launch_us": round(gu["avg_us"], 2),
+                                  "launches": gu["launches"], "bytes_per_launch": round(gu["bytes_per_launch"])}
+        result["stages_ms"] = {k: round(v, 2) for k, v in kernel["stages_ms"].items()}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["sample_parity"] = cpu_baseline(wl, routing, steps, sample_steps, samples,
+                                                                       M, D)
+    m.close()
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D):
+    """The CPU oracle as it stands, on a bounded sample: the LRU simulator over the
+    whole window and the fp32 unpaged layer on a few evenly spaced steps (all
+    layers).  Expert tensors are generated untimed (they are inputs)."""
+    import numpy as np
+    import threadpoolctl
+
+    import harness
+    import synth
+    from oracle import formats, moe
+    from oracle.lru import LayerLRU
+
+    L, B = wl.layers, wl.batch
+    t0 = time.perf_counter()
+    misses = distinct = 0
+    for l in range(L):
+        sim = LayerLRU(wl.experts, wl.resident)
+        for s in range(steps):
+            ids = routing["decode_ids"][s, l].ravel()
+            misses += sum(w.count for w in sim.step(ids))
+            distinct += len(set(ids.tolist()))
+    t_sim = time.perf_counter() - t0
+    plan_ok = (misses == M and distinct == D)
+    log("oracle LRU simulator: %d layer-steps in %.2fs, plans %s" % (L * steps, t_sim,
+                                                                     "match" if plan_ok else "DIFFER"))
+    t_moe = 0.0
+    worst = 0.0
+    for s in sample_steps:
+        x = formats.bf16_to_f32(synth.hidden_states(wl, s, B))
+        for l in range(L):
+            ids, w = routing["decode_ids"][s, l], routing["decode_w"][s, l]
+            canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(ids)}
+            t0 = time.perf_counter()
+            ref = moe.moe_layer(x, ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+            t_moe += time.perf_counter() - t0
+            if s in samples:
+                got = harness.bf16_to_f32(samples[s][l])
+                worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    tokens = len(sample_steps) * B
+    t_total = t_moe + t_sim * len(sample_steps) / steps
+    log("oracle MoE: %d steps x %d layers in %.2fs" % (len(sample_steps), L, t_moe))
+    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2}[wl.wtype]
+    cpu = {"value": round(tokens / t_total, 5) if t_total > 0 else None, "unit": "tok/s", "cores": threads,
+           "kind": "oracle",
+           "sample": "%d of %d decode steps (all %d layers) through the fp32 unpaged oracle, plus the LRU "
+                     "simulator over all %d steps; %s" % (len(sample_steps), steps, L, steps,
+                                                          "host %s, %d cpus" % (cpu_model(), os.cpu_count()))}
+    parity = {"steps": sample_steps, "max_rel_err": worst, "tol": tol, "ok": bool(worst <= tol) if samples else None,
+              "plans_match_simulator": plan_ok}
+    return cpu, parity
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,74 @@
+"""Harness around libpe for tests, the benchmark and smoke(): builds a context
+for a synthetic workload, fills its host store from `synth` (in parallel
+threads: the generator and pe_load_expert both release the GIL), and turns
+the workload's routing into device tensors.  No method arithmetic here.
+"""
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import synth
+import host_paged_expert_amd as pe
+
+
+def host_threads() -> int:
+    """Worker threads for loading: the machine's CPU share (at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+def make_moe(wl, flags=0, max_tokens=None, device=0):
+    if max_tokens is None:
+        max_tokens = max(wl.batch, wl.prefill_tokens, 1)
+    return pe.PagedMoE(wl.layers, wl.experts, wl.top_k, wl.resident, wl.hidden, wl.inter, max_tokens,
+                       wl.wtype, device, flags)
+
+
+def load_store(moe, wl, threads=None, layers=None, experts=None, progress=None):
+    """Generate every expert of the workload and write it with pe_load_expert."""
+    layers = range(wl.layers) if layers is None else layers
+    experts = range(wl.experts) if experts is None else experts
+    jobs = [(l, e) for l in layers for e in experts]
+    done = [0]
+    lock = threading.Lock()
+
+    def one(job):
+        l, e = job
+        t13, t2, s13, s2 = synth.expert_tensors(wl, l, e)
+        moe.load_expert(l, e, t13, t2, s13, s2)
+        if progress is not None:
+            with lock:
+                done[0] += 1
+                if done[0] % progress == 0:
+                    print("  loaded %d/%d experts" % (done[0], len(jobs)), flush=True)
+
+    with ThreadPoolExecutor(threads or host_threads()) as ex:
+        list(ex.map(one, jobs))
+
+
+def decode_inputs(wl, routing, device, steps=None):
+    """Device tensors for decode: x [S, B, H] bf16 (as int16 bits viewed bf16),
+    ids [S, L, B, k] int32, w [S, L, B, k] fp32."""
+    import torch
+    steps = wl.steps if steps is None else steps
+    B = wl.batch
+    x = np.stack([synth.hidden_states(wl, s, B) for s in range(steps)])
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+    ids = torch.from_numpy(np.ascontiguousarray(routing["decode_ids"][:steps])).to(device)
+    w = torch.from_numpy(np.ascontiguousarray(routing["decode_w"][:steps])).to(device)
+    return xt, ids, w
+
+
+def bf16_bits(t) -> np.ndarray:
+    """A bf16 torch tensor's raw bits as numpy uint16."""
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)

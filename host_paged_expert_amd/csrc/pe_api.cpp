@@ -1,0 +1,693 @@
+// libpe: context, host store, orchestration and the C ABI declared in include/pe.h.
+//
+// SGLang "Paged Experts" docs page: "The K-slot table and the host store"
+// (K-row slot tables on the GPU, every expert in a page-locked host store whose
+// rows have the slots' layout), "A step: waves, page-in, merge" and "Captured
+// decode" (one device-planned wave with no host synchronisation when
+// tokens x top_k <= K, host-planned waves otherwise, one shared LRU state).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pe.h"
+#include "pe_kernels.h"
+#include "pe_layout.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define PE_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(PE_ERR_HIP, "%s failed: %s (line %d)", #call, hipGetErrorString(e_), \
+                  __LINE__);                                                          \
+  } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct BlobLayout {
+  size_t w13, w2, s13, s2;              // sub-tensor bytes
+  size_t off_w13, off_w2, off_s13, off_s2;
+  size_t algorithmic, copied, stride;
+};
+
+// One contiguous blob per expert: W13 | W2 | S13 | S2, each 256-byte aligned.
+// Keeping every sub-tensor of an expert in one blob means one page-in moves all
+// of them; no part of an expert can be left behind in a slot.
+bool blob_layout(int wtype, int H, int I, BlobLayout* b) {
+  const size_t n13 = (size_t)2 * I * H, n2 = (size_t)H * I;
+  switch (wtype) {
+    case PE_W_BF16: b->w13 = 2 * n13; b->w2 = 2 * n2; b->s13 = 0; b->s2 = 0; break;
+    case PE_W_FP8_B128:
+      b->w13 = n13; b->w2 = n2;
+      b->s13 = (size_t)(2 * I / 128) * (H / 128) * 4;
+      b->s2 = (size_t)(H / 128) * (I / 128) * 4;
+      break;
+    case PE_W_INT4_G128:
+      b->w13 = n13 / 2; b->w2 = n2 / 2;
+      b->s13 = (size_t)2 * I * (H / 128) * 2;
+      b->s2 = (size_t)H * (I / 128) * 2;
+      break;
+    default: return false;
+  }
+  b->off_w13 = 0;
+  b->off_w2 = align_up(b->off_w13 + b->w13, 256);
+  b->off_s13 = align_up(b->off_w2 + b->w2, 256);
+  b->off_s2 = align_up(b->off_s13 + b->s13, 256);
+  b->copied = align_up(b->off_s2 + b->s2, 256);
+  b->stride = align_up(b->copied, 4096);
+  b->algorithmic = b->w13 + b->w2 + b->s13 + b->s2;
+  return true;
+}
+
+constexpr int kPageInGrid = 1024;
+
+}  // namespace
+
+struct pe_ctx {
+  pe_config cfg{};
+  pe::Dims d{};
+  pe::LayerLayout ll{};
+  pe::WorkLayout wl{};
+  pe::Offsets o{};
+  BlobLayout b{};
+  bool unpaged = false;
+  int mfma_min = 1 << 30;
+  uint8_t* host_store = nullptr;       // page-locked, mapped: [L][E][stride]
+  uint8_t* host_store_dev = nullptr;   // its device-visible address
+  uint8_t* slots = nullptr;            // device: [L][K][stride]
+  int32_t* blocks = nullptr;           // device: [L][ll.total]
+  int32_t* work = nullptr;             // device: [wl.total]
+  uint16_t* h = nullptr;               // device: [max_entries][I] bf16
+  float* merged = nullptr;             // device: [max_entries][H] fp32
+  unsigned long long* stats = nullptr; // device: [ST_COUNT]
+  int32_t* st_ids = nullptr;           // pinned staging: [max_entries]
+  int32_t* st_blk = nullptr;           // pinned staging: [ll.total]
+  int32_t* st_work = nullptr;          // pinned staging: [wl.total]
+  pe::HostPlanSummary* sum = nullptr;
+  unsigned long long host_counts[pe::ST_COUNT] = {};
+  // measurement mode
+  bool timing = false;
+  std::vector<hipEvent_t> ev_free;
+  struct Pending { int stage; hipEvent_t a, b; };
+  std::vector<Pending> pending;
+  double stage_ms[PE_NUM_STAGES] = {};
+  unsigned long long stage_n[PE_NUM_STAGES] = {};
+};
+
+namespace {
+
+void free_ctx(pe_ctx* c) {
+  if (!c) return;
+  for (auto& p : c->pending) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
+  for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
+  if (c->host_store) (void)hipHostFree(c->host_store);
+  if (c->st_ids) (void)hipHostFree(c->st_ids);
+  if (c->st_blk) (void)hipHostFree(c->st_blk);
+  if (c->st_work) (void)hipHostFree(c->st_work);
+  for (void* p : {(void*)c->slots, (void*)c->blocks, (void*)c->work, (void*)c->h, (void*)c->merged,
+                  (void*)c->stats})
+    if (p) (void)hipFree(p);
+  delete c->sum;
+  delete c;
+}
+
+int use_device(const pe_ctx* c) {
+  int cur = -1;
+  PE_HIP(hipGetDevice(&cur));
+  if (cur != c->cfg.device) PE_HIP(hipSetDevice(c->cfg.device));
+  return PE_OK;
+}
+
+pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const float* w) {
+  pe::ExpertArgs a{};
+  a.slots = c->slots + (size_t)layer * c->d.K * c->b.stride;
+  a.slot_stride = c->b.stride;
+  a.off_w13 = c->b.off_w13; a.off_w2 = c->b.off_w2; a.off_s13 = c->b.off_s13; a.off_s2 = c->b.off_s2;
+  a.work = c->work;
+  a.o = c->o;
+  a.MW = c->d.max_waves;
+  a.wave = wave;
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_w = w;
+  a.h = c->h;
+  a.merged = c->merged;
+  a.H = c->d.H; a.I = c->d.I; a.k = c->d.k;
+  return a;
+}
+
+hipEvent_t take_event(pe_ctx* c) {
+  if (!c->ev_free.empty()) {
+    hipEvent_t e = c->ev_free.back();
+    c->ev_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Fold finished event pairs into the per-stage sums; with `wait`, all of them.
+int drain_timing(pe_ctx* c, bool wait) {
+  size_t keep = 0;
+  for (size_t i = 0; i < c->pending.size(); ++i) {
+    auto& p = c->pending[i];
+    if (!wait && hipEventQuery(p.b) != hipSuccess) { c->pending[keep++] = p; continue; }
+    PE_HIP(hipEventSynchronize(p.b));
+    float ms = 0.f;
+    PE_HIP(hipEventElapsedTime(&ms, p.a, p.b));
+    c->stage_ms[p.stage] += ms;
+    c->stage_n[p.stage] += 1;
+    c->ev_free.push_back(p.a);
+    c->ev_free.push_back(p.b);
+  }
+  c->pending.resize(keep);
+  return PE_OK;
+}
+
+// Brackets one stage's launches with events when timing is on.
+struct StageTimer {
+  pe_ctx* c;
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  StageTimer(pe_ctx* c_, int stage_, hipStream_t s_) : c(c_), stage(stage_), s(s_) {
+    if (!c->timing) return;
+    a = take_event(c);
+    if (a && hipEventRecord(a, s) != hipSuccess) a = nullptr;
+  }
+  ~StageTimer() {
+    if (!a) return;
+    hipEvent_t b = take_event(c);
+    if (!b || hipEventRecord(b, s) != hipSuccess) { c->ev_free.push_back(a); return; }
+    c->pending.push_back({stage, a, b});
+    if (c->pending.size() > 4096) (void)drain_timing(c, false);
+    if (c->pending.size() > 8192) (void)drain_timing(c, true);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* pe_strerror(int status) {
+  switch (status) {
+    case PE_OK: return "ok";
+    case PE_ERR_INVALID_ARG: return "invalid argument";
+    case PE_ERR_UNSUPPORTED: return "unsupported";
+    case PE_ERR_OOM_HOST_PIN: return "cannot pin host memory";
+    case PE_ERR_OOM_DEVICE: return "out of device memory";
+    case PE_ERR_HIP: return "HIP runtime error";
+    case PE_ERR_NOT_CAPTURABLE: return "host-planned step under stream capture";
+    default: return "unknown status";
+  }
+}
+
+const char* pe_last_error(void) { return g_err.c_str(); }
+
+int pe_expert_bytes(int wtype, int hidden, int inter, size_t* algorithmic, size_t* copied) {
+  if (hidden <= 0 || inter <= 0) return fail(PE_ERR_INVALID_ARG, "hidden and inter must be positive");
+  if (wtype != PE_W_BF16 && (hidden % 128 || inter % 128))
+    return fail(PE_ERR_INVALID_ARG, "quantized formats need hidden and inter multiples of 128");
+  BlobLayout b;
+  if (!blob_layout(wtype, hidden, inter, &b)) return fail(PE_ERR_INVALID_ARG, "unknown weight type %d", wtype);
+  if (algorithmic) *algorithmic = b.algorithmic;
+  if (copied) *copied = b.copied;
+  return PE_OK;
+}
+
+int pe_create(const pe_config* cfg, pe_ctx** out) {
+  if (!out) return fail(PE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(PE_ERR_INVALID_ARG, "cfg is NULL");
+  const pe_config& g = *cfg;
+  const bool unpaged = (g.flags & PE_FLAG_UNPAGED) != 0;
+  if (g.num_layers < 1) return fail(PE_ERR_INVALID_ARG, "num_layers must be >= 1");
+  if (g.num_experts < 1 || g.num_experts > pe::kMaxExperts)
+    return fail(PE_ERR_INVALID_ARG, "num_experts must be in [1, %d]", pe::kMaxExperts);
+  if (g.top_k < 1 || g.top_k > g.num_experts) return fail(PE_ERR_INVALID_ARG, "top_k must be in [1, E]");
+  const int K = unpaged ? g.num_experts : g.num_resident;
+  if (K < g.top_k) return fail(PE_ERR_INVALID_ARG, "num_resident K=%d must be at least top_k=%d", K, g.top_k);
+  if (K > g.num_experts) return fail(PE_ERR_INVALID_ARG, "num_resident K=%d exceeds num_experts", K);
+  if (g.max_tokens < 1) return fail(PE_ERR_INVALID_ARG, "max_tokens must be >= 1");
+  if (g.hidden <= 0 || g.inter <= 0 || g.hidden % 8 || g.inter % 8)
+    return fail(PE_ERR_INVALID_ARG, "hidden and inter must be positive multiples of 8");
+  if (g.hidden > 4096 || g.inter > 4096)
+    return fail(PE_ERR_UNSUPPORTED, "hidden and inter above 4096 are not supported");
+  if (g.wtype != PE_W_BF16 && g.wtype != PE_W_FP8_B128 && g.wtype != PE_W_INT4_G128)
+    return fail(PE_ERR_INVALID_ARG, "unknown weight type %d", g.wtype);
+  if (g.wtype != PE_W_BF16 && (g.hidden % 128 || g.inter % 128))
+    return fail(PE_ERR_INVALID_ARG, "quantized formats need hidden and inter multiples of 128");
+  if (g.flags & ~(PE_FLAG_PAGEIN_DMA | PE_FLAG_FORCE_HOST_PLAN | PE_FLAG_UNPAGED))
+    return fail(PE_ERR_INVALID_ARG, "unknown flags 0x%x", g.flags);
+  if ((long long)g.max_tokens * g.top_k > (1 << 24))
+    return fail(PE_ERR_UNSUPPORTED, "max_tokens * top_k too large");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || g.device < 0 || g.device >= ndev)
+    return fail(PE_ERR_INVALID_ARG, "device %d not available", g.device);
+
+  pe_ctx* c = new pe_ctx;
+  c->cfg = g;
+  c->cfg.num_resident = K;
+  c->unpaged = unpaged;
+  c->d = pe::make_dims(g.num_layers, g.num_experts, K, g.top_k, g.hidden, g.inter, g.max_tokens);
+  c->ll = pe::make_layer_layout(c->d);
+  c->wl = pe::make_work_layout(c->d);
+  c->o = pe::make_offsets(c->ll, c->wl);
+  blob_layout(g.wtype, g.hidden, g.inter, &c->b);
+  c->sum = new pe::HostPlanSummary;
+  int rc = use_device(c);
+  if (rc) { free_ctx(c); return rc; }
+
+  const pe::Dims& d = c->d;
+  if (!unpaged) {
+    size_t bytes = (size_t)d.L * d.E * c->b.stride;
+    if (hipHostMalloc(reinterpret_cast<void**>(&c->host_store), bytes, hipHostMallocMapped) != hipSuccess) {
+      c->host_store = nullptr;
+      (void)hipGetLastError();
+      free_ctx(c);
+      return fail(PE_ERR_OOM_HOST_PIN, "cannot pin %zu bytes of host memory for the expert store", bytes);
+    }
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, c->host_store, 0) != hipSuccess) {
+      free_ctx(c);
+      return fail(PE_ERR_HIP, "hipHostGetDevicePointer failed for the host store");
+    }
+    c->host_store_dev = static_cast<uint8_t*>(dp);
+  }
+  struct { void** p; size_t bytes; } dev[] = {
+      {reinterpret_cast<void**>(&c->slots), (size_t)d.L * d.K * c->b.stride},
+      {reinterpret_cast<void**>(&c->blocks), (size_t)d.L * c->ll.total * 4},
+      {reinterpret_cast<void**>(&c->work), c->wl.total * 4},
+      {reinterpret_cast<void**>(&c->h), (size_t)d.max_entries * d.I * 2},
+      {reinterpret_cast<void**>(&c->merged), (size_t)d.max_entries * d.H * 4},
+      {reinterpret_cast<void**>(&c->stats), pe::ST_COUNT * 8},
+  };
+  for (auto& a : dev) {
+    if (hipMalloc(a.p, a.bytes) != hipSuccess) {
+      *a.p = nullptr;
+      (void)hipGetLastError();
+      free_ctx(c);
+      return fail(PE_ERR_OOM_DEVICE, "cannot allocate %zu bytes of device memory", a.bytes);
+    }
+  }
+  struct { int32_t** p; size_t words; } pin[] = {
+      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, c->ll.total}, {&c->st_work, c->wl.total}};
+  for (auto& a : pin) {
+    if (hipHostMalloc(reinterpret_cast<void**>(a.p), a.words * 4, hipHostMallocDefault) != hipSuccess) {
+      *a.p = nullptr;
+      (void)hipGetLastError();
+      free_ctx(c);
+      return fail(PE_ERR_OOM_HOST_PIN, "cannot pin staging buffers");
+    }
+  }
+  if (hipMemset(c->stats, 0, pe::ST_COUNT * 8) != hipSuccess ||
+      hipMemset(c->blocks, 0, (size_t)d.L * c->ll.total * 4) != hipSuccess ||
+      hipMemset(c->work, 0, c->wl.total * 4) != hipSuccess) {
+    free_ctx(c);
+    return fail(PE_ERR_HIP, "initialising device buffers failed");
+  }
+  pe::launch_reset_lru(c->blocks, c->ll.total, 0, d.L, c->o, d.E, d.K, unpaged, nullptr);
+  if (hipDeviceSynchronize() != hipSuccess) {
+    free_ctx(c);
+    return fail(PE_ERR_HIP, "resetting the LRU state failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  *out = c;
+  return PE_OK;
+}
+
+void pe_destroy(pe_ctx* ctx) {
+  if (!ctx) return;
+  (void)use_device(ctx);
+  (void)hipDeviceSynchronize();
+  free_ctx(ctx);
+}
+
+int pe_load_expert(pe_ctx* c, int layer, int expert, const void* w13, const void* w2, const void* s13,
+                   const void* s2) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (layer < 0 || layer >= c->d.L || expert < 0 || expert >= c->d.E)
+    return fail(PE_ERR_INVALID_ARG, "layer %d / expert %d out of range", layer, expert);
+  if (!w13 || !w2) return fail(PE_ERR_INVALID_ARG, "w13 and w2 are required");
+  const bool quant = c->cfg.wtype != PE_W_BF16;
+  if (quant && (!s13 || !s2)) return fail(PE_ERR_INVALID_ARG, "scales are required for quantized formats");
+  const BlobLayout& b = c->b;
+  if (c->unpaged) {
+    int rc = use_device(c);
+    if (rc) return rc;
+    uint8_t* dst = c->slots + ((size_t)layer * c->d.K + expert) * b.stride;
+    PE_HIP(hipMemcpy(dst + b.off_w13, w13, b.w13, hipMemcpyHostToDevice));
+    PE_HIP(hipMemcpy(dst + b.off_w2, w2, b.w2, hipMemcpyHostToDevice));
+    if (quant) {
+      PE_HIP(hipMemcpy(dst + b.off_s13, s13, b.s13, hipMemcpyHostToDevice));
+      PE_HIP(hipMemcpy(dst + b.off_s2, s2, b.s2, hipMemcpyHostToDevice));
+    }
+    return PE_OK;
+  }
+  uint8_t* dst = c->host_store + ((size_t)layer * c->d.E + expert) * b.stride;
+  memcpy(dst + b.off_w13, w13, b.w13);
+  memcpy(dst + b.off_w2, w2, b.w2);
+  if (quant) {
+    memcpy(dst + b.off_s13, s13, b.s13);
+    memcpy(dst + b.off_s2, s2, b.s2);
+  }
+  return PE_OK;
+}
+
+int pe_reset_lru(pe_ctx* c, int layer, void* stream) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (layer < -1 || layer >= c->d.L) return fail(PE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  int rc = use_device(c);
+  if (rc) return rc;
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->d.L : layer + 1;
+  pe::launch_reset_lru(c->blocks, c->ll.total, l0, l1, c->o, c->d.E, c->d.K, c->unpaged,
+                       static_cast<hipStream_t>(stream));
+  PE_HIP(hipGetLastError());
+  return PE_OK;
+}
+
+int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, const float* topk_w, int T,
+               void* out, void* stream) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (layer < 0 || layer >= c->d.L) return fail(PE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (T < 0 || T > c->d.max_tokens) return fail(PE_ERR_INVALID_ARG, "T=%d outside [0, %d]", T, c->d.max_tokens);
+  if (T == 0) return PE_OK;
+  if (!x || !topk_ids || !topk_w || !out) return fail(PE_ERR_INVALID_ARG, "NULL tensor pointer");
+  int rc = use_device(c);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pe::Dims& d = c->d;
+  const int n = T * d.k;
+  int32_t* blk = c->blocks + (size_t)layer * c->ll.total;
+  uint8_t* slots_l = c->slots + (size_t)layer * d.K * c->b.stride;
+  const uint8_t* host_l = c->unpaged ? nullptr : c->host_store_dev + (size_t)layer * d.E * c->b.stride;
+  const bool device_plan = n <= d.K && !(c->cfg.flags & PE_FLAG_FORCE_HOST_PLAN);
+
+  if (device_plan) {
+    {
+      StageTimer tm(c, PE_STAGE_PLAN, s);
+      pe::launch_plan_single_wave(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, s);
+    }
+    if (!c->unpaged) {
+      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+      pe::launch_page_in(blk, c->o, 0, d.K, host_l, slots_l, c->b.stride, c->b.copied, kPageInGrid, s);
+    }
+    pe::ExpertArgs a = expert_args(c, layer, 0, x, topk_w);
+    const int items = std::min(n, d.K);
+    {
+      StageTimer tm(c, PE_STAGE_GATE_UP, s);
+      pe::launch_gemv_gate_up(c->cfg.wtype, a, items, T, s);
+    }
+    {
+      StageTimer tm(c, PE_STAGE_DOWN, s);
+      pe::launch_gemv_down(c->cfg.wtype, a, items, T, s);
+    }
+    {
+      StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
+      pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), s);
+    }
+    PE_HIP(hipGetLastError());
+    return PE_OK;
+  }
+
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  PE_HIP(hipStreamIsCapturing(s, &cap));
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(PE_ERR_NOT_CAPTURABLE, "T*top_k=%d > K=%d needs host planning, which cannot be captured", n, d.K);
+
+  // Host-planned step: read ids and LRU state back (the one synchronisation),
+  // plan every wave, upload plans and work lists, then run the waves in order.
+  PE_HIP(hipMemcpyAsync(c->st_ids, topk_ids, (size_t)n * 4, hipMemcpyDeviceToHost, s));
+  PE_HIP(hipMemcpyAsync(c->st_blk, blk, c->ll.state_words * 4, hipMemcpyDeviceToHost, s));
+  PE_HIP(hipStreamSynchronize(s));
+  pe::HostPlanSummary& sm = *c->sum;
+  if (pe::host_plan_step(d, c->ll, c->wl, c->st_ids, n, c->st_blk, c->st_work, &sm) != 0)
+    return fail(PE_ERR_INVALID_ARG, "step needs more waves than the context holds");
+  PE_HIP(hipMemcpyAsync(blk, c->st_blk, (c->ll.slot_of + n) * 4, hipMemcpyHostToDevice, s));
+  PE_HIP(hipMemcpyAsync(c->work, c->st_work, (c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));
+  const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
+  for (int w = 0; w < sm.n_waves; ++w) {
+    const int cnt = c->st_blk[c->ll.plan_count + w];
+    if (!c->unpaged && cnt > 0) {
+      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+      if (dma) {
+        const int32_t* pe_ = c->st_blk + c->ll.plan_expert + (size_t)w * d.K;
+        const int32_t* ps_ = c->st_blk + c->ll.plan_slot + (size_t)w * d.K;
+        for (int r = 0; r < cnt; ++r)
+          PE_HIP(hipMemcpyAsync(slots_l + (size_t)ps_[r] * c->b.stride,
+                                c->host_store + ((size_t)layer * d.E + pe_[r]) * c->b.stride, c->b.copied,
+                                hipMemcpyHostToDevice, s));
+      } else {
+        pe::launch_page_in(blk, c->o, w, d.K, host_l, slots_l, c->b.stride, c->b.copied, kPageInGrid, s);
+      }
+    }
+    pe::ExpertArgs a = expert_args(c, layer, w, x, topk_w);
+    if (sm.gemv_items[w] > 0) {
+      {
+        StageTimer tm(c, PE_STAGE_GATE_UP, s);
+        pe::launch_gemv_gate_up(c->cfg.wtype, a, sm.gemv_items[w], sm.max_gemv_tokens, s);
+      }
+      StageTimer tm(c, PE_STAGE_DOWN, s);
+      pe::launch_gemv_down(c->cfg.wtype, a, sm.gemv_items[w], sm.max_gemv_tokens, s);
+    }
+  }
+  {
+    StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
+    pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), s);
+  }
+  PE_HIP(hipGetLastError());
+  c->host_counts[pe::ST_STEPS] += 1;
+  c->host_counts[pe::ST_HOST_PLANNED] += 1;
+  c->host_counts[pe::ST_WAVES] += sm.n_waves;
+  c->host_counts[pe::ST_PAGE_INS] += sm.page_ins;
+  c->host_counts[pe::ST_DISTINCT] += sm.distinct;
+  c->host_counts[pe::ST_ENTRIES] += sm.valid_entries;
+  c->host_counts[pe::ST_BAD_IDS] += sm.bad_ids;
+  return PE_OK;
+}
+
+int pe_max_captured_batch(const pe_ctx* c) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  return c->d.K / c->d.k;
+}
+
+int pe_max_waves(const pe_ctx* c) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  return c->d.max_waves;
+}
+
+int pe_get_lru_state(pe_ctx* c, int layer, int32_t* slot_expert, uint32_t* last_use, uint32_t* tick,
+                     void* stream) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (layer < 0 || layer >= c->d.L) return fail(PE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  int rc = use_device(c);
+  if (rc) return rc;
+  PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  std::vector<int32_t> st(c->ll.state_words);
+  PE_HIP(hipMemcpy(st.data(), c->blocks + (size_t)layer * c->ll.total, st.size() * 4, hipMemcpyDeviceToHost));
+  if (slot_expert) memcpy(slot_expert, st.data() + c->ll.slot_expert, (size_t)c->d.K * 4);
+  if (last_use) memcpy(last_use, st.data() + c->ll.last_use, (size_t)c->d.K * 4);
+  if (tick) *tick = (uint32_t)st[c->ll.tick];
+  return PE_OK;
+}
+
+int pe_get_plan(pe_ctx* c, int layer, int wave, int32_t* count, int32_t* experts, int32_t* slots,
+                int32_t* evicted, int32_t* n_waves, void* stream) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (layer < 0 || layer >= c->d.L || wave < 0 || wave >= c->d.max_waves)
+    return fail(PE_ERR_INVALID_ARG, "layer %d / wave %d out of range", layer, wave);
+  int rc = use_device(c);
+  if (rc) return rc;
+  PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  std::vector<int32_t> blk(c->ll.slot_of);
+  PE_HIP(hipMemcpy(blk.data(), c->blocks + (size_t)layer * c->ll.total, blk.size() * 4, hipMemcpyDeviceToHost));
+  const int K = c->d.K;
+  if (count) *count = blk[c->ll.plan_count + wave];
+  if (experts) memcpy(experts, blk.data() + c->ll.plan_expert + (size_t)wave * K, (size_t)K * 4);
+  if (slots) memcpy(slots, blk.data() + c->ll.plan_slot + (size_t)wave * K, (size_t)K * 4);
+  if (evicted) memcpy(evicted, blk.data() + c->ll.plan_evicted + (size_t)wave * K, (size_t)K * 4);
+  if (n_waves) *n_waves = blk[c->ll.n_waves];
+  return PE_OK;
+}
+
+int pe_get_slot_map(pe_ctx* c, int layer, int32_t* slot_of, int T, void* stream) {
+  if (!c || !slot_of) return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens)
+    return fail(PE_ERR_INVALID_ARG, "layer %d / T %d out of range", layer, T);
+  int rc = use_device(c);
+  if (rc) return rc;
+  PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  PE_HIP(hipMemcpy(slot_of, c->blocks + (size_t)layer * c->ll.total + c->ll.slot_of, (size_t)T * c->d.k * 4,
+                   hipMemcpyDeviceToHost));
+  return PE_OK;
+}
+
+int pe_get_stats(pe_ctx* c, pe_stats* out) {
+  if (!c || !out) return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  int rc = use_device(c);
+  if (rc) return rc;
+  unsigned long long dv[pe::ST_COUNT];
+  PE_HIP(hipDeviceSynchronize());
+  PE_HIP(hipMemcpy(dv, c->stats, sizeof dv, hipMemcpyDeviceToHost));
+  unsigned long long t[pe::ST_COUNT];
+  for (int i = 0; i < pe::ST_COUNT; ++i) t[i] = dv[i] + c->host_counts[i];
+  out->steps = t[pe::ST_STEPS];
+  out->device_planned = t[pe::ST_DEVICE_PLANNED];
+  out->host_planned = t[pe::ST_HOST_PLANNED];
+  out->waves = t[pe::ST_WAVES];
+  out->page_ins = c->unpaged ? 0 : t[pe::ST_PAGE_INS];
+  out->page_in_bytes = out->page_ins * c->b.copied;
+  out->distinct = t[pe::ST_DISTINCT];
+  out->entries = t[pe::ST_ENTRIES];
+  out->bad_ids = t[pe::ST_BAD_IDS];
+  return PE_OK;
+}
+
+int pe_reset_stats(pe_ctx* c) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  int rc = use_device(c);
+  if (rc) return rc;
+  PE_HIP(hipDeviceSynchronize());
+  PE_HIP(hipMemset(c->stats, 0, pe::ST_COUNT * 8));
+  for (auto& v : c->host_counts) v = 0;
+  return PE_OK;
+}
+
+int pe_link_probe(pe_ctx* c, size_t bytes, int use_kernel, int reps, double* gbps, void* stream) {
+  if (!c || !gbps || bytes < 16 || bytes % 16 || reps < 1) return fail(PE_ERR_INVALID_ARG, "bad probe arguments");
+  int rc = use_device(c);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* hbuf = nullptr;
+  void* dbuf = nullptr;
+  if (hipHostMalloc(&hbuf, bytes, hipHostMallocMapped) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PE_ERR_OOM_HOST_PIN, "probe: cannot pin %zu bytes", bytes);
+  }
+  memset(hbuf, 0x5A, bytes);
+  if (hipMalloc(&dbuf, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipHostFree(hbuf);
+    return fail(PE_ERR_OOM_DEVICE, "probe: cannot allocate %zu device bytes", bytes);
+  }
+  void* hdev = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int status = PE_OK;
+  double best = 0.0;
+  do {
+    if (hipHostGetDevicePointer(&hdev, hbuf, 0) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
+        hipEventCreate(&e1) != hipSuccess) {
+      status = fail(PE_ERR_HIP, "probe: HIP setup failed");
+      break;
+    }
+    for (int r = 0; r <= reps && status == PE_OK; ++r) {   // r == 0 warms up
+      if (hipEventRecord(e0, s) != hipSuccess) { status = fail(PE_ERR_HIP, "probe: event record"); break; }
+      if (use_kernel) pe::launch_copy(dbuf, hdev, bytes, kPageInGrid, s);
+      else if (hipMemcpyAsync(dbuf, hbuf, bytes, hipMemcpyHostToDevice, s) != hipSuccess) {
+        status = fail(PE_ERR_HIP, "probe: hipMemcpyAsync");
+        break;
+      }
+      float ms = 0.f;
+      if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+        status = fail(PE_ERR_HIP, "probe: timing failed: %s", hipGetErrorString(hipGetLastError()));
+        break;
+      }
+      if (r > 0 && ms > 0.f) best = std::max(best, bytes / (ms * 1e-3) / 1e9);
+    }
+  } while (false);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(dbuf);
+  (void)hipHostFree(hbuf);
+  if (status == PE_OK) *gbps = best;
+  return status;
+}
+
+int pe_set_timing(pe_ctx* c, int enable) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  int rc = use_device(c);
+  if (rc) return rc;
+  rc = drain_timing(c, true);
+  if (rc) return rc;
+  c->timing = enable != 0;
+  for (int i = 0; i < PE_NUM_STAGES; ++i) { c->stage_ms[i] = 0.0; c->stage_n[i] = 0; }
+  return PE_OK;
+}
+
+int pe_get_timing(pe_ctx* c, uint64_t* launches, double* total_ms) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  int rc = use_device(c);
+  if (rc) return rc;
+  rc = drain_timing(c, true);
+  if (rc) return rc;
+  for (int i = 0; i < PE_NUM_STAGES; ++i) {
+    if (launches) launches[i] = c->stage_n[i];
+    if (total_ms) total_ms[i] = c->stage_ms[i];
+  }
+  return PE_OK;
+}
+
+int pe_plan_host(int num_experts, int num_resident, int top_k, int T, const int32_t* topk_ids,
+                 int32_t* slot_expert, uint32_t* last_use, uint32_t* tick, int max_waves, int32_t* n_waves,
+                 int32_t* counts, int32_t* experts, int32_t* slots, int32_t* evicted, int32_t* slot_of) {
+  if (num_experts < 1 || num_experts > pe::kMaxExperts || top_k < 1 || num_resident < top_k ||
+      num_resident > num_experts || T < 1 || max_waves < 1)
+    return fail(PE_ERR_INVALID_ARG, "bad planner dimensions");
+  if (!topk_ids || !slot_expert || !last_use || !tick || !n_waves || !counts || !experts || !slots || !evicted ||
+      !slot_of)
+    return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  pe::Dims d = pe::make_dims(1, num_experts, num_resident, top_k, 8, 8, T);
+  d.max_waves = max_waves;
+  const pe::LayerLayout ll = pe::make_layer_layout(d);
+  const pe::WorkLayout wl = pe::make_work_layout(d);
+  std::vector<int32_t> blk(ll.total, 0), work(wl.total, 0);
+  const int K = num_resident, E = num_experts;
+  blk[ll.tick] = (int32_t)*tick;
+  for (int e = 0; e < E; ++e) blk[ll.expert_slot + e] = -1;
+  for (int j = 0; j < K; ++j) {
+    const int e = slot_expert[j];
+    if (e >= E) return fail(PE_ERR_INVALID_ARG, "slot_expert[%d] = %d out of range", j, e);
+    blk[ll.slot_expert + j] = e;
+    blk[ll.last_use + j] = (int32_t)last_use[j];
+    if (e >= 0) {
+      if (blk[ll.expert_slot + e] >= 0) return fail(PE_ERR_INVALID_ARG, "expert %d in two slots", e);
+      blk[ll.expert_slot + e] = j;
+    }
+  }
+  pe::HostPlanSummary* sm = new pe::HostPlanSummary;
+  const int rc = pe::host_plan_step(d, ll, wl, topk_ids, T * top_k, blk.data(), work.data(), sm);
+  delete sm;
+  if (rc != 0) return fail(PE_ERR_INVALID_ARG, "step needs more than %d waves", max_waves);
+  for (int j = 0; j < K; ++j) {
+    slot_expert[j] = blk[ll.slot_expert + j];
+    last_use[j] = (uint32_t)blk[ll.last_use + j];
+  }
+  *tick = (uint32_t)blk[ll.tick];
+  *n_waves = blk[ll.n_waves];
+  for (int w = 0; w < max_waves; ++w) counts[w] = w < *n_waves ? blk[ll.plan_count + w] : 0;
+  memcpy(experts, blk.data() + ll.plan_expert, (size_t)max_waves * K * 4);
+  memcpy(slots, blk.data() + ll.plan_slot, (size_t)max_waves * K * 4);
+  memcpy(evicted, blk.data() + ll.plan_evicted, (size_t)max_waves * K * 4);
+  memcpy(slot_of, blk.data() + ll.slot_of, (size_t)T * top_k * 4);
+  return PE_OK;
+}
+
+}  // extern "C"

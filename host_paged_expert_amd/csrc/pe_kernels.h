@@ -1,0 +1,63 @@
+// Launchers of the libpe HIP kernels (defined in pe_kernels.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "pe_layout.h"
+
+namespace pe {
+
+// Offsets of the layer block and the work arena, in int32 words, as kernel arguments.
+struct Offsets {
+  int tick, slot_expert, expert_slot, last_use, n_waves, plan_count, plan_expert, plan_slot,
+      plan_evicted, slot_of;
+  int hdr, used_expert, used_slot, used_off, gemv_u, tile_u, tile_row, entries;
+};
+
+Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl);
+
+// Everything the expert kernels read: one layer's slot table, the step work
+// lists and the activations.
+struct ExpertArgs {
+  const uint8_t* slots;       // slot 0 of the layer
+  size_t slot_stride;         // bytes between slots
+  size_t off_w13, off_w2, off_s13, off_s2;   // sub-tensor offsets inside a blob
+  const int32_t* work;        // work arena
+  Offsets o;
+  int MW;                     // header capacity (max waves)
+  int wave;                   // wave whose experts this launch runs
+  const uint16_t* x;          // [T, H] bf16
+  const float* topk_w;        // [T*k]
+  uint16_t* h;                // [max_entries, I] bf16, by sorted position
+  float* merged;              // [T*k, H] fp32, by entry index
+  int H, I, k;
+};
+
+// Single-wave device planner (T*k <= K): LRU decision, plan, slot map, work
+// lists and counters for one layer, in one workgroup.
+void launch_plan_single_wave(int32_t* blk, const int32_t* ids, int n, const Dims& d,
+                             const Offsets& o, int mfma_min, int32_t* work,
+                             unsigned long long* stats, hipStream_t s);
+
+// Copy the planned experts of wave `wave` from the mapped host rows into their
+// slots, reading the page-in count on the device.
+void launch_page_in(const int32_t* blk, const Offsets& o, int wave, int K,
+                    const uint8_t* host_rows, uint8_t* slots, size_t stride, size_t copy_bytes,
+                    int grid, hipStream_t s);
+
+// Raw mapped-read copy (the page-in copy routine on plain buffers).
+void launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t s);
+
+// GEMV expert kernels for the experts of one wave with few tokens each.
+// `items` bounds the experts of the launch; `max_m` bounds their token counts.
+void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
+void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
+
+// out[t] = bf16(sum_j merged[t,j]) over valid entries, j in order.
+void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int E, int H,
+                     uint16_t* out, hipStream_t s);
+
+// Reset the LRU state of layers [l0, l1): empty, or the identity map.
+void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const Offsets& o,
+                      int E, int K, bool identity, hipStream_t s);
+
+}  // namespace pe

@@ -1,0 +1,676 @@
+// HIP kernels of libpe for gfx950 (CDNA4, 64-wide wavefronts).
+//
+// Steps of one MoE-layer forward with paged experts (SGLang "Paged Experts"
+// docs page, "A step: waves, page-in, merge" and "Captured decode"):
+//   plan_single_wave  the LRU decision made on the device, writing the page-in
+//                     plan (experts, slots, count) to device buffers, plus the
+//                     slot remap and per-slot entry lists;
+//   page_in           copies the planned expert blobs from pinned host memory,
+//                     read through its mapped address, with the count read on
+//                     the device;
+//   gemv_gate_up      per used slot: h = silu(W1 x) * (W3 x) (fp32 accumulation,
+//                     inline dequantisation), stored as bf16;
+//   gemv_down         per used slot: merged[t,j] = w[t,j] * (W2 h) in fp32,
+//                     no top-k sum;
+//   topk_sum          the fixed-order top-k sum of the merged entries.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "../../include/pe.h"
+#include "pe_kernels.h"
+
+namespace pe {
+
+Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl) {
+  Offsets o;
+  o.tick = (int)ll.tick; o.slot_expert = (int)ll.slot_expert; o.expert_slot = (int)ll.expert_slot;
+  o.last_use = (int)ll.last_use; o.n_waves = (int)ll.n_waves; o.plan_count = (int)ll.plan_count;
+  o.plan_expert = (int)ll.plan_expert; o.plan_slot = (int)ll.plan_slot;
+  o.plan_evicted = (int)ll.plan_evicted; o.slot_of = (int)ll.slot_of;
+  o.hdr = (int)wl.hdr; o.used_expert = (int)wl.used_expert; o.used_slot = (int)wl.used_slot;
+  o.used_off = (int)wl.used_off; o.gemv_u = (int)wl.gemv_u; o.tile_u = (int)wl.tile_u;
+  o.tile_row = (int)wl.tile_row; o.entries = (int)wl.entries;
+  return o;
+}
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+
+// Inclusive scan across the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int n = __shfl_up(v, off, 64);
+    if (lane >= off) v += n;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------------ planner
+
+namespace {
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kScanVals = 5;   // missing, present, entries, gemv, tiles
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
+    int32_t* __restrict__ blk, const int32_t* __restrict__ ids, int n, int E, int K, int MW,
+    Offsets o, int mfma_min, int32_t* __restrict__ work, unsigned long long* __restrict__ stats) {
+  __shared__ int s_es[kMaxExperts];        // expert -> slot (updated in place)
+  __shared__ int s_cnt[kMaxExperts];       // entries per expert
+  __shared__ int s_se[kMaxExperts];        // slot -> expert
+  __shared__ unsigned s_lu[kMaxExperts];   // slot last use
+  __shared__ int s_cand[kMaxExperts];      // slot is evictable in this wave
+  __shared__ int s_victim[kMaxExperts];    // victims by rank
+  __shared__ int s_ids[kMaxExperts];       // valid id or -1
+  __shared__ int s_pref[kScanVals][kMaxExperts];   // exclusive prefixes per expert
+  __shared__ int s_wtot[kScanVals][kPlanWaves];
+  __shared__ int s_tot[kScanVals];
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const unsigned tick = (unsigned)blk[o.tick];
+  if (tid == 0) s_bad = 0;
+  for (int e = tid; e < E; e += kPlanThreads) { s_es[e] = blk[o.expert_slot + e]; s_cnt[e] = 0; }
+  for (int j = tid; j < K; j += kPlanThreads) {
+    s_se[j] = blk[o.slot_expert + j];
+    s_lu[j] = (unsigned)blk[o.last_use + j];
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kPlanThreads) {
+    int id = ids[i];
+    bool ok = id >= 0 && id < E;
+    s_ids[i] = ok ? id : -1;
+    if (ok) atomicAdd(&s_cnt[id], 1); else atomicAdd(&s_bad, 1);
+  }
+  __syncthreads();
+
+  // Exclusive prefixes over experts of: missing, present, entry count, GEMV
+  // flag and MFMA tile count.  Thread t owns experts [t*per, (t+1)*per).
+  const int per = (E + kPlanThreads - 1) / kPlanThreads;
+  const int e0 = tid * per;
+  int loc[kScanVals] = {0, 0, 0, 0, 0};
+  for (int q = 0; q < per; ++q) {
+    int e = e0 + q;
+    if (e >= E) break;
+    int c = s_cnt[e];
+    if (c > 0) {
+      loc[0] += s_es[e] < 0;
+      loc[1] += 1;
+      loc[2] += c;
+      if (c < mfma_min) loc[3] += 1; else loc[4] += (c + kTileM - 1) / kTileM;
+    }
+  }
+  int inc[kScanVals];
+#pragma unroll
+  for (int v = 0; v < kScanVals; ++v) inc[v] = wave_incl_scan(loc[v], lane);
+  if (lane == 63) {
+#pragma unroll
+    for (int v = 0; v < kScanVals; ++v) s_wtot[v][wv] = inc[v];
+  }
+  __syncthreads();
+  int base[kScanVals];
+#pragma unroll
+  for (int v = 0; v < kScanVals; ++v) {
+    int b = 0, t = 0;
+    for (int w = 0; w < kPlanWaves; ++w) { if (w < wv) b += s_wtot[v][w]; t += s_wtot[v][w]; }
+    base[v] = b + inc[v] - loc[v];
+    if (tid == 0) s_tot[v] = t;
+  }
+  {
+    int run[kScanVals];
+#pragma unroll
+    for (int v = 0; v < kScanVals; ++v) run[v] = base[v];
+    for (int q = 0; q < per; ++q) {
+      int e = e0 + q;
+      if (e >= E) break;
+#pragma unroll
+      for (int v = 0; v < kScanVals; ++v) s_pref[v][e] = run[v];
+      int c = s_cnt[e];
+      if (c > 0) {
+        run[0] += s_es[e] < 0;
+        run[1] += 1;
+        run[2] += c;
+        if (c < mfma_min) run[3] += 1; else run[4] += (c + kTileM - 1) / kTileM;
+      }
+    }
+  }
+  // Evictable slots: empty, or holding an expert outside this wave (the wave is
+  // every routed expert of the step).
+  for (int j = tid; j < K; j += kPlanThreads) {
+    int occ = s_se[j];
+    s_cand[j] = occ < 0 || s_cnt[occ] == 0;
+  }
+  __syncthreads();
+  const int n_miss = s_tot[0], D = s_tot[1], n_valid = s_tot[2], n_gemv = s_tot[3], n_tiles = s_tot[4];
+  // Victims by ascending (last_use, slot): rank = candidates ordered before j.
+  for (int j = tid; j < K; j += kPlanThreads) {
+    if (!s_cand[j]) continue;
+    unsigned lj = s_lu[j];
+    int r = 0;
+    for (int q = 0; q < K; ++q)
+      r += s_cand[q] && (s_lu[q] < lj || (s_lu[q] == lj && q < j));
+    if (r < n_miss) s_victim[r] = j;
+  }
+  __syncthreads();
+  // Place the i-th missing expert (ascending id) into the i-th victim.
+  int32_t* plan_e = blk + o.plan_expert;
+  int32_t* plan_s = blk + o.plan_slot;
+  int32_t* plan_v = blk + o.plan_evicted;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    if (s_cnt[e] == 0 || s_es[e] >= 0) continue;
+    int r = s_pref[0][e];
+    int j = s_victim[r];
+    int old = s_se[j];
+    plan_e[r] = e; plan_s[r] = j; plan_v[r] = old;
+    s_se[j] = e;
+    s_es[e] = j;
+    if (old >= 0) s_es[old] = -1;      // old is outside the wave: no other thread reads it
+  }
+  __syncthreads();
+  // The wave is one use: stamp every routed expert's slot; emit work lists.
+  int32_t* used_expert = work + o.used_expert;
+  int32_t* used_slot = work + o.used_slot;
+  int32_t* used_off = work + o.used_off;
+  int32_t* gemv_u = work + o.gemv_u;
+  int32_t* tile_u = work + o.tile_u;
+  int32_t* tile_row = work + o.tile_row;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int c = s_cnt[e];
+    if (c == 0) continue;
+    int j = s_es[e];
+    s_lu[j] = tick;
+    int u = s_pref[1][e];
+    used_expert[u] = e;
+    used_slot[u] = j;
+    used_off[u] = s_pref[2][e];
+    if (c < mfma_min) {
+      gemv_u[s_pref[3][e]] = u;
+    } else {
+      int t0 = s_pref[4][e];
+      for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
+    }
+  }
+  __syncthreads();
+  // Entries: ascending entry index inside each expert; slot map.
+  int32_t* entries = work + o.entries;
+  int32_t* slot_of = blk + o.slot_of;
+  for (int i = tid; i < n; i += kPlanThreads) {
+    int id = s_ids[i];
+    if (id < 0) { slot_of[i] = -1; continue; }
+    int r = 0;
+    for (int q = 0; q < i; ++q) r += s_ids[q] == id;
+    entries[s_pref[2][id] + r] = i;
+    slot_of[i] = s_es[id];
+  }
+  // Write back the LRU state.
+  for (int e = tid; e < E; e += kPlanThreads) blk[o.expert_slot + e] = s_es[e];
+  for (int j = tid; j < K; j += kPlanThreads) {
+    blk[o.slot_expert + j] = s_se[j];
+    blk[o.last_use + j] = (int32_t)s_lu[j];
+  }
+  if (tid == 0) {
+    const int nw = D > 0 ? 1 : 0;
+    blk[o.tick] = (int32_t)(tick + nw);
+    blk[o.n_waves] = nw;
+    blk[o.plan_count] = n_miss;
+    int32_t* hdr = work + o.hdr;
+    hdr[0] = nw;
+    hdr[hdr_wave_u(MW, 0)] = 0; hdr[hdr_wave_u(MW, 1)] = D;
+    hdr[hdr_gemv(MW, 0)] = 0;   hdr[hdr_gemv(MW, 1)] = n_gemv;
+    hdr[hdr_tile(MW, 0)] = 0;   hdr[hdr_tile(MW, 1)] = n_tiles;
+    used_off[D] = n_valid;
+    atomicAdd(stats + ST_STEPS, 1ull);
+    atomicAdd(stats + ST_DEVICE_PLANNED, 1ull);
+    atomicAdd(stats + ST_WAVES, (unsigned long long)nw);
+    atomicAdd(stats + ST_PAGE_INS, (unsigned long long)n_miss);
+    atomicAdd(stats + ST_DISTINCT, (unsigned long long)D);
+    atomicAdd(stats + ST_ENTRIES, (unsigned long long)n_valid);
+    if (s_bad) atomicAdd(stats + ST_BAD_IDS, (unsigned long long)s_bad);
+  }
+}
+
+void launch_plan_single_wave(int32_t* blk, const int32_t* ids, int n, const Dims& d,
+                             const Offsets& o, int mfma_min, int32_t* work,
+                             unsigned long long* stats, hipStream_t s) {
+  plan_single_wave_kernel<<<1, kPlanThreads, 0, s>>>(blk, ids, n, d.E, d.K, d.max_waves, o,
+                                                     mfma_min, work, stats);
+}
+
+// ------------------------------------------------------------------ page-in
+
+namespace {
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+}
+
+// Every thread of the grid takes 16-byte chunks gtid, gtid + gstride, ...,
+// kCopyUnroll loads in flight before the stores.
+__device__ __forceinline__ void copy_chunks(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                            size_t n16, size_t gtid, size_t gstride) {
+  for (size_t base = gtid; base < n16; base += kCopyUnroll * gstride) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q) {
+      size_t i = base + q * gstride;
+      if (i < n16) v[q] = src[i];
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q) {
+      size_t i = base + q * gstride;
+      if (i < n16) dst[i] = v[q];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kCopyThreads) void page_in_kernel(
+    const int32_t* __restrict__ blk, Offsets o, int wave, int K, const uint8_t* __restrict__ host_rows,
+    uint8_t* __restrict__ slots, size_t stride, size_t copy_bytes) {
+  int cnt = blk[o.plan_count + wave];
+  if (cnt > K) cnt = K;
+  const int32_t* pe_ = blk + o.plan_expert + (size_t)wave * K;
+  const int32_t* ps_ = blk + o.plan_slot + (size_t)wave * K;
+  const size_t n16 = copy_bytes / 16;
+  const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t gstride = (size_t)gridDim.x * blockDim.x;
+  for (int r = 0; r < cnt; ++r) {
+    const uint4* src = reinterpret_cast<const uint4*>(host_rows + (size_t)pe_[r] * stride);
+    uint4* dst = reinterpret_cast<uint4*>(slots + (size_t)ps_[r] * stride);
+    copy_chunks(dst, src, n16, gtid, gstride);
+  }
+}
+
+void launch_page_in(const int32_t* blk, const Offsets& o, int wave, int K,
+                    const uint8_t* host_rows, uint8_t* slots, size_t stride, size_t copy_bytes,
+                    int grid, hipStream_t s) {
+  page_in_kernel<<<grid, kCopyThreads, 0, s>>>(blk, o, wave, K, host_rows, slots, stride, copy_bytes);
+}
+
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(uint4* __restrict__ dst,
+                                                            const uint4* __restrict__ src, size_t n16) {
+  copy_chunks(dst, src, n16, (size_t)blockIdx.x * blockDim.x + threadIdx.x,
+              (size_t)gridDim.x * blockDim.x);
+}
+
+void launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t s) {
+  copy_kernel<<<grid, kCopyThreads, 0, s>>>(static_cast<uint4*>(dst), static_cast<const uint4*>(src),
+                                            bytes / 16);
+}
+
+// ------------------------------------------------------------------ GEMV expert kernels
+//
+// Weights are row-major; a row is read in 16-byte chunks by a group of LG lanes
+// (LG = 8..64, 64/LG rows per wavefront at a time): lane g of the group takes
+// chunks g, g + LG, ... so each load instruction of the wave reads contiguous
+// memory.  Each lane accumulates its chunks in fp32 for every token of the
+// expert, then the group reduces by an xor butterfly.  The arithmetic of one
+// (token, row) dot product depends only on the row length and the format, never
+// on which slot, wave or batch the expert is in.
+
+namespace {
+constexpr int kGemvThreads = 256;
+constexpr int kMaxChunksInFlight = 4;
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<PE_W_BF16> { static constexpr int VPC = 8; };        // values per 16-B chunk
+template <> struct Fmt<PE_W_FP8_B128> { static constexpr int VPC = 16; };
+template <> struct Fmt<PE_W_INT4_G128> { static constexpr int VPC = 32; };
+}  // namespace
+
+// Dot products of the chunks of one weight row with MB token vectors staged
+// in LDS as bf16 [MB][C].  `scale_at(col)` gives the multiplier of the block
+// or group containing column col (bf16: unused).
+template <int FMT, int MB>
+__device__ __forceinline__ void row_dot(const uint4* __restrict__ row, int n_ch, int lig, int LG,
+                                        const uint16_t* __restrict__ xs, int C, int m,
+                                        const float* __restrict__ s_fp8_row,   // fp8: scales of this row's 128-row block
+                                        const uint16_t* __restrict__ s_i4_row, // int4: scales of this row
+                                        float (&acc)[MB]) {
+  constexpr int VPC = Fmt<FMT>::VPC;
+  for (int c0 = lig; c0 < n_ch; c0 += LG * kMaxChunksInFlight) {
+    uint4 w[kMaxChunksInFlight];
+#pragma unroll
+    for (int q = 0; q < kMaxChunksInFlight; ++q) {
+      int c = c0 + q * LG;
+      if (c < n_ch) w[q] = row[c];
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxChunksInFlight; ++q) {
+      int c = c0 + q * LG;
+      if (c >= n_ch) break;
+      const int col = c * VPC;
+      const uint32_t wd[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+      if constexpr (FMT == PE_W_BF16) {
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+          if (t >= m) break;
+          const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * C + col);
+          const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
+          float a = acc[t];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            a = __builtin_fmaf(bf16_lo(wd[p]), bf16_lo(xd[p]), a);
+            a = __builtin_fmaf(bf16_hi(wd[p]), bf16_hi(xd[p]), a);
+          }
+          acc[t] = a;
+        }
+      } else if constexpr (FMT == PE_W_FP8_B128) {
+        // 16 e4m3 codes; the hardware conversion decodes OCP e4m3fn exactly.
+        float wf[16];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
+          auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
+          wf[4 * p + 0] = lo[0]; wf[4 * p + 1] = lo[1];
+          wf[4 * p + 2] = hi[0]; wf[4 * p + 3] = hi[1];
+        }
+        const float sc = s_fp8_row[col >> 7];
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+          if (t >= m) break;
+          const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+          const uint4 x0 = xp[0], x1 = xp[1];
+          const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float part = 0.0f;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            part = __builtin_fmaf(wf[2 * p], bf16_lo(xd[p]), part);
+            part = __builtin_fmaf(wf[2 * p + 1], bf16_hi(xd[p]), part);
+          }
+          acc[t] = __builtin_fmaf(sc, part, acc[t]);
+        }
+      } else {
+        // 32 nibbles; element 2i is the low nibble of byte i; value = nibble - 8.
+        float wf[32];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            uint32_t byte = (wd[p] >> (8 * b)) & 0xFFu;
+            wf[8 * p + 2 * b] = (float)(int)(byte & 0xFu) - 8.0f;
+            wf[8 * p + 2 * b + 1] = (float)(int)(byte >> 4) - 8.0f;
+          }
+        }
+        const float sc = half_bits_to_f32(s_i4_row[col >> 7]);
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+          if (t >= m) break;
+          const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+          float part = 0.0f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint4 xv = xp[v];
+            const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              part = __builtin_fmaf(wf[8 * v + 2 * p], bf16_lo(xd[p]), part);
+              part = __builtin_fmaf(wf[8 * v + 2 * p + 1], bf16_hi(xd[p]), part);
+            }
+          }
+          acc[t] = __builtin_fmaf(sc, part, acc[t]);
+        }
+      }
+    }
+  }
+}
+
+// Sum over the LG lanes of a group (xor butterfly; every lane gets the total).
+template <int MB>
+__device__ __forceinline__ void group_reduce(float (&acc)[MB], int LG) {
+  for (int off = LG >> 1; off > 0; off >>= 1) {
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
+  }
+}
+
+// Stage rows `entries[pos0 + t] / k` (t < mb) of a bf16 [*, C] matrix into LDS.
+__device__ __forceinline__ void stage_rows(uint16_t* xs, const uint16_t* __restrict__ src, int C,
+                                           const int32_t* __restrict__ row_idx, int mb, int divisor) {
+  const int n16 = C / 8;
+  for (int i = threadIdx.x; i < mb * n16; i += blockDim.x) {
+    int t = i / n16, c = i - t * n16;
+    int r = row_idx[t] / divisor;
+    reinterpret_cast<uint4*>(xs + t * C)[c] = reinterpret_cast<const uint4*>(src + (size_t)r * C)[c];
+  }
+}
+
+// Stage consecutive rows [pos0, pos0 + mb) of a bf16 [*, C] matrix into LDS.
+__device__ __forceinline__ void stage_consecutive(uint16_t* xs, const uint16_t* __restrict__ src, int C,
+                                                  int pos0, int mb) {
+  const int n16 = C / 8;
+  for (int i = threadIdx.x; i < mb * n16; i += blockDim.x) {
+    int t = i / n16, c = i - t * n16;
+    reinterpret_cast<uint4*>(xs + t * C)[c] = reinterpret_cast<const uint4*>(src + (size_t)(pos0 + t) * C)[c];
+  }
+}
+
+struct GemvItem {
+  int u, slot, off, m;
+};
+
+__device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvItem& it) {
+  const int32_t* hdr = a.work + a.o.hdr;
+  const int g0 = hdr[hdr_gemv(a.MW, a.wave)], g1 = hdr[hdr_gemv(a.MW, a.wave + 1)];
+  if (item >= g1 - g0) return false;
+  it.u = a.work[a.o.gemv_u + g0 + item];
+  it.slot = a.work[a.o.used_slot + it.u];
+  it.off = a.work[a.o.used_off + it.u];
+  it.m = a.work[a.o.used_off + it.u + 1] - it.off;
+  return true;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// Gate/up projection + SwiGLU for one used expert (blockIdx.y) and a range of
+// intermediate rows (blockIdx.x).  h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a, int LG, int rows_per_block) {
+  extern __shared__ __align__(16) uint16_t xs[];   // [MB][H]
+  GemvItem it;
+  if (!gemv_item(a, blockIdx.y, it)) return;
+  constexpr int VPC = Fmt<FMT>::VPC;
+  const int H = a.H, I = a.I;
+  const int n_ch = H / VPC;
+  const uint8_t* blob = a.slots + (size_t)it.slot * a.slot_stride;
+  const uint4* W13 = reinterpret_cast<const uint4*>(blob + a.off_w13);
+  const float* S13f = reinterpret_cast<const float*>(blob + a.off_s13);
+  const uint16_t* S13h = reinterpret_cast<const uint16_t*>(blob + a.off_s13);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
+  const int row_step = (kGemvThreads / 64) * groups;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(I, r0 + rows_per_block);
+  const int32_t* ent = a.work + a.o.entries + it.off;
+  for (int tb = 0; tb < it.m; tb += MB) {
+    const int mb = min(MB, it.m - tb);
+    __syncthreads();
+    stage_rows(xs, a.x, H, ent + tb, mb, a.k);
+    __syncthreads();
+    for (int i = r0 + wv * groups + grp; i < r1; i += row_step) {
+      float g[MB], u[MB];
+#pragma unroll
+      for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
+      const int ru = I + i;
+      row_dot<FMT, MB>(W13 + (size_t)i * n_ch, n_ch, lig, LG, xs, H, mb,
+                       S13f + (size_t)(i >> 7) * (H / 128), S13h + (size_t)i * (H / 128), g);
+      row_dot<FMT, MB>(W13 + (size_t)ru * n_ch, n_ch, lig, LG, xs, H, mb,
+                       S13f + (size_t)(ru >> 7) * (H / 128), S13h + (size_t)ru * (H / 128), u);
+      group_reduce<MB>(g, LG);
+      group_reduce<MB>(u, LG);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        if (t < mb && lig == t)
+          a.h[(size_t)(it.off + tb + t) * I + i] = f32_to_bf16(silu_f(g[t]) * u[t]);
+      }
+    }
+  }
+}
+
+// Down projection for one used expert: merged[entry, n] = w[entry] * (W2[n] . h[pos]).
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, int LG, int rows_per_block) {
+  extern __shared__ __align__(16) uint16_t hs[];   // [MB][I]
+  GemvItem it;
+  if (!gemv_item(a, blockIdx.y, it)) return;
+  constexpr int VPC = Fmt<FMT>::VPC;
+  const int H = a.H, I = a.I;
+  const int n_ch = I / VPC;
+  const uint8_t* blob = a.slots + (size_t)it.slot * a.slot_stride;
+  const uint4* W2 = reinterpret_cast<const uint4*>(blob + a.off_w2);
+  const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
+  const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
+  const int row_step = (kGemvThreads / 64) * groups;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(H, r0 + rows_per_block);
+  const int32_t* ent = a.work + a.o.entries + it.off;
+  for (int tb = 0; tb < it.m; tb += MB) {
+    const int mb = min(MB, it.m - tb);
+    __syncthreads();
+    stage_consecutive(hs, a.h, I, it.off + tb, mb);
+    __syncthreads();
+    for (int n = r0 + wv * groups + grp; n < r1; n += row_step) {
+      float y[MB];
+#pragma unroll
+      for (int t = 0; t < MB; ++t) y[t] = 0.0f;
+      row_dot<FMT, MB>(W2 + (size_t)n * n_ch, n_ch, lig, LG, hs, I, mb,
+                       S2f + (size_t)(n >> 7) * (I / 128), S2h + (size_t)n * (I / 128), y);
+      group_reduce<MB>(y, LG);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        if (t < mb && lig == t) {
+          const int e = ent[tb + t];
+          a.merged[(size_t)e * H + n] = a.topk_w[e] * y[t];
+        }
+      }
+    }
+  }
+}
+
+// Lanes per row: 64 when the row has a multiple of 64 chunks, else the largest
+// power of two (>= 8) dividing the chunk count, so every lane has work.
+static int lanes_per_row(int n_ch) {
+  if (n_ch % 64 == 0 || n_ch >= 256) return 64;
+  int lg = 32;
+  while (lg > 8 && n_ch % lg) lg >>= 1;
+  return lg;
+}
+
+static int pick_mb(int max_m) {
+  if (max_m <= 1) return 1;
+  if (max_m <= 2) return 2;
+  if (max_m <= 4) return 4;
+  return 8;
+}
+
+template <int FMT>
+static void gate_up_fmt(const ExpertArgs& a, int items, int mb, hipStream_t s) {
+  const int n_ch = a.H / Fmt<FMT>::VPC;
+  const int LG = lanes_per_row(n_ch);
+  const int rows_per_block = (kGemvThreads / 64) * (64 / LG) * 2;
+  dim3 grid((a.I + rows_per_block - 1) / rows_per_block, items);
+  size_t lds = (size_t)mb * a.H * 2;
+  switch (mb) {
+    case 1: gemv_gate_up_kernel<FMT, 1><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+    case 2: gemv_gate_up_kernel<FMT, 2><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+    case 4: gemv_gate_up_kernel<FMT, 4><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+    default: gemv_gate_up_kernel<FMT, 8><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+  }
+}
+
+template <int FMT>
+static void down_fmt(const ExpertArgs& a, int items, int mb, hipStream_t s) {
+  const int n_ch = a.I / Fmt<FMT>::VPC;
+  const int LG = lanes_per_row(n_ch);
+  const int rows_per_block = (kGemvThreads / 64) * (64 / LG) * 2;
+  dim3 grid((a.H + rows_per_block - 1) / rows_per_block, items);
+  size_t lds = (size_t)mb * a.I * 2;
+  switch (mb) {
+    case 1: gemv_down_kernel<FMT, 1><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+    case 2: gemv_down_kernel<FMT, 2><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+    case 4: gemv_down_kernel<FMT, 4><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+    default: gemv_down_kernel<FMT, 8><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
+  }
+}
+
+void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s) {
+  if (items <= 0) return;
+  const int mb = pick_mb(max_m);
+  if (wtype == PE_W_BF16) gate_up_fmt<PE_W_BF16>(a, items, mb, s);
+  else if (wtype == PE_W_FP8_B128) gate_up_fmt<PE_W_FP8_B128>(a, items, mb, s);
+  else gate_up_fmt<PE_W_INT4_G128>(a, items, mb, s);
+}
+
+void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s) {
+  if (items <= 0) return;
+  const int mb = pick_mb(max_m);
+  if (wtype == PE_W_BF16) down_fmt<PE_W_BF16>(a, items, mb, s);
+  else if (wtype == PE_W_FP8_B128) down_fmt<PE_W_FP8_B128>(a, items, mb, s);
+  else down_fmt<PE_W_INT4_G128>(a, items, mb, s);
+}
+
+// ------------------------------------------------------------------ top-k sum
+
+__global__ __launch_bounds__(256) void topk_sum_kernel(const float* __restrict__ merged,
+                                                       const int32_t* __restrict__ ids, int T, int k,
+                                                       int E, int H, uint16_t* __restrict__ out) {
+  const int q4 = H / 4;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)T * q4) return;
+  const int t = (int)(i / q4), c = (int)(i - (size_t)t * q4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int id = ids[t * k + j];
+    if (id < 0 || id >= E) continue;
+    const float4 v = reinterpret_cast<const float4*>(merged + ((size_t)t * k + j) * H)[c];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  ushort4 o;
+  o.x = f32_to_bf16(acc.x); o.y = f32_to_bf16(acc.y); o.z = f32_to_bf16(acc.z); o.w = f32_to_bf16(acc.w);
+  reinterpret_cast<ushort4*>(out + (size_t)t * H)[c] = o;
+}
+
+void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int E, int H,
+                     uint16_t* out, hipStream_t s) {
+  const size_t n = (size_t)T * (H / 4);
+  const int grid = (int)((n + 255) / 256);
+  topk_sum_kernel<<<grid, 256, 0, s>>>(merged, ids, T, k, E, H, out);
+}
+
+// ------------------------------------------------------------------ LRU reset
+
+__global__ void reset_lru_kernel(int32_t* blocks, size_t layer_words, int l0, Offsets o, int E, int K,
+                                 int identity) {
+  int32_t* blk = blocks + (size_t)(l0 + blockIdx.x) * layer_words;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blk[o.expert_slot + e] = identity ? e : -1;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) {
+    blk[o.slot_expert + j] = identity ? j : -1;
+    blk[o.last_use + j] = 0;
+  }
+  if (threadIdx.x == 0) { blk[o.tick] = 1; blk[o.n_waves] = 0; }
+}
+
+void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const Offsets& o,
+                      int E, int K, bool identity, hipStream_t s) {
+  if (l1 <= l0) return;
+  reset_lru_kernel<<<l1 - l0, 256, 0, s>>>(blocks, layer_words, l0, o, E, K, identity ? 1 : 0);
+}
+
+}  // namespace pe

@@ -1,0 +1,136 @@
+// Memory layout shared by the host orchestration, the host wave planner and
+// the HIP kernels of libpe.  Plain C++ (no HIP types) so the host planner can
+// be built and tested without a GPU toolchain.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace pe {
+
+constexpr int kMaxExperts = 1024;
+// An expert whose entries in one step number at least this many runs on the
+// MFMA grouped-GEMM kernels, otherwise on the GEMV kernels.  The choice depends
+// only on that count, which no wave split changes, so a paged step and an
+// unpaged step run every expert through the same arithmetic.
+constexpr int kMfmaMinTokens = 16;
+constexpr int kTileM = 32;   // token rows per MFMA tile
+
+// Device statistic counters (uint64 each).
+enum StatIdx {
+  ST_STEPS = 0, ST_DEVICE_PLANNED, ST_HOST_PLANNED, ST_WAVES, ST_PAGE_INS,
+  ST_DISTINCT, ST_ENTRIES, ST_BAD_IDS, ST_COUNT
+};
+
+struct Dims {
+  int L, E, K, k, H, I;
+  int max_tokens;
+  int max_entries;   // max_tokens * k
+  int max_waves;     // ceil(min(max_entries, E) / K)
+  int max_tiles;     // MFMA tiles one step can need
+};
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+inline Dims make_dims(int L, int E, int K, int k, int H, int I, int max_tokens) {
+  Dims d{L, E, K, k, H, I, max_tokens, max_tokens * k, 0, 0};
+  int most = d.max_entries < E ? d.max_entries : E;
+  d.max_waves = ceil_div(most, K);
+  if (d.max_waves < 1) d.max_waves = 1;
+  d.max_tiles = ceil_div(d.max_entries, kTileM) + E;
+  return d;
+}
+
+// Per-layer block (int32 words): LRU state, the last step's plans and slot map.
+struct LayerLayout {
+  size_t tick;          // [1]    uint32: tick of the next wave
+  size_t slot_expert;   // [K]    expert in slot j, -1 = empty
+  size_t expert_slot;   // [E]    slot of expert e, -1 = not resident
+  size_t last_use;      // [K]    uint32: tick of the wave that last used slot j
+  size_t n_waves;       // [1]    waves of the last step
+  size_t plan_count;    // [MW]   page-ins of wave w
+  size_t plan_expert;   // [MW*K] expert copied in
+  size_t plan_slot;     // [MW*K] slot it went to
+  size_t plan_evicted;  // [MW*K] previous occupant (-1 = empty)
+  size_t slot_of;       // [max_entries] slot entry t*k+j ran in (-1 invalid id)
+  size_t state_words;   // words of the LRU-state prefix (tick..last_use)
+  size_t total;         // words per layer (rounded to 64)
+};
+
+inline LayerLayout make_layer_layout(const Dims& d) {
+  LayerLayout l{};
+  size_t o = 0;
+  l.tick = o; o += 1;
+  l.slot_expert = o; o += d.K;
+  l.expert_slot = o; o += d.E;
+  l.last_use = o; o += d.K;
+  l.state_words = o;
+  l.n_waves = o; o += 1;
+  l.plan_count = o; o += d.max_waves;
+  l.plan_expert = o; o += (size_t)d.max_waves * d.K;
+  l.plan_slot = o; o += (size_t)d.max_waves * d.K;
+  l.plan_evicted = o; o += (size_t)d.max_waves * d.K;
+  l.slot_of = o; o += d.max_entries;
+  l.total = (o + 63) / 64 * 64;
+  return l;
+}
+
+// Step work arena (int32 words), shared by all layers (steps run in stream order).
+// "Used" experts are those with at least one valid entry; they are numbered u in
+// wave order and, inside a wave, by ascending expert id.  Entries of used expert
+// u occupy sorted positions [used_off[u], used_off[u+1]) in ascending entry index.
+struct WorkLayout {
+  size_t hdr;           // header, see hdr_* below
+  size_t used_expert;   // [E]
+  size_t used_slot;     // [E]
+  size_t used_off;      // [E+1]
+  size_t gemv_u;        // [E]          used experts on the GEMV kernels, per wave
+  size_t tile_u;        // [max_tiles]  MFMA tiles: used expert
+  size_t tile_row;      // [max_tiles]  MFMA tiles: first row inside the expert
+  size_t entries;       // [max_entries] entry index t*k+j at each sorted position
+  size_t total;
+};
+
+// Header words (constexpr, so kernels can use them too): [0] n_waves, then wave_u_begin[MW+1], gemv_begin[MW+1], tile_begin[MW+1].
+constexpr size_t hdr_wave_u(int MW, int w) { return (void)MW, 1 + (size_t)w; }
+constexpr size_t hdr_gemv(int MW, int w) { return 1 + (size_t)(MW + 1) + w; }
+constexpr size_t hdr_tile(int MW, int w) { return 1 + 2 * (size_t)(MW + 1) + w; }
+constexpr size_t hdr_words(int MW) { return 1 + 3 * (size_t)(MW + 1); }
+
+inline WorkLayout make_work_layout(const Dims& d) {
+  WorkLayout w{};
+  size_t o = 0;
+  w.hdr = o; o += (hdr_words(d.max_waves) + 15) / 16 * 16;
+  w.used_expert = o; o += d.E;
+  w.used_slot = o; o += d.E;
+  w.used_off = o; o += d.E + 1;
+  w.gemv_u = o; o += d.E;
+  w.tile_u = o; o += d.max_tiles;
+  w.tile_row = o; o += d.max_tiles;
+  w.entries = o; o += d.max_entries;
+  w.total = (o + 63) / 64 * 64;
+  return w;
+}
+
+// Result of one host-planned step, beyond what is written into the layer
+// block and the work arena.
+struct HostPlanSummary {
+  int n_waves;
+  int distinct;
+  int page_ins;
+  int valid_entries;
+  int bad_ids;
+  int max_gemv_tokens;   // largest entry count among GEMV experts
+  int gemv_items[kMaxExperts];   // per wave: experts on the GEMV kernels
+  int tiles[kMaxExperts];        // per wave: MFMA tiles
+};
+
+// Plan one step of one layer on the host (the multi-wave path).  `blk` is a
+// host mirror of the layer block holding the current LRU state; on return it
+// holds the new state, the plans of every wave and the slot map.  `work` is a
+// host mirror of the work arena, filled for the step.  Returns 0 or -1 if the
+// step needs more waves than the layout holds.
+int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
+                   const int32_t* ids, int n_entries, int32_t* blk, int32_t* work,
+                   HostPlanSummary* sum);
+
+}  // namespace pe

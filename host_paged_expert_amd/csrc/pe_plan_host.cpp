@@ -1,0 +1,140 @@
+// Host wave planner of libpe: the multi-wave step of one layer.
+//
+// SGLang "Paged Experts" docs page, "A step: waves, page-in, merge", steps 1-2:
+// the distinct experts a step routes to are split into waves of at most K,
+// already-resident experts first; each wave makes its experts resident,
+// evicting the least recently used experts outside the wave, and copies only
+// the missing ones.  "Captured decode": steps that do not fit one wave are
+// planned on the host, sharing the LRU state with device-planned steps.
+//
+// Readings where the page is silent (the device planner makes the same ones):
+// resident-first order with ascending ids inside each part; waves are
+// consecutive chunks of K; a wave is one use (all its experts get the current
+// tick, then the tick advances); victims are slots whose expert is outside the
+// wave, by ascending (last_use, slot); the i-th missing expert (ascending id)
+// takes the i-th victim; ids outside [0, E) are ignored.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "pe_layout.h"
+
+namespace pe {
+
+int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
+                   const int32_t* ids, int n_entries, int32_t* blk, int32_t* work,
+                   HostPlanSummary* sum) {
+  const int E = d.E, K = d.K, MW = d.max_waves;
+  uint32_t tick = (uint32_t)blk[ll.tick];
+  int32_t* slot_expert = blk + ll.slot_expert;
+  int32_t* expert_slot = blk + ll.expert_slot;
+  uint32_t* last_use = reinterpret_cast<uint32_t*>(blk + ll.last_use);
+  int32_t* slot_of = blk + ll.slot_of;
+
+  std::vector<int> cnt(E, 0);
+  int bad = 0, valid = 0;
+  for (int i = 0; i < n_entries; ++i) {
+    int e = ids[i];
+    if (e < 0 || e >= E) { ++bad; continue; }
+    ++cnt[e];
+    ++valid;
+  }
+  std::vector<int> order;
+  for (int e = 0; e < E; ++e) if (cnt[e] && expert_slot[e] >= 0) order.push_back(e);
+  for (int e = 0; e < E; ++e) if (cnt[e] && expert_slot[e] < 0) order.push_back(e);
+  const int D = (int)order.size();
+  const int n_waves = ceil_div(D, K);
+  if (n_waves > MW) return -1;
+
+  int32_t* hdr = work + wl.hdr;
+  int32_t* used_expert = work + wl.used_expert;
+  int32_t* used_slot = work + wl.used_slot;
+  int32_t* used_off = work + wl.used_off;
+  int32_t* gemv_u = work + wl.gemv_u;
+  int32_t* tile_u = work + wl.tile_u;
+  int32_t* tile_row = work + wl.tile_row;
+  int32_t* entries = work + wl.entries;
+
+  std::vector<int> u_of(E, -1), in_wave(E, -1);
+  std::vector<std::pair<uint32_t, int>> cand;
+  int u = 0, off = 0, ng = 0, nt = 0, page_ins = 0, max_gemv = 0;
+  hdr[0] = n_waves;
+  hdr[hdr_wave_u(MW, 0)] = 0;
+  hdr[hdr_gemv(MW, 0)] = 0;
+  hdr[hdr_tile(MW, 0)] = 0;
+  for (int w = 0; w < n_waves; ++w) {
+    const int b = w * K, n = std::min(K, D - b);
+    for (int i = 0; i < n; ++i) in_wave[order[b + i]] = w;
+    // victims: slots whose occupant is outside this wave, by (last_use, slot)
+    cand.clear();
+    for (int j = 0; j < K; ++j) {
+      int occ = slot_expert[j];
+      if (occ < 0 || in_wave[occ] != w) cand.push_back({last_use[j], j});
+    }
+    std::sort(cand.begin(), cand.end());
+    int r = 0;
+    int32_t* pe_ = blk + ll.plan_expert + (size_t)w * K;
+    int32_t* ps_ = blk + ll.plan_slot + (size_t)w * K;
+    int32_t* pv_ = blk + ll.plan_evicted + (size_t)w * K;
+    for (int i = 0; i < n; ++i) {
+      int e = order[b + i];
+      if (expert_slot[e] >= 0) continue;
+      int j = cand[r].second;
+      int old = slot_expert[j];
+      if (old >= 0) expert_slot[old] = -1;
+      slot_expert[j] = e;
+      expert_slot[e] = j;
+      pe_[r] = e; ps_[r] = j; pv_[r] = old;
+      ++r;
+    }
+    blk[ll.plan_count + w] = r;
+    page_ins += r;
+    for (int i = 0; i < n; ++i) last_use[expert_slot[order[b + i]]] = tick;
+    ++tick;
+    // used experts of this wave, ascending id
+    std::vector<int> wave(order.begin() + b, order.begin() + b + n);
+    std::sort(wave.begin(), wave.end());
+    int g0 = ng, t0 = nt;
+    for (int e : wave) {
+      u_of[e] = u;
+      used_expert[u] = e;
+      used_slot[u] = expert_slot[e];
+      used_off[u] = off;
+      off += cnt[e];
+      if (cnt[e] < kMfmaMinTokens) {
+        gemv_u[ng++] = u;
+        max_gemv = std::max(max_gemv, cnt[e]);
+      } else {
+        for (int q = 0; q < cnt[e]; q += kTileM) { tile_u[nt] = u; tile_row[nt] = q; ++nt; }
+      }
+      ++u;
+    }
+    hdr[hdr_wave_u(MW, w + 1)] = u;
+    hdr[hdr_gemv(MW, w + 1)] = ng;
+    hdr[hdr_tile(MW, w + 1)] = nt;
+    sum->gemv_items[w] = ng - g0;
+    sum->tiles[w] = nt - t0;
+  }
+  used_off[u] = off;
+  // entries in ascending index at their expert's positions; slot map at wave time
+  std::vector<int> seen(E, 0);
+  for (int i = 0; i < n_entries; ++i) {
+    int e = ids[i];
+    if (e < 0 || e >= E) { slot_of[i] = -1; continue; }
+    int uu = u_of[e];
+    entries[used_off[uu] + seen[e]++] = i;
+    slot_of[i] = used_slot[uu];
+  }
+  blk[ll.tick] = (int32_t)tick;
+  blk[ll.n_waves] = n_waves;
+
+  sum->n_waves = n_waves;
+  sum->distinct = D;
+  sum->page_ins = page_ins;
+  sum->valid_entries = valid;
+  sum->bad_ids = bad;
+  sum->max_gemv_tokens = max_gemv;
+  return 0;
+}
+
+}  // namespace pe

@@ -1,0 +1,294 @@
+"""GPU parity of libpe against the CPU oracle (MI355X only).
+
+- Plans, LRU state and slot maps are bit-exact against the oracle's simulator.
+- Outputs are within max|gpu - ref| <= 1e-2 * max|ref| (bf16, FP8) or 2e-2
+  (int4) of the oracle's fp32 unpaged layer.
+- Paged output is bit-identical to an unpaged run of the same kernels
+  (PE_FLAG_UNPAGED: K = E, every expert resident), for every K.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+import harness
+import host_paged_expert_amd as pe
+from oracle import formats, moe
+from oracle.lru import LayerLRU
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2}
+
+
+def _expert_fn(wl, layer):
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = formats.dequant_expert(wl.wtype, *synth.expert_tensors(wl, layer, e))
+        return cache[e]
+    return get
+
+
+def _check_close(got_bits, ref, wtype, what=""):
+    got = harness.bf16_to_f32(got_bits)
+    err = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    assert err <= TOL[wtype] * scale, "%s: max|d|=%g, max|ref|=%g" % (what, err, scale)
+
+
+def _check_plan(moe_obj, layer, waves, T, k, ids_flat):
+    st = torch.cuda.current_stream()
+    nw = None
+    for w, wv in enumerate(waves):
+        p = moe_obj.plan(layer, w, st)
+        nw = p["n_waves"]
+        assert p["count"] == wv.count, (w, p, wv)
+        assert p["experts"].tolist() == wv.plan_experts
+        assert p["slots"].tolist() == wv.plan_slots
+        assert p["evicted"].tolist() == wv.evicted
+    if waves:
+        assert nw == len(waves)
+    sm = moe_obj.slot_map(layer, T, st)
+    want = []
+    for e in ids_flat:
+        e = int(e)
+        s = -1
+        for wv in waves:
+            if e in wv.slot_of:
+                s = wv.slot_of[e]
+        want.append(s)
+    assert sm.tolist() == want
+
+
+def _check_state(moe_obj, layer, sim):
+    se, lu, tick = moe_obj.lru_state(layer, torch.cuda.current_stream())
+    assert se.tolist() == sim.slot_expert
+    assert lu.tolist() == sim.last_use
+    assert tick == sim.tick
+
+
+def _run_decode(wl, flags=0, steps=None, check_oracle=True, sims=None, collect=True):
+    """Run the workload's decode steps eagerly; check plans/state every step."""
+    steps = wl.steps if steps is None else steps
+    r = synth.routing_for(wl)
+    m = harness.make_moe(wl, flags=flags)
+    harness.load_store(m, wl)
+    x, ids, w = harness.decode_inputs(wl, r, DEV, steps)
+    B, H, k = wl.batch, wl.hidden, wl.top_k
+    out = torch.empty((steps, wl.layers, B, H), dtype=torch.bfloat16, device=DEV)
+    unpaged = bool(flags & pe.PE_FLAG_UNPAGED)
+    sims = sims if sims is not None else [LayerLRU(wl.experts, m.K) for _ in range(wl.layers)]
+    fns = [_expert_fn(wl, l) for l in range(wl.layers)]
+    for s in range(steps):
+        for l in range(wl.layers):
+            m.forward(l, x[s], ids[s, l], w[s, l], out[s, l])
+            if not unpaged:
+                waves = sims[l].step(r["decode_ids"][s, l].ravel())
+                _check_plan(m, l, waves, B, k, r["decode_ids"][s, l].ravel())
+                _check_state(m, l, sims[l])
+            if check_oracle:
+                xr = formats.bf16_to_f32(harness.bf16_bits(x[s]))
+                ref = moe.moe_layer(xr, r["decode_ids"][s, l], r["decode_w"][s, l], fns[l])
+                _check_close(harness.bf16_bits(out[s, l]), ref, wl.wtype, "step %d layer %d" % (s, l))
+    torch.cuda.synchronize()
+    res = harness.bf16_bits(out) if collect else None
+    stats = m.stats()
+    m.close()
+    return res, stats
+
+
+def test_tiny_workload_vs_oracle_and_simulator():
+    wl = synth.WORKLOADS["tiny_bf16"]
+    print("case tiny_bf16 K=%d" % wl.resident, flush=True)
+    out, st = _run_decode(wl)
+    assert st["steps"] == wl.steps and st["device_planned"] == wl.steps and st["bad_ids"] == 0
+
+
+def test_tiny_paged_bit_identical_to_unpaged_for_every_k():
+    base = synth.WORKLOADS["tiny_bf16"]
+    ref, _ = _run_decode(base, flags=pe.PE_FLAG_UNPAGED, check_oracle=False)
+    for K in range(base.top_k, base.experts + 1):
+        print("case tiny_bf16 K=%d vs unpaged" % K, flush=True)
+        wl = synth.workload("tiny_bf16", resident=K)
+        got, _ = _run_decode(wl, check_oracle=False)
+        assert np.array_equal(got, ref), K
+
+
+SMALL = dict(layers=2, experts=16, top_k=4, hidden=256, inter=256, steps=10)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4"])
+@pytest.mark.parametrize("batch,K", [(1, 6), (3, 6), (2, 8)])
+def test_small_formats_paged_vs_oracle_and_unpaged(wtype, batch, K):
+    """Device-planned (batch*k <= K) and host-planned multi-wave (batch*k > K)
+    steps, three formats, against the oracle and an unpaged run."""
+    wl = synth.workload("decode_bf16_k40_b1", wtype=wtype, batch=batch, resident=K, **SMALL)
+    print("case small %s B=%d K=%d" % (wtype, batch, K), flush=True)
+    got, st = _run_decode(wl)
+    if batch * wl.top_k > K:
+        assert st["host_planned"] == wl.steps * wl.layers
+    else:
+        assert st["device_planned"] == wl.steps * wl.layers
+    ref, _ = _run_decode(wl, flags=pe.PE_FLAG_UNPAGED, check_oracle=False)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int4"])
+def test_ragged_shapes(wtype):
+    """Row lengths that leave lanes idle and token batches past the GEMV batch."""
+    H, I = (384, 640) if wtype == "int4" else (200, 72)
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=12, top_k=3, resident=12, hidden=H, inter=I,
+                        wtype=wtype, batch=5, steps=3)
+    print("case ragged %s H=%d I=%d" % (wtype, H, I), flush=True)
+    _run_decode(wl)
+
+
+def test_force_host_plan_and_dma_match_device_plan_bitwise():
+    wl = synth.workload("decode_bf16_k40_b1", wtype="fp8", batch=1, resident=6, **SMALL)
+    print("case host-plan/dma equivalence", flush=True)
+    a, sa = _run_decode(wl, check_oracle=False)
+    b, sb = _run_decode(wl, flags=pe.PE_FLAG_FORCE_HOST_PLAN, check_oracle=False)
+    c, sc = _run_decode(wl, flags=pe.PE_FLAG_FORCE_HOST_PLAN | pe.PE_FLAG_PAGEIN_DMA, check_oracle=False)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert sb["host_planned"] == wl.steps * wl.layers and sa["device_planned"] == wl.steps * wl.layers
+    for key in ("page_ins", "distinct", "entries", "waves"):
+        assert sa[key] == sb[key] == sc[key], key
+
+
+def test_stats_count_simulator_misses():
+    wl = synth.workload("decode_bf16_k40_b1", batch=2, resident=5, **SMALL)
+    sims = [LayerLRU(wl.experts, wl.resident) for _ in range(wl.layers)]
+    _, st = _run_decode(wl, check_oracle=False, sims=sims)
+    r = synth.routing_for(wl)
+    misses = distinct = 0
+    check = [LayerLRU(wl.experts, wl.resident) for _ in range(wl.layers)]
+    for s in range(wl.steps):
+        for l in range(wl.layers):
+            ids = r["decode_ids"][s, l].ravel()
+            misses += sum(w.count for w in check[l].step(ids))
+            distinct += len(set(ids.tolist()))
+    assert st["page_ins"] == misses and st["distinct"] == distinct
+    _, copied = pe.pe_expert_bytes("bf16", wl.hidden, wl.inter)
+    assert st["page_in_bytes"] == misses * copied
+
+
+def test_invalid_ids_are_counted_and_contribute_nothing():
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=8, top_k=2, resident=4, hidden=64, inter=128,
+                        batch=2, steps=1)
+    print("case invalid ids", flush=True)
+    m = harness.make_moe(wl)
+    harness.load_store(m, wl)
+    x = torch.from_numpy(synth.hidden_states(wl, 0, 2).view(np.int16)).view(torch.bfloat16).to(DEV)
+    ids_np = np.array([[3, 9], [-2, 5]], np.int32)
+    w_np = np.array([[0.5, 0.5], [0.25, 0.75]], np.float32)
+    out = torch.empty((2, 64), dtype=torch.bfloat16, device=DEV)
+    m.forward(0, x, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), out)
+    torch.cuda.synchronize()
+    assert m.stats()["bad_ids"] == 2
+    ref = moe.moe_layer(formats.bf16_to_f32(harness.bf16_bits(x)), ids_np, w_np, _expert_fn(wl, 0), num_experts=8)
+    _check_close(harness.bf16_bits(out), ref, "bf16")
+    assert m.slot_map(0, 2).tolist()[1] == -1 and m.slot_map(0, 2).tolist()[2] == -1
+    m.close()
+
+
+def test_zero_tokens_is_a_noop():
+    wl = synth.workload("tiny_bf16")
+    m = harness.make_moe(wl)
+    out = torch.zeros((1, wl.hidden), dtype=torch.bfloat16, device=DEV)
+    m.forward(0, out, torch.zeros((1, 2), dtype=torch.int32, device=DEV),
+              torch.zeros((1, 2), dtype=torch.float32, device=DEV), out, T=0)
+    assert m.stats()["steps"] == 0
+    m.close()
+
+
+def _graph_case(wl):
+    r = synth.routing_for(wl)
+    m = harness.make_moe(wl)
+    harness.load_store(m, wl)
+    x, ids, w = harness.decode_inputs(wl, r, DEV)
+    return r, m, x, ids, w
+
+
+def test_captured_graph_matches_eager():
+    """Capture one decode step of every layer into a hipGraph; replay it over
+    the steps (inputs copied in between replays) and compare bit-for-bit with
+    an eager run from the same cold state, plans included."""
+    wl = synth.workload("decode_bf16_k40_b1", wtype="int4", batch=2, resident=8, **SMALL)
+    print("case graph capture", flush=True)
+    r, m, x, ids, w = _graph_case(wl)
+    L, B, H = wl.layers, wl.batch, wl.hidden
+    # eager reference
+    eager = torch.empty((wl.steps, L, B, H), dtype=torch.bfloat16, device=DEV)
+    for s in range(wl.steps):
+        for l in range(L):
+            m.forward(l, x[s], ids[s, l], w[s, l], eager[s, l])
+    torch.cuda.synchronize()
+    st_eager = [m.lru_state(l) for l in range(L)]
+    m.reset_lru()
+    m.reset_stats()
+    xin = torch.empty_like(x[0])
+    iin = torch.empty_like(ids[0])
+    win = torch.empty_like(w[0])
+    oout = torch.empty((L, B, H), dtype=torch.bfloat16, device=DEV)
+    xin.copy_(x[0]); iin.copy_(ids[0]); win.copy_(w[0])
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for l in range(L):
+                m.forward(l, xin, iin[l], win[l], oout[l], stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    m.reset_lru()          # capture does not run the kernels; start cold like the eager run
+    m.reset_stats()
+    torch.cuda.synchronize()
+    for s in range(wl.steps):
+        xin.copy_(x[s]); iin.copy_(ids[s]); win.copy_(w[s])
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(harness.bf16_bits(oout), harness.bf16_bits(eager[s])), s
+    for l in range(L):
+        se, lu, tick = m.lru_state(l)
+        assert np.array_equal(se, st_eager[l][0]) and np.array_equal(lu, st_eager[l][1]) and tick == st_eager[l][2]
+    assert m.stats()["device_planned"] == wl.steps * L
+    m.close()
+
+
+def test_host_planned_step_refuses_capture():
+    wl = synth.workload("decode_bf16_k40_b1", batch=3, resident=6, **SMALL)
+    r, m, x, ids, w = _graph_case(wl)
+    out = torch.empty((wl.batch, wl.hidden), dtype=torch.bfloat16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    rc = None
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            rc = pe.pe_forward_rc(m.ctx, 0, x[0], ids[0, 0], w[0, 0], wl.batch, out, side)
+    torch.cuda.synchronize()
+    assert rc == pe.PE_ERR_NOT_CAPTURABLE
+    assert m.stats()["steps"] == 0
+    m.close()
+
+
+def test_reset_lru_midway_matches_resetting_simulator():
+    wl = synth.workload("decode_bf16_k40_b1", batch=1, resident=5, **SMALL)
+    r = synth.routing_for(wl)
+    m = harness.make_moe(wl)
+    harness.load_store(m, wl)
+    x, ids, w = harness.decode_inputs(wl, r, DEV)
+    sims = [LayerLRU(wl.experts, wl.resident) for _ in range(wl.layers)]
+    out = torch.empty((wl.batch, wl.hidden), dtype=torch.bfloat16, device=DEV)
+    for s in range(wl.steps):
+        if s == 4:
+            m.reset_lru(1)
+            sims[1].reset()
+        for l in range(wl.layers):
+            m.forward(l, x[s], ids[s, l], w[s, l], out)
+            waves = sims[l].step(r["decode_ids"][s, l].ravel())
+            _check_plan(m, l, waves, wl.batch, wl.top_k, r["decode_ids"][s, l].ravel())
+            _check_state(m, l, sims[l])
+    m.close()
