@@ -52,6 +52,11 @@ void launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t
 void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
 void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
 
+// MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
+// tokens).  Need H and I multiples of 128.
+void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);
+void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);
+
 // out[t] = bf16(sum_j merged[t,j]) over valid entries, j in order.
 void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int E, int H,
                      uint16_t* out, hipStream_t s);

@@ -626,6 +626,262 @@ void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipS
   else down_fmt<PE_W_INT4_G128>(a, items, mb, s);
 }
 
+// ------------------------------------------------------------------ MFMA grouped GEMM
+//
+// Experts with at least kMfmaMinTokens entries in a step (prefill waves) run on
+// v_mfma_f32_16x16x32_bf16.  A block computes a tile of kTileM = 32 token rows
+// of one used expert against 64 weight rows, staging K in blocks of 128 through
+// LDS (rows padded by 8 bf16 against bank conflicts).  FP8 and int4 weights are
+// decoded into LDS as exact bf16 (every e4m3 value and every nibble - 8 is a
+// bf16 number); their block / group scale multiplies the fp32 partial product
+// of each 128-wide K block.  Every output element's arithmetic depends only on
+// its own token row and weight row, never on the other rows of the tile.
+
+namespace {
+constexpr int kMfmaThreads = 256;
+constexpr int kNT = 64;          // weight rows per block (16 per wavefront)
+constexpr int kKB = 128;         // K per LDS stage = one FP8 block / int4 group
+constexpr int kLdsRow = kKB + 8; // padded LDS row, bf16 elements
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+}  // namespace
+
+// Decode one 16-byte chunk of weights of format FMT into bf16 in LDS at `dst`
+// (VPC values); returns nothing, writes VPC/8 16-byte LDS words.
+template <int FMT>
+__device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst) {
+  if constexpr (FMT == PE_W_BF16) {
+    *reinterpret_cast<uint4*>(dst) = w;
+  } else if constexpr (FMT == PE_W_FP8_B128) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
+      // e4m3 values have at most 4 significant bits: the top half of the fp32 is exact
+      o[2 * p] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+      o[2 * p + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+    }
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[16];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t byte = (wd[p] >> (8 * b)) & 0xFFu;
+        const float lo = (float)(int)(byte & 0xFu) - 8.0f, hi = (float)(int)(byte >> 4) - 8.0f;
+        o[4 * p + b] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<uint4*>(dst)[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  }
+}
+
+// Stage kNT weight rows [row0, row0 + kNT) x K block kb of a row-major matrix with
+// C columns into LDS (bf16, padded rows).
+template <int FMT>
+__device__ __forceinline__ void stage_weights(uint16_t* sB, const uint8_t* __restrict__ W, int C, int row0,
+                                              int kb) {
+  constexpr int VPC = Fmt<FMT>::VPC;
+  constexpr int CPR = kKB / VPC;                       // chunks per row per stage
+  const size_t row_bytes = (size_t)C * (FMT == PE_W_BF16 ? 2 : FMT == PE_W_FP8_B128 ? 1 : 0) +
+                           (FMT == PE_W_INT4_G128 ? (size_t)C / 2 : 0);
+  const uint4* base = reinterpret_cast<const uint4*>(W);
+  for (int i = threadIdx.x; i < kNT * CPR; i += kMfmaThreads) {
+    const int r = i / CPR, c = i - r * CPR;
+    const size_t chunk = ((size_t)(row0 + r) * row_bytes) / 16 + (size_t)kb * CPR + c;
+    decode_chunk_to_lds<FMT>(base[chunk], sB + r * kLdsRow + c * VPC);
+  }
+}
+
+// Gate/up + SwiGLU on MFMA: tile (blockIdx.y within the wave's tiles) x 64
+// intermediate rows (blockIdx.x).
+template <int FMT>
+__global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a) {
+  __shared__ __align__(16) uint16_t sA[kTileM * kLdsRow];
+  __shared__ __align__(16) uint16_t sG[kNT * kLdsRow];
+  __shared__ __align__(16) uint16_t sU[kNT * kLdsRow];
+  __shared__ int sTok[kTileM];
+  const int32_t* hdr = a.work + a.o.hdr;
+  const int t0 = hdr[hdr_tile(a.MW, a.wave)], t1 = hdr[hdr_tile(a.MW, a.wave + 1)];
+  const int tile = t0 + blockIdx.y;
+  if (tile >= t1) return;
+  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
+  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
+  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  const int H = a.H, I = a.I;
+  const int n0 = blockIdx.x * kNT;
+  const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
+  const uint8_t* W13 = blob + a.off_w13;
+  const float* S13f = reinterpret_cast<const float*>(blob + a.off_s13);
+  const uint16_t* S13h = reinterpret_cast<const uint16_t*>(blob + a.off_s13);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ln = lane & 15, lk = lane >> 4;
+  if (threadIdx.x < kTileM)
+    sTok[threadIdx.x] = threadIdx.x < rows ? a.work[a.o.entries + off + row0 + threadIdx.x] / a.k : -1;
+  f32x4_t accg[2], accu[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { accg[h][i] = 0.f; accu[h][i] = 0.f; }
+  const int ncol = n0 + 16 * wv + ln;     // this lane's output column (intermediate row)
+  for (int kb = 0; kb < H / kKB; ++kb) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTileM * (kKB / 8); i += kMfmaThreads) {
+      const int r = i / (kKB / 8), c = i - r * (kKB / 8);
+      const int tok = sTok[r];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (tok >= 0) v = reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + kb * kKB)[c];
+      *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = v;
+    }
+    stage_weights<FMT>(sG, W13, H, n0, kb);
+    stage_weights<FMT>(sU, W13, H, I + n0, kb);
+    __syncthreads();
+    f32x4_t pg[2], pu[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { pg[h][i] = 0.f; pu[h][i] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < kKB / 32; ++ks) {
+      const int kc = ks * 32 + 8 * lk;
+      const bf16x8_t bg = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sG + (16 * wv + ln) * kLdsRow + kc));
+      const bf16x8_t bu = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sU + (16 * wv + ln) * kLdsRow + kc));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (16 * h + ln) * kLdsRow + kc));
+        pg[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, pg[h], 0, 0, 0);
+        pu[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, pu[h], 0, 0, 0);
+      }
+    }
+    float sg = 1.f, su = 1.f;
+    if constexpr (FMT == PE_W_FP8_B128) {
+      sg = S13f[(size_t)(n0 >> 7) * (H / 128) + kb];
+      su = S13f[(size_t)((I + n0) >> 7) * (H / 128) + kb];
+    } else if constexpr (FMT == PE_W_INT4_G128) {
+      sg = half_bits_to_f32(S13h[(size_t)ncol * (H / 128) + kb]);
+      su = half_bits_to_f32(S13h[(size_t)(I + ncol) * (H / 128) + kb]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FMT == PE_W_BF16) {
+          accg[h][i] += pg[h][i];
+          accu[h][i] += pu[h][i];
+        } else {
+          accg[h][i] = __builtin_fmaf(sg, pg[h][i], accg[h][i]);
+          accu[h][i] = __builtin_fmaf(su, pu[h][i], accu[h][i]);
+        }
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * h + 4 * lk + i;
+      if (r < rows)
+        a.h[(size_t)(off + row0 + r) * I + ncol] = f32_to_bf16(silu_f(accg[h][i]) * accu[h][i]);
+    }
+}
+
+// Down projection x router weight on MFMA: tile x 64 output columns.
+template <int FMT>
+__global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
+  __shared__ __align__(16) uint16_t sA[kTileM * kLdsRow];
+  __shared__ __align__(16) uint16_t sB[kNT * kLdsRow];
+  const int32_t* hdr = a.work + a.o.hdr;
+  const int t0 = hdr[hdr_tile(a.MW, a.wave)], t1 = hdr[hdr_tile(a.MW, a.wave + 1)];
+  const int tile = t0 + blockIdx.y;
+  if (tile >= t1) return;
+  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
+  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
+  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  const int H = a.H, I = a.I;
+  const int n0 = blockIdx.x * kNT;
+  const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
+  const uint8_t* W2 = blob + a.off_w2;
+  const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
+  const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ln = lane & 15, lk = lane >> 4;
+  f32x4_t acc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+  const int ncol = n0 + 16 * wv + ln;
+  for (int kb = 0; kb < I / kKB; ++kb) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTileM * (kKB / 8); i += kMfmaThreads) {
+      const int r = i / (kKB / 8), c = i - r * (kKB / 8);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < rows) v = reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB)[c];
+      *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = v;
+    }
+    stage_weights<FMT>(sB, W2, I, n0, kb);
+    __syncthreads();
+    f32x4_t p[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[h][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKB / 32; ++ks) {
+      const int kc = ks * 32 + 8 * lk;
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sB + (16 * wv + ln) * kLdsRow + kc));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (16 * h + ln) * kLdsRow + kc));
+        p[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, p[h], 0, 0, 0);
+      }
+    }
+    float sc = 1.f;
+    if constexpr (FMT == PE_W_FP8_B128) sc = S2f[(size_t)(n0 >> 7) * (I / 128) + kb];
+    else if constexpr (FMT == PE_W_INT4_G128) sc = half_bits_to_f32(S2h[(size_t)ncol * (I / 128) + kb]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FMT == PE_W_BF16) acc[h][i] += p[h][i];
+        else acc[h][i] = __builtin_fmaf(sc, p[h][i], acc[h][i]);
+      }
+  }
+  const int32_t* ent = a.work + a.o.entries + off + row0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * h + 4 * lk + i;
+      if (r < rows) {
+        const int e = ent[r];
+        a.merged[(size_t)e * H + ncol] = a.topk_w[e] * acc[h][i];
+      }
+    }
+}
+
+void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) {
+  if (tiles <= 0) return;
+  dim3 grid(a.I / kNT, tiles);
+  if (wtype == PE_W_BF16) mfma_gate_up_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
+  else if (wtype == PE_W_FP8_B128) mfma_gate_up_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
+  else mfma_gate_up_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
+}
+
+void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) {
+  if (tiles <= 0) return;
+  dim3 grid(a.H / kNT, tiles);
+  if (wtype == PE_W_BF16) mfma_down_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
+  else if (wtype == PE_W_FP8_B128) mfma_down_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
+  else mfma_down_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
+}
+
 // ------------------------------------------------------------------ top-k sum
 
 __global__ __launch_bounds__(256) void topk_sum_kernel(const float* __restrict__ merged,
