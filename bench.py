@@ -42,9 +42,17 @@ def parse():
     ap.add_argument("--workload", default="decode_bf16_k40_b1")
     ap.add_argument("--cpu-samples", type=int, default=None, help="decode steps the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU oracle time to sample")
     ap.add_argument("--no-timing-pass", action="store_true")
     ap.add_argument("--dma", action="store_true", help="host-planned page-in with hipMemcpyAsync")
     ap.add_argument("--repeats", type=int, default=2, help="timed repetitions (best and median reported)")
+    ap.add_argument("--eager", action="store_true",
+                    help="profiling: run device-planned steps without the hipGraph (per-dispatch counters)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="profiling: fewer MoE layers (never used for the reported number)")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="profiling: first run one plain device-to-device copy of this many MiB, "
+                         "a known-size kernel to scale memory counters by")
     return ap.parse_args()
 
 
@@ -64,11 +72,24 @@ def main():
     base = synth.WORKLOADS[args.workload]
     steps = args.steps or base.steps
     warmup = max(0, args.warmup)
-    wl = synth.workload(args.workload, steps=max(steps, warmup, base.steps))
+    over = {"steps": max(steps, warmup, base.steps)}
+    if args.layers:
+        over["layers"] = args.layers
+    wl = synth.workload(args.workload, **over)
     dev = "cuda:0"
     torch.cuda.init()
+    if args.copy_reference:
+        n = args.copy_reference << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("reference copy: %d MiB device-to-device" % args.copy_reference)
+        del src, dst
     flags = pe.PE_FLAG_PAGEIN_DMA if args.dma else 0
-    captured = wl.batch * wl.top_k <= wl.resident
+    device_planned = wl.batch * wl.top_k <= wl.resident
+    captured = device_planned and not args.eager
 
     t0 = time.time()
     m = harness.make_moe(wl, flags=flags)
@@ -88,6 +109,21 @@ def main():
     L, B, H = wl.layers, wl.batch, wl.hidden
     out = torch.empty((L, B, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+
+    # Prefill workloads: a cold chunk of prefill_tokens tokens through every layer
+    # (host-planned waves, MFMA expert kernels), then the decode continuation.
+    has_prefill = wl.routing == "prefill_zipf"
+    if has_prefill:
+        Tp = wl.prefill_tokens
+        xp_np = synth.hidden_states(wl, -1, Tp)
+        xp = torch.from_numpy(xp_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        idsp = torch.from_numpy(np.ascontiguousarray(routing["prefill_ids"])).to(dev)
+        wp = torch.from_numpy(np.ascontiguousarray(routing["prefill_w"])).to(dev)
+        outp = torch.empty((L, Tp, H), dtype=torch.bfloat16, device=dev)
+
+    def run_prefill():
+        for l in range(L):
+            m.forward(l, xp, idsp[l], wp[l], outp[l], stream=stream)
 
     graph = None
     sidx = torch.zeros(1, dtype=torch.long, device=dev)
@@ -124,14 +160,33 @@ def main():
         torch.cuda.synchronize()
         m.reset_stats()
 
+    def diff(a, b):
+        return {k: a[k] - b[k] for k in a}
+
     # warm-up (untimed), then timed repetitions from a cold slot table
     cold()
+    if has_prefill:
+        run_prefill()
     run(warmup)
     torch.cuda.synchronize()
     times = []
     stats = None
+    prefill_ms, prefill_stats = [], None
     for rep in range(max(1, args.repeats)):
         cold()
+        before = m.stats()
+        if has_prefill:
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            run_prefill()
+            p1.record(stream)
+            torch.cuda.synchronize()
+            prefill_ms.append(p0.elapsed_time(p1))
+            after_p = m.stats()
+            prefill_stats = diff(after_p, before)
+            before = after_p
+            log("rep %d: prefill of %d tokens in %.1f ms, %d page-ins" % (rep, Tp, prefill_ms[-1],
+                                                                         prefill_stats["page_ins"]))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -140,7 +195,7 @@ def main():
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         times.append(ms)
-        st = m.stats()
+        st = diff(m.stats(), before)
         if stats is None:
             stats = st
         elif st["page_ins"] != stats["page_ins"] or st["distinct"] != stats["distinct"]:
@@ -161,10 +216,18 @@ def main():
     sample_steps = []
     samples = {}
     if not args.no_cpu_baseline:
-        n_samp = args.cpu_samples or (4 if B == 1 else 2)
+        n_samp = args.cpu_samples or 4
         sample_steps = sorted(set(int(round(v)) for v in np.linspace(0, steps - 1, n_samp)))
+    prefill_kernel = None
     if not args.no_timing_pass:
         cold()
+        if has_prefill:
+            m.set_timing(1)
+            run_prefill()
+            prefill_kernel = m.timing()
+            if not args.no_cpu_baseline:
+                samples["prefill"] = harness.bf16_bits(outp)
+        before = m.stats()
         m.set_timing(1)
         for s in range(steps):
             for l in range(L):
@@ -173,7 +236,7 @@ def main():
                 samples[s] = harness.bf16_bits(out)
         tm = m.timing()
         m.set_timing(0)
-        st2 = m.stats()
+        st2 = diff(m.stats(), before)
         if st2["page_ins"] != M or st2["distinct"] != D:
             raise RuntimeError("timing pass planned differently from the timed run")
         w13b = 2 * wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5}[wl.wtype]
@@ -208,7 +271,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "experts": wl.experts, "top_k": wl.top_k,
                    "resident": wl.resident, "hidden": H, "inter": wl.inter, "wtype": wl.wtype,
-                   "batch": B, "path": "captured" if captured else "host-planned",
+                   "batch": B, "path": "captured" if captured else ("device-planned eager" if device_planned
+                                                                     else "host-planned"),
                    "pagein": "dma" if (args.dma and not captured) else "kernel"},
         "window": {"distinct": D, "page_ins": M, "expert_bytes": S_alg,
                    "miss_rate": M / max(stats["entries"], 1)},
@@ -233,17 +297,35 @@ def main():
                                   "launches": gu["launches"], "bytes_per_launch": round(gu["bytes_per_launch"])}
         result["stages_ms"] = {k: round(v, 2) for k, v in kernel["stages_ms"].items()}
 
+    if has_prefill:
+        Dp, Mp = prefill_stats["distinct"], prefill_stats["page_ins"]
+        flops = prefill_stats["entries"] * 2.0 * 3 * wl.hidden * wl.inter
+        roof_p = Dp * S_alg / (HBM_PEAK_GBS * 1e9) + Mp * S_alg / (link * 1e9)
+        best_p = min(prefill_ms)
+        pre = {"tokens": Tp, "ms": round(best_p, 2), "ms_median": round(sorted(prefill_ms)[len(prefill_ms) // 2], 2),
+               "tok_s": round(Tp / (best_p / 1e3), 1), "distinct": Dp, "page_ins": Mp,
+               "waves": prefill_stats["waves"], "roof_ms": round(roof_p * 1e3, 2),
+               "frac": round(roof_p * 1e3 / best_p, 4), "gflop": round(flops / 1e9, 1)}
+        if prefill_kernel:
+            ex_ms = prefill_kernel["gate_up"][1] + prefill_kernel["down"][1]
+            pre["expert_kernels_ms"] = round(ex_ms, 2)
+            pre["expert_tflops"] = round(flops / (ex_ms / 1e3) / 1e12, 2) if ex_ms > 0 else None
+            pre["mfma_frac_bf16_peak"] = round(flops / (ex_ms / 1e3) / 2.5e15, 4) if ex_ms > 0 else None
+            pre["page_in_ms"] = round(prefill_kernel["page_in"][1], 2)
+            pre["page_in_gbs"] = round(Mp * S_alg / 1e9 / (prefill_kernel["page_in"][1] / 1e3), 2)
+        result["prefill"] = pre
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["sample_parity"] = cpu_baseline(wl, routing, steps, sample_steps, samples,
-                                                                       M, D)
+                                                                       M, D, has_prefill, args.cpu_budget)
     m.close()
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D):
+def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=False, budget_s=20.0):
     """The CPU oracle as it stands, on a bounded sample: the LRU simulator over the
-    whole window and the fp32 unpaged layer on a few evenly spaced steps (all
-    layers).  Expert tensors are generated untimed (they are inputs)."""
+    whole window, and the fp32 unpaged layer on (step, layer) pairs of a few evenly
+    spaced steps until about `budget_s` seconds of oracle time are spent.  Expert
+    tensors are generated untimed (they are inputs)."""
     import numpy as np
     import threadpoolctl
 
@@ -257,6 +339,8 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D):
     misses = distinct = 0
     for l in range(L):
         sim = LayerLRU(wl.experts, wl.resident)
+        if has_prefill:
+            sim.step(routing["prefill_ids"][l].ravel())
         for s in range(steps):
             ids = routing["decode_ids"][s, l].ravel()
             misses += sum(w.count for w in sim.step(ids))
@@ -265,31 +349,54 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D):
     plan_ok = (misses == M and distinct == D)
     log("oracle LRU simulator: %d layer-steps in %.2fs, plans %s" % (L * steps, t_sim,
                                                                      "match" if plan_ok else "DIFFER"))
-    t_moe = 0.0
-    worst = 0.0
-    for s in sample_steps:
-        x = formats.bf16_to_f32(synth.hidden_states(wl, s, B))
-        for l in range(L):
-            ids, w = routing["decode_ids"][s, l], routing["decode_w"][s, l]
+    # (step, layer) pairs: layers interleaved across the sample steps so a cut-off
+    # sample still spans the window
+    pairs = [(s, l) for l in range(L) for s in sample_steps]
+    t_moe, worst, done = 0.0, 0.0, []
+    wall0 = time.perf_counter()
+    xs = {s: formats.bf16_to_f32(synth.hidden_states(wl, s, B)) for s in sample_steps}
+    for s, l in pairs:
+        if t_moe >= budget_s or time.perf_counter() - wall0 >= 4 * budget_s:
+            break
+        ids, w = routing["decode_ids"][s, l], routing["decode_w"][s, l]
+        canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(ids)}
+        t1 = time.perf_counter()
+        ref = moe.moe_layer(xs[s], ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+        t_moe += time.perf_counter() - t1
+        done.append((s, l))
+        if s in samples:
+            got = harness.bf16_to_f32(samples[s][l])
+            worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+        if len(done) % 8 == 0:
+            log("oracle: %d (step, layer) pairs, %.1fs of oracle time" % (len(done), t_moe))
+    pre_worst = None
+    if has_prefill and "prefill" in samples:
+        xp = formats.bf16_to_f32(synth.hidden_states(wl, -1, wl.prefill_tokens))
+        pre_worst = 0.0
+        for l in (0, L - 1):
+            ids, w = routing["prefill_ids"][l], routing["prefill_w"][l]
             canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(ids)}
-            t0 = time.perf_counter()
-            ref = moe.moe_layer(x, ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
-            t_moe += time.perf_counter() - t0
-            if s in samples:
-                got = harness.bf16_to_f32(samples[s][l])
-                worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+            ref = moe.moe_layer(xp, ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+            got = harness.bf16_to_f32(samples["prefill"][l])
+            pre_worst = max(pre_worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+            log("oracle prefill layer %d done" % l)
+        log("oracle prefill layers 0 and %d: max rel err %.2e" % (L - 1, pre_worst))
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    tokens = len(sample_steps) * B
-    t_total = t_moe + t_sim * len(sample_steps) / steps
-    log("oracle MoE: %d steps x %d layers in %.2fs" % (len(sample_steps), L, t_moe))
+    tokens = B * len(done) / L                      # a token passes all L layers
+    t_total = t_moe + t_sim * (len(done) / L) / steps
+    log("oracle MoE: %d (step, layer) pairs in %.2fs" % (len(done), t_moe))
     tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2}[wl.wtype]
     cpu = {"value": round(tokens / t_total, 5) if t_total > 0 else None, "unit": "tok/s", "cores": threads,
            "kind": "oracle",
-           "sample": "%d of %d decode steps (all %d layers) through the fp32 unpaged oracle, plus the LRU "
-                     "simulator over all %d steps; %s" % (len(sample_steps), steps, L, steps,
-                                                          "host %s, %d cpus" % (cpu_model(), os.cpu_count()))}
-    parity = {"steps": sample_steps, "max_rel_err": worst, "tol": tol, "ok": bool(worst <= tol) if samples else None,
+           "sample": "%d (step, layer) pairs from decode steps %s (batch %d) through the fp32 unpaged oracle, "
+                     "plus the LRU simulator over all %d steps x %d layers; host %s, %d cpus" % (
+                         len(done), sample_steps, B, steps, L, cpu_model(), os.cpu_count())}
+    parity = {"pairs": len(done), "max_rel_err": worst, "tol": tol,
+              "ok": bool(worst <= tol and (pre_worst is None or pre_worst <= tol)) if samples else None,
               "plans_match_simulator": plan_ok}
+    if pre_worst is not None:
+        parity["prefill_layers"] = [0, L - 1]
+        parity["prefill_max_rel_err"] = pre_worst
     return cpu, parity
 
 

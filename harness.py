@@ -4,6 +4,7 @@ threads: the generator and pe_load_expert both release the GIL), and turns
 the workload's routing into device tensors.  No method arithmetic here.
 """
 import os
+import sys
 import threading
 from concurrent.futures import ThreadPoolExecutor
 
@@ -45,7 +46,7 @@ def load_store(moe, wl, threads=None, layers=None, experts=None, progress=None):
             with lock:
                 done[0] += 1
                 if done[0] % progress == 0:
-                    print("  loaded %d/%d experts" % (done[0], len(jobs)), flush=True)
+                    print("  loaded %d/%d experts" % (done[0], len(jobs)), file=sys.stderr, flush=True)
 
     with ThreadPoolExecutor(threads or host_threads()) as ex:
         list(ex.map(one, jobs))

@@ -59,6 +59,7 @@ SIGNATURES = {
     "pe_forward": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "pe_reset_lru": (_i, [_vp, _i, _vp]),
     "pe_expert_bytes": (_i, [_i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "pe_suggest_k": (_i, [_i, _i, _i, _i, _i, _i, ctypes.c_double]),
     "pe_max_captured_batch": (_i, [_vp]),
     "pe_max_waves": (_i, [_vp]),
     "pe_get_lru_state": (_i, [_vp, _i, _vp, _vp, _vp, _vp]),
@@ -156,6 +157,14 @@ def pe_expert_bytes(wtype, hidden, inter):
     _check(lib().pe_expert_bytes(WTYPES[wtype] if isinstance(wtype, str) else wtype, hidden, inter,
                                  ctypes.byref(a), ctypes.byref(c)))
     return a.value, c.value
+
+
+def pe_suggest_k(wtype, hidden, inter, num_layers, num_experts, top_k, budget_bytes):
+    v = lib().pe_suggest_k(WTYPES[wtype] if isinstance(wtype, str) else wtype, hidden, inter, num_layers,
+                           num_experts, top_k, float(budget_bytes))
+    if v < 0:
+        _check(v)
+    return v
 
 
 def pe_max_captured_batch(ctx):

@@ -77,7 +77,10 @@ bool blob_layout(int wtype, int H, int I, BlobLayout* b) {
   return true;
 }
 
-constexpr int kPageInGrid = 1024;
+// Page-in grid: a one-expert copy (9.4 MB) is fastest with few blocks and two 16-byte
+// loads in flight per thread (about 169 us, 56 GB/s, back to back), and a small grid
+// leaves most CUs to the expert kernels that overlap it.
+constexpr int kPageInGrid = 128;
 
 }  // namespace
 
@@ -89,7 +92,7 @@ struct pe_ctx {
   pe::Offsets o{};
   BlobLayout b{};
   bool unpaged = false;
-  int mfma_min = 1 << 30;
+  int mfma_min = 1 << 30;             // = d.mfma_min
   uint8_t* host_store = nullptr;       // page-locked, mapped: [L][E][stride]
   uint8_t* host_store_dev = nullptr;   // its device-visible address
   uint8_t* slots = nullptr;            // device: [L][K][stride]
@@ -103,6 +106,10 @@ struct pe_ctx {
   int32_t* st_work = nullptr;          // pinned staging: [wl.total]
   pe::HostPlanSummary* sum = nullptr;
   unsigned long long host_counts[pe::ST_COUNT] = {};
+  // Second stream (default priority): runs the experts that were already
+  // resident while the page-in is in flight; forked and joined with events.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // measurement mode
   bool timing = false;
   std::vector<hipEvent_t> ev_free;
@@ -125,6 +132,9 @@ void free_ctx(pe_ctx* c) {
   for (void* p : {(void*)c->slots, (void*)c->blocks, (void*)c->work, (void*)c->h, (void*)c->merged,
                   (void*)c->stats})
     if (p) (void)hipFree(p);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->side) (void)hipStreamDestroy(c->side);
   delete c->sum;
   delete c;
 }
@@ -136,8 +146,9 @@ int use_device(const pe_ctx* c) {
   return PE_OK;
 }
 
-pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const float* w) {
+pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const float* w, int part = 0) {
   pe::ExpertArgs a{};
+  a.part = part;
   a.slots = c->slots + (size_t)layer * c->d.K * c->b.stride;
   a.slot_stride = c->b.stride;
   a.off_w13 = c->b.off_w13; a.off_w2 = c->b.off_w2; a.off_s13 = c->b.off_s13; a.off_s2 = c->b.off_s2;
@@ -203,6 +214,30 @@ struct StageTimer {
   }
 };
 
+// Expert kernels (gate/up then down; GEMV items, then MFMA tiles) of one part
+// of one wave.  `items`/`tiles` bound the launches' grids; `max_m` bounds the
+// GEMV experts' token counts.
+void run_experts(pe_ctx* c, int layer, int wave, int part, const void* x, const float* w, int items, int max_m,
+                 int tiles, hipStream_t s) {
+  pe::ExpertArgs a = expert_args(c, layer, wave, x, w, part);
+  if (items > 0) {
+    {
+      StageTimer tm(c, PE_STAGE_GATE_UP, s);
+      pe::launch_gemv_gate_up(c->cfg.wtype, a, items, max_m, s);
+    }
+    StageTimer tm(c, PE_STAGE_DOWN, s);
+    pe::launch_gemv_down(c->cfg.wtype, a, items, max_m, s);
+  }
+  if (tiles > 0) {
+    {
+      StageTimer tm(c, PE_STAGE_GATE_UP, s);
+      pe::launch_mfma_gate_up(c->cfg.wtype, a, tiles, s);
+    }
+    StageTimer tm(c, PE_STAGE_DOWN, s);
+    pe::launch_mfma_down(c->cfg.wtype, a, tiles, s);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +266,21 @@ int pe_expert_bytes(int wtype, int hidden, int inter, size_t* algorithmic, size_
   if (algorithmic) *algorithmic = b.algorithmic;
   if (copied) *copied = b.copied;
   return PE_OK;
+}
+
+int pe_suggest_k(int wtype, int hidden, int inter, int num_layers, int num_experts, int top_k,
+                 double budget_bytes) {
+  size_t alg = 0, copied = 0;
+  const int rc = pe_expert_bytes(wtype, hidden, inter, &alg, &copied);
+  if (rc) return rc;
+  if (num_layers < 1 || num_experts < 1 || top_k < 1 || top_k > num_experts || !(budget_bytes >= 0))
+    return fail(PE_ERR_INVALID_ARG, "bad sizing arguments");
+  const double per_slot = (double)copied * num_layers;
+  const double k = budget_bytes / per_slot;
+  const int K = k >= num_experts ? num_experts : (int)k;
+  if (K < top_k)
+    return fail(PE_ERR_INVALID_ARG, "budget holds %d slots per layer, fewer than top_k=%d", K, top_k);
+  return K;
 }
 
 int pe_create(const pe_config* cfg, pe_ctx** out) {
@@ -272,6 +322,9 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   c->wl = pe::make_work_layout(c->d);
   c->o = pe::make_offsets(c->ll, c->wl);
   blob_layout(g.wtype, g.hidden, g.inter, &c->b);
+  // The MFMA kernels stage K in blocks of 128 and tile weight rows by 64.
+  c->mfma_min = (g.hidden % 128 == 0 && g.inter % 128 == 0) ? pe::kMfmaMinTokens : (1 << 30);
+  c->d.mfma_min = c->mfma_min;
   c->sum = new pe::HostPlanSummary;
   int rc = use_device(c);
   if (rc) { free_ctx(c); return rc; }
@@ -323,6 +376,12 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
       hipMemset(c->work, 0, c->wl.total * 4) != hipSuccess) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "initialising device buffers failed");
+  }
+  if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
+    free_ctx(c);
+    return fail(PE_ERR_HIP, "creating the side stream and its events failed");
   }
   pe::launch_reset_lru(c->blocks, c->ll.total, 0, d.L, c->o, d.E, d.K, unpaged, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
@@ -405,19 +464,24 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       StageTimer tm(c, PE_STAGE_PLAN, s);
       pe::launch_plan_single_wave(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, s);
     }
-    if (!c->unpaged) {
-      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-      pe::launch_page_in(blk, c->o, 0, d.K, host_l, slots_l, c->b.stride, c->b.copied, kPageInGrid, s);
-    }
-    pe::ExpertArgs a = expert_args(c, layer, 0, x, topk_w);
     const int items = std::min(n, d.K);
-    {
-      StageTimer tm(c, PE_STAGE_GATE_UP, s);
-      pe::launch_gemv_gate_up(c->cfg.wtype, a, items, T, s);
-    }
-    {
-      StageTimer tm(c, PE_STAGE_DOWN, s);
-      pe::launch_gemv_down(c->cfg.wtype, a, items, T, s);
+    // an expert may hold T >= mfma_min entries: then launch the MFMA kernels over
+    // the most tiles one wave can have; surplus blocks exit on the device count
+    const int tiles = T >= c->mfma_min ? pe::ceil_div(n, pe::kTileM) + items : 0;
+    if (c->unpaged) {
+      run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
+    } else {
+      // fork: experts already resident run on the side stream during the page-in
+      PE_HIP(hipEventRecord(c->ev_fork, s));
+      PE_HIP(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+      run_experts(c, layer, 0, 1, x, topk_w, items, T, tiles, c->side);
+      PE_HIP(hipEventRecord(c->ev_join, c->side));
+      {
+        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+        pe::launch_page_in(blk, c->o, 0, d.K, host_l, slots_l, c->b.stride, c->b.copied, kPageInGrid, s);
+      }
+      run_experts(c, layer, 0, 2, x, topk_w, items, T, tiles, s);
+      PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
     }
     {
       StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
@@ -445,6 +509,15 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
   for (int w = 0; w < sm.n_waves; ++w) {
     const int cnt = c->st_blk[c->ll.plan_count + w];
+    const int g_all = sm.gemv_items[w], g_hit = sm.gemv_hits[w];
+    const int t_all = sm.tiles[w], t_hit = sm.tile_hits[w];
+    const bool fork = !c->unpaged && cnt > 0 && (g_hit > 0 || t_hit > 0);
+    if (fork) {
+      PE_HIP(hipEventRecord(c->ev_fork, s));
+      PE_HIP(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+      run_experts(c, layer, w, 1, x, topk_w, g_hit, sm.max_gemv_tokens, t_hit, c->side);
+      PE_HIP(hipEventRecord(c->ev_join, c->side));
+    }
     if (!c->unpaged && cnt > 0) {
       StageTimer tm(c, PE_STAGE_PAGE_IN, s);
       if (dma) {
@@ -458,14 +531,11 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
         pe::launch_page_in(blk, c->o, w, d.K, host_l, slots_l, c->b.stride, c->b.copied, kPageInGrid, s);
       }
     }
-    pe::ExpertArgs a = expert_args(c, layer, w, x, topk_w);
-    if (sm.gemv_items[w] > 0) {
-      {
-        StageTimer tm(c, PE_STAGE_GATE_UP, s);
-        pe::launch_gemv_gate_up(c->cfg.wtype, a, sm.gemv_items[w], sm.max_gemv_tokens, s);
-      }
-      StageTimer tm(c, PE_STAGE_DOWN, s);
-      pe::launch_gemv_down(c->cfg.wtype, a, sm.gemv_items[w], sm.max_gemv_tokens, s);
+    if (fork) {
+      run_experts(c, layer, w, 2, x, topk_w, g_all - g_hit, sm.max_gemv_tokens, t_all - t_hit, s);
+      PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));    // before the next wave may evict these slots
+    } else {
+      run_experts(c, layer, w, 0, x, topk_w, g_all, sm.max_gemv_tokens, t_all, s);
     }
   }
   {

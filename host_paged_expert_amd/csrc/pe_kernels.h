@@ -25,6 +25,8 @@ struct ExpertArgs {
   Offsets o;
   int MW;                     // header capacity (max waves)
   int wave;                   // wave whose experts this launch runs
+  int part;                   // 0: all its experts; 1: those resident before the
+                              // wave's page-in; 2: those it pages in
   const uint16_t* x;          // [T, H] bf16
   const float* topk_w;        // [T*k]
   uint16_t* h;                // [max_entries, I] bf16, by sorted position

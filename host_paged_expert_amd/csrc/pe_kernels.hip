@@ -66,7 +66,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kScanVals = 5;   // missing, present, entries, gemv, tiles
+// prefix values: missing, present, entries, GEMV hit/miss, MFMA tiles hit/miss
+constexpr int kScanVals = 7;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
@@ -102,19 +103,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
   __syncthreads();
 
   // Exclusive prefixes over experts of: missing, present, entry count, GEMV
-  // flag and MFMA tile count.  Thread t owns experts [t*per, (t+1)*per).
+  // items of resident / missing experts, MFMA tiles of resident / missing
+  // experts.  Thread t owns experts [t*per, (t+1)*per).
   const int per = (E + kPlanThreads - 1) / kPlanThreads;
   const int e0 = tid * per;
-  int loc[kScanVals] = {0, 0, 0, 0, 0};
+  int loc[kScanVals] = {0, 0, 0, 0, 0, 0, 0};
   for (int q = 0; q < per; ++q) {
     int e = e0 + q;
     if (e >= E) break;
     int c = s_cnt[e];
     if (c > 0) {
-      loc[0] += s_es[e] < 0;
+      const int miss = s_es[e] < 0;
+      loc[0] += miss;
       loc[1] += 1;
       loc[2] += c;
-      if (c < mfma_min) loc[3] += 1; else loc[4] += (c + kTileM - 1) / kTileM;
+      if (c < mfma_min) loc[3 + miss] += 1; else loc[5 + miss] += (c + kTileM - 1) / kTileM;
     }
   }
   int inc[kScanVals];
@@ -144,10 +147,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
       for (int v = 0; v < kScanVals; ++v) s_pref[v][e] = run[v];
       int c = s_cnt[e];
       if (c > 0) {
-        run[0] += s_es[e] < 0;
+        const int miss = s_es[e] < 0;
+        run[0] += miss;
         run[1] += 1;
         run[2] += c;
-        if (c < mfma_min) run[3] += 1; else run[4] += (c + kTileM - 1) / kTileM;
+        if (c < mfma_min) run[3 + miss] += 1; else run[5 + miss] += (c + kTileM - 1) / kTileM;
       }
     }
   }
@@ -158,7 +162,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
     s_cand[j] = occ < 0 || s_cnt[occ] == 0;
   }
   __syncthreads();
-  const int n_miss = s_tot[0], D = s_tot[1], n_valid = s_tot[2], n_gemv = s_tot[3], n_tiles = s_tot[4];
+  const int n_miss = s_tot[0], D = s_tot[1], n_valid = s_tot[2];
+  const int g_hit = s_tot[3], n_gemv = s_tot[3] + s_tot[4], t_hit = s_tot[5], n_tiles = s_tot[5] + s_tot[6];
   // Victims by ascending (last_use, slot): rank = candidates ordered before j.
   for (int j = tid; j < K; j += kPlanThreads) {
     if (!s_cand[j]) continue;
@@ -200,10 +205,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
     used_expert[u] = e;
     used_slot[u] = j;
     used_off[u] = s_pref[2][e];
+    // was this expert missing? (its missing-prefix steps up right after it)
+    const bool miss = (e + 1 < E ? s_pref[0][e + 1] : n_miss) > s_pref[0][e];
     if (c < mfma_min) {
-      gemv_u[s_pref[3][e]] = u;
+      gemv_u[miss ? g_hit + s_pref[4][e] : s_pref[3][e]] = u;
     } else {
-      int t0 = s_pref[4][e];
+      int t0 = miss ? t_hit + s_pref[6][e] : s_pref[5][e];
       for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
     }
   }
@@ -235,6 +242,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
     hdr[hdr_wave_u(MW, 0)] = 0; hdr[hdr_wave_u(MW, 1)] = D;
     hdr[hdr_gemv(MW, 0)] = 0;   hdr[hdr_gemv(MW, 1)] = n_gemv;
     hdr[hdr_tile(MW, 0)] = 0;   hdr[hdr_tile(MW, 1)] = n_tiles;
+    hdr[hdr_gemv_split(MW, 0)] = g_hit;
+    hdr[hdr_tile_split(MW, 0)] = t_hit;
     used_off[D] = n_valid;
     atomicAdd(stats + ST_STEPS, 1ull);
     atomicAdd(stats + ST_DEVICE_PLANNED, 1ull);
@@ -257,7 +266,7 @@ void launch_plan_single_wave(int32_t* blk, const int32_t* ids, int n, const Dims
 
 namespace {
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyUnroll = 2;
 }
 
 // Every thread of the grid takes 16-byte chunks gtid, gtid + gstride, ...,
@@ -464,9 +473,17 @@ struct GemvItem {
   int u, slot, off, m;
 };
 
+// Range [b, e) of a wave's list selected by a.part: 0 all, 1 resident before
+// the wave ("hits"), 2 paged in by it.
+__device__ __forceinline__ void part_range(const ExpertArgs& a, int begin, int split, int end, int& b, int& e) {
+  b = a.part == 2 ? split : begin;
+  e = a.part == 1 ? split : end;
+}
+
 __device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvItem& it) {
   const int32_t* hdr = a.work + a.o.hdr;
-  const int g0 = hdr[hdr_gemv(a.MW, a.wave)], g1 = hdr[hdr_gemv(a.MW, a.wave + 1)];
+  int g0, g1;
+  part_range(a, hdr[hdr_gemv(a.MW, a.wave)], hdr[hdr_gemv_split(a.MW, a.wave)], hdr[hdr_gemv(a.MW, a.wave + 1)], g0, g1);
   if (item >= g1 - g0) return false;
   it.u = a.work[a.o.gemv_u + g0 + item];
   it.slot = a.work[a.o.used_slot + it.u];
@@ -709,7 +726,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
   __shared__ __align__(16) uint16_t sU[kNT * kLdsRow];
   __shared__ int sTok[kTileM];
   const int32_t* hdr = a.work + a.o.hdr;
-  const int t0 = hdr[hdr_tile(a.MW, a.wave)], t1 = hdr[hdr_tile(a.MW, a.wave + 1)];
+  int t0, t1;
+  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
   const int tile = t0 + blockIdx.y;
   if (tile >= t1) return;
   const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
@@ -797,7 +815,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
   __shared__ __align__(16) uint16_t sA[kTileM * kLdsRow];
   __shared__ __align__(16) uint16_t sB[kNT * kLdsRow];
   const int32_t* hdr = a.work + a.o.hdr;
-  const int t0 = hdr[hdr_tile(a.MW, a.wave)], t1 = hdr[hdr_tile(a.MW, a.wave + 1)];
+  int t0, t1;
+  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
   const int tile = t0 + blockIdx.y;
   if (tile >= t1) return;
   const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];

@@ -27,12 +27,13 @@ struct Dims {
   int max_entries;   // max_tokens * k
   int max_waves;     // ceil(min(max_entries, E) / K)
   int max_tiles;     // MFMA tiles one step can need
+  int mfma_min;      // experts with at least this many entries take the MFMA kernels
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 inline Dims make_dims(int L, int E, int K, int k, int H, int I, int max_tokens) {
-  Dims d{L, E, K, k, H, I, max_tokens, max_tokens * k, 0, 0};
+  Dims d{L, E, K, k, H, I, max_tokens, max_tokens * k, 0, 0, kMfmaMinTokens};
   int most = d.max_entries < E ? d.max_entries : E;
   d.max_waves = ceil_div(most, K);
   if (d.max_waves < 1) d.max_waves = 1;
@@ -90,11 +91,18 @@ struct WorkLayout {
   size_t total;
 };
 
-// Header words (constexpr, so kernels can use them too): [0] n_waves, then wave_u_begin[MW+1], gemv_begin[MW+1], tile_begin[MW+1].
+// Header words (constexpr, so kernels can use them too): [0] n_waves, then
+// wave_u_begin[MW+1], gemv_begin[MW+1], tile_begin[MW+1], gemv_split[MW],
+// tile_split[MW].  Inside a wave, GEMV items and MFMA tiles list first the
+// experts that were resident before the wave's page-in ("hits"), then the ones
+// it copies in; *_split[w] is where the second group starts, so the hits can
+// run while the page-in is in flight.
 constexpr size_t hdr_wave_u(int MW, int w) { return (void)MW, 1 + (size_t)w; }
 constexpr size_t hdr_gemv(int MW, int w) { return 1 + (size_t)(MW + 1) + w; }
 constexpr size_t hdr_tile(int MW, int w) { return 1 + 2 * (size_t)(MW + 1) + w; }
-constexpr size_t hdr_words(int MW) { return 1 + 3 * (size_t)(MW + 1); }
+constexpr size_t hdr_gemv_split(int MW, int w) { return 1 + 3 * (size_t)(MW + 1) + w; }
+constexpr size_t hdr_tile_split(int MW, int w) { return 1 + 3 * (size_t)(MW + 1) + MW + w; }
+constexpr size_t hdr_words(int MW) { return 1 + 3 * (size_t)(MW + 1) + 2 * (size_t)MW; }
 
 inline WorkLayout make_work_layout(const Dims& d) {
   WorkLayout w{};
@@ -121,7 +129,9 @@ struct HostPlanSummary {
   int bad_ids;
   int max_gemv_tokens;   // largest entry count among GEMV experts
   int gemv_items[kMaxExperts];   // per wave: experts on the GEMV kernels
+  int gemv_hits[kMaxExperts];    // per wave: of which resident before the wave
   int tiles[kMaxExperts];        // per wave: MFMA tiles
+  int tile_hits[kMaxExperts];    // per wave: of which for resident experts
 };
 
 // Plan one step of one layer on the host (the multi-wave path).  `blk` is a

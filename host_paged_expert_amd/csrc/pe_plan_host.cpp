@@ -76,9 +76,11 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     int32_t* pe_ = blk + ll.plan_expert + (size_t)w * K;
     int32_t* ps_ = blk + ll.plan_slot + (size_t)w * K;
     int32_t* pv_ = blk + ll.plan_evicted + (size_t)w * K;
+    std::vector<char> hit(n);
+    for (int i = 0; i < n; ++i) hit[i] = expert_slot[order[b + i]] >= 0;
     for (int i = 0; i < n; ++i) {
       int e = order[b + i];
-      if (expert_slot[e] >= 0) continue;
+      if (hit[i]) continue;
       int j = cand[r].second;
       int old = slot_expert[j];
       if (old >= 0) expert_slot[old] = -1;
@@ -91,23 +93,39 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     page_ins += r;
     for (int i = 0; i < n; ++i) last_use[expert_slot[order[b + i]]] = tick;
     ++tick;
-    // used experts of this wave, ascending id
+    // used experts of this wave, ascending id; GEMV items and MFMA tiles list the
+    // experts resident before the wave first, then the ones paged in
     std::vector<int> wave(order.begin() + b, order.begin() + b + n);
+    std::vector<char> was_hit(E, 0);
+    for (int i = 0; i < n; ++i) was_hit[order[b + i]] = hit[i];
     std::sort(wave.begin(), wave.end());
     int g0 = ng, t0 = nt;
+    const int u0 = u;
     for (int e : wave) {
       u_of[e] = u;
       used_expert[u] = e;
       used_slot[u] = expert_slot[e];
       used_off[u] = off;
       off += cnt[e];
-      if (cnt[e] < kMfmaMinTokens) {
-        gemv_u[ng++] = u;
-        max_gemv = std::max(max_gemv, cnt[e]);
-      } else {
-        for (int q = 0; q < cnt[e]; q += kTileM) { tile_u[nt] = u; tile_row[nt] = q; ++nt; }
-      }
       ++u;
+    }
+    for (int pass = 0; pass < 2; ++pass) {          // 0: hits, 1: paged in
+      for (int uu = u0; uu < u; ++uu) {
+        const int e = used_expert[uu];
+        if (was_hit[e] != (pass == 0)) continue;
+        if (cnt[e] < d.mfma_min) {
+          gemv_u[ng++] = uu;
+          max_gemv = std::max(max_gemv, cnt[e]);
+        } else {
+          for (int q = 0; q < cnt[e]; q += kTileM) { tile_u[nt] = uu; tile_row[nt] = q; ++nt; }
+        }
+      }
+      if (pass == 0) {
+        hdr[hdr_gemv_split(MW, w)] = ng;
+        hdr[hdr_tile_split(MW, w)] = nt;
+        sum->gemv_hits[w] = ng - g0;
+        sum->tile_hits[w] = nt - t0;
+      }
     }
     hdr[hdr_wave_u(MW, w + 1)] = u;
     hdr[hdr_gemv(MW, w + 1)] = ng;

@@ -145,6 +145,15 @@ int pe_reset_lru(pe_ctx* ctx, int layer, void* stream);
  * what one page-in moves (sub-tensors 256-byte aligned).  No GPU needed. */
 int pe_expert_bytes(int wtype, int hidden, int inter, size_t* algorithmic, size_t* copied);
 
+/* Slots per layer that fit a device-memory budget: one resident expert per
+ * layer costs its blob bytes times the MoE layers (docs page, "Choosing K"),
+ * so K = floor(budget_bytes / (copied blob bytes x num_layers)), capped at
+ * num_experts.  Returns K, or PE_ERR_INVALID_ARG if the budget holds fewer
+ * than top_k slots (the method needs K >= top_k) or an argument is invalid.
+ * No GPU needed. */
+int pe_suggest_k(int wtype, int hidden, int inter, int num_layers, int num_experts, int top_k,
+                 double budget_bytes);
+
 /* Largest decode batch whose step is device-planned: floor(K / top_k)
  * (docs page, "Captured decode").  Returns the value, or < 0 on error. */
 int pe_max_captured_batch(const pe_ctx* ctx);

@@ -114,3 +114,19 @@ def test_create_validates_before_touching_the_gpu():
         with pytest.raises(pe.PEError) as ei:
             pe.pe_create(**kw)
         assert ei.value.code == pe.PE_ERR_INVALID_ARG
+
+
+def test_suggest_k_matches_sizing_rule_and_docs_example():
+    """The docs' "Choosing K" rule: per-slot bytes = blob bytes x MoE layers."""
+    slot = sizes.slot_bytes("int4", 2048, 768, 48)
+    assert pe.pe_suggest_k("int4", 2048, 768, 48, 128, 8, 92 * slot) == 92
+    assert pe.pe_suggest_k("int4", 2048, 768, 48, 128, 8, 92 * slot - 1) == 91
+    assert pe.pe_suggest_k("bf16", 2048, 768, 48, 128, 8, 1e15) == 128
+    for budget in (1e9, 5e9, 20e9, 60e9):
+        want = sizes.suggest_k(budget, sizes.slot_bytes("fp8", 2048, 768, 48), 128)
+        _, copied = pe.pe_expert_bytes("fp8", 2048, 768)
+        got = pe.pe_suggest_k("fp8", 2048, 768, 48, 128, 8, budget) if want >= 8 else None
+        if got is not None:
+            assert abs(got - want) <= 1 and got == min(128, int(budget // (copied * 48)))
+    with pytest.raises(pe.PEError):
+        pe.pe_suggest_k("bf16", 2048, 768, 48, 128, 8, 1e9)       # fewer than top_k slots
