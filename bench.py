@@ -57,6 +57,9 @@ def parse():
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        pmc_summary(*sys.argv[2:5])
+        return
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: this method keeps its slot tables and LRU state on one GPU, "
@@ -286,7 +289,7 @@ def main():
                               "achieved": round(pi["gbs"], 2) if pi["gbs"] else None,
                               "peak": round(PCIE5_X16_GBS, 2), "unit": "GB/s",
                               "frac": round(pi["gbs"] / PCIE5_X16_GBS, 4) if pi["gbs"] else None,
-                              "traffic": None, "avg_launch_us": round(pi["avg_us"], 2),
+                              "traffic": traffic_for(pi["bytes_per_launch"]), "avg_launch_us": round(pi["avg_us"], 2),
                               "launches": pi["launches"], "bytes_per_launch": round(pi["bytes_per_launch"])}
         gu = kernel["gate_up"]
         result["roofline_hbm"] = {"kernel": "gemv_gate_up_kernel", "bound": "hbm",
@@ -398,6 +401,77 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
         parity["prefill_layers"] = [0, L - 1]
         parity["prefill_max_rel_err"] = pre_worst
     return cpu, parity
+
+
+def page_in_source_hash():
+    """Hash of the page-in kernel's source (its copy routine, the kernel and their
+    launch constants): memory-traffic counters stay valid while it is unchanged."""
+    import hashlib
+    import re
+    src = open(os.path.join(ROOT, "host_paged_expert_amd", "csrc", "pe_kernels.hip")).read()
+    api = open(os.path.join(ROOT, "host_paged_expert_amd", "csrc", "pe_api.cpp")).read()
+
+    def body(name):
+        i = src.index(name)
+        start = src.rfind("\n\n", 0, i) + 2
+        depth, j = 0, src.index("{", i)
+        for k in range(j, len(src)):
+            depth += {"{": 1, "}": -1}.get(src[k], 0)
+            if depth == 0:
+                return src[start:k + 1]
+        raise ValueError(name)
+    consts = re.findall(r"constexpr int kCopy\w+ = \d+;", src) + re.findall(r"constexpr int kPageInGrid = \d+;", api)
+    text = body("__device__ __forceinline__ void copy_chunks(") + body("void page_in_kernel(") + "".join(consts)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
+def pmc_summary(fetch_csv, write_csv, out_json):
+    """Per-launch memory traffic of the page-in kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for a plain 256 MiB device-to-device copy (--copy-reference 256),
+    relative to the planned bytes (page-ins x expert bytes / launches) of that run,
+    which the run's log line gives."""
+    import collections
+    import csv
+
+    def load(path):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+    f, w = load(fetch_csv), load(write_csv)
+    ref = 256 * 1024.0
+    fs = ref / max(f["__amd_rocclr_copyBuffer"])
+    ws = ref / max(w["__amd_rocclr_copyBuffer"])
+    key = [k for k in f if "page_in_kernel" in k][0]
+    rd = sum(f[key]) / len(f[key]) * fs
+    wr = sum(w[key]) / len(w[key]) * ws
+    log_lines = open(fetch_csv.replace(".csv", ".log")).read()
+    import re
+    m = re.search(r"(\d+) page-ins", log_lines)
+    page_ins = int(m.group(1))
+    alg = page_ins * int(re.search(r"expert_bytes\D+(\d+)", open(fetch_csv.replace(".csv", ".json")).read()).group(1)) \
+        / len(f[key]) / 1024.0
+    out = {"page_in_kernel": {"source_sha256_16": page_in_source_hash(), "fetch_scale": round(fs, 4),
+                              "write_scale": round(ws, 4), "read_kib_per_launch": round(rd, 1),
+                              "write_kib_per_launch": round(wr, 1),
+                              "algorithmic_kib_per_launch_each_way": round(alg, 1),
+                              "traffic_over_algorithmic": round((rd + wr) / (2 * alg), 4),
+                              "launches": len(f[key]), "page_ins": page_ins}}
+    json.dump(out, open(out_json, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def traffic_for(bytes_per_launch):
+    """Read+write bytes per page-in launch implied by the committed counter
+    summary, or None if the page-in kernel changed since it was taken."""
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["page_in_kernel"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256_16") != page_in_source_hash():
+        return None
+    return round(2 * bytes_per_launch * t["traffic_over_algorithmic"])
 
 
 def cpu_model():
