@@ -161,6 +161,8 @@ pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const 
   a.h = c->h;
   a.merged = c->merged;
   a.H = c->d.H; a.I = c->d.I; a.k = c->d.k;
+  a.lean = 0;
+  a.mfma_min = c->mfma_min;
   return a;
 }
 
@@ -460,32 +462,48 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   const bool device_plan = n <= d.K && !(c->cfg.flags & PE_FLAG_FORCE_HOST_PLAN);
 
   if (device_plan) {
-    {
-      StageTimer tm(c, PE_STAGE_PLAN, s);
-      pe::launch_plan_single_wave(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, s);
-    }
+    // One wave.  Planning and page-in are one launch: every workgroup makes the
+    // same LRU decision in LDS from the current state copy (no workgroup waits for
+    // another) and workgroup 0 publishes it, writing the new state into the other
+    // copy.  Meanwhile a second stream runs the experts that were already resident,
+    // each workgroup finding its expert from the ids and the current copy.  The
+    // paged-in experts run after the page-in; the top-k sum joins both and makes
+    // the new state copy current.  No host synchronisation: capturable.
     const int items = std::min(n, d.K);
     // an expert may hold T >= mfma_min entries: then launch the MFMA kernels over
     // the most tiles one wave can have; surplus blocks exit on the device count
     const int tiles = T >= c->mfma_min ? pe::ceil_div(n, pe::kTileM) + items : 0;
-    if (c->unpaged) {
-      run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
-    } else {
-      // fork: experts already resident run on the side stream during the page-in
+    const bool overlap = !c->unpaged && tiles == 0;
+    if (overlap) {
       PE_HIP(hipEventRecord(c->ev_fork, s));
       PE_HIP(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-      run_experts(c, layer, 0, 1, x, topk_w, items, T, tiles, c->side);
-      PE_HIP(hipEventRecord(c->ev_join, c->side));
+      pe::ExpertArgs h = expert_args(c, layer, 0, x, topk_w, 1);
+      h.lean = 1;
+      h.ids = topk_ids;
+      h.T = T;
+      h.E = d.E;
+      h.blk = blk;
       {
-        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-        pe::launch_page_in(blk, c->o, 0, d.K, host_l, slots_l, c->b.stride, c->b.copied, kPageInGrid, s);
+        StageTimer tm(c, PE_STAGE_GATE_UP, c->side);
+        pe::launch_gemv_gate_up(c->cfg.wtype, h, items, T, c->side);
       }
-      run_experts(c, layer, 0, 2, x, topk_w, items, T, tiles, s);
-      PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
+      {
+        StageTimer tm(c, PE_STAGE_DOWN, c->side);
+        pe::launch_gemv_down(c->cfg.wtype, h, items, T, c->side);
+      }
+      PE_HIP(hipEventRecord(c->ev_join, c->side));
     }
     {
+      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+      pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l, slots_l,
+                              c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
+    }
+    run_experts(c, layer, 0, overlap ? 2 : 0, x, topk_w, items, T, tiles, s);
+    if (overlap) PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
+    {
       StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
-      pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), s);
+      pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out),
+                          blk + c->ll.cur, s);
     }
     PE_HIP(hipGetLastError());
     return PE_OK;
@@ -499,7 +517,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   // Host-planned step: read ids and LRU state back (the one synchronisation),
   // plan every wave, upload plans and work lists, then run the waves in order.
   PE_HIP(hipMemcpyAsync(c->st_ids, topk_ids, (size_t)n * 4, hipMemcpyDeviceToHost, s));
-  PE_HIP(hipMemcpyAsync(c->st_blk, blk, c->ll.state_words * 4, hipMemcpyDeviceToHost, s));
+  PE_HIP(hipMemcpyAsync(c->st_blk, blk, c->ll.state_prefix * 4, hipMemcpyDeviceToHost, s));
   PE_HIP(hipStreamSynchronize(s));
   pe::HostPlanSummary& sm = *c->sum;
   if (pe::host_plan_step(d, c->ll, c->wl, c->st_ids, n, c->st_blk, c->st_work, &sm) != 0)
@@ -540,7 +558,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   }
   {
     StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
-    pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), s);
+    pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), nullptr, s);
   }
   PE_HIP(hipGetLastError());
   c->host_counts[pe::ST_STEPS] += 1;
@@ -570,10 +588,11 @@ int pe_get_lru_state(pe_ctx* c, int layer, int32_t* slot_expert, uint32_t* last_
   int rc = use_device(c);
   if (rc) return rc;
   PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  std::vector<int32_t> st(c->ll.state_words);
-  PE_HIP(hipMemcpy(st.data(), c->blocks + (size_t)layer * c->ll.total, st.size() * 4, hipMemcpyDeviceToHost));
-  if (slot_expert) memcpy(slot_expert, st.data() + c->ll.slot_expert, (size_t)c->d.K * 4);
-  if (last_use) memcpy(last_use, st.data() + c->ll.last_use, (size_t)c->d.K * 4);
+  std::vector<int32_t> blk(c->ll.state_prefix);
+  PE_HIP(hipMemcpy(blk.data(), c->blocks + (size_t)layer * c->ll.total, blk.size() * 4, hipMemcpyDeviceToHost));
+  const int32_t* st = blk.data() + c->ll.state(blk[c->ll.cur] & 1);
+  if (slot_expert) memcpy(slot_expert, st + c->ll.slot_expert, (size_t)c->d.K * 4);
+  if (last_use) memcpy(last_use, st + c->ll.last_use, (size_t)c->d.K * 4);
   if (tick) *tick = (uint32_t)st[c->ll.tick];
   return PE_OK;
 }
@@ -730,16 +749,18 @@ int pe_plan_host(int num_experts, int num_resident, int top_k, int T, const int3
   const pe::WorkLayout wl = pe::make_work_layout(d);
   std::vector<int32_t> blk(ll.total, 0), work(wl.total, 0);
   const int K = num_resident, E = num_experts;
-  blk[ll.tick] = (int32_t)*tick;
-  for (int e = 0; e < E; ++e) blk[ll.expert_slot + e] = -1;
+  blk[ll.cur] = 0;
+  int32_t* st = blk.data() + ll.state(0);
+  st[ll.tick] = (int32_t)*tick;
+  for (int e = 0; e < E; ++e) st[ll.expert_slot + e] = -1;
   for (int j = 0; j < K; ++j) {
     const int e = slot_expert[j];
     if (e >= E) return fail(PE_ERR_INVALID_ARG, "slot_expert[%d] = %d out of range", j, e);
-    blk[ll.slot_expert + j] = e;
-    blk[ll.last_use + j] = (int32_t)last_use[j];
+    st[ll.slot_expert + j] = e;
+    st[ll.last_use + j] = (int32_t)last_use[j];
     if (e >= 0) {
-      if (blk[ll.expert_slot + e] >= 0) return fail(PE_ERR_INVALID_ARG, "expert %d in two slots", e);
-      blk[ll.expert_slot + e] = j;
+      if (st[ll.expert_slot + e] >= 0) return fail(PE_ERR_INVALID_ARG, "expert %d in two slots", e);
+      st[ll.expert_slot + e] = j;
     }
   }
   pe::HostPlanSummary* sm = new pe::HostPlanSummary;
@@ -747,10 +768,10 @@ int pe_plan_host(int num_experts, int num_resident, int top_k, int T, const int3
   delete sm;
   if (rc != 0) return fail(PE_ERR_INVALID_ARG, "step needs more than %d waves", max_waves);
   for (int j = 0; j < K; ++j) {
-    slot_expert[j] = blk[ll.slot_expert + j];
-    last_use[j] = (uint32_t)blk[ll.last_use + j];
+    slot_expert[j] = st[ll.slot_expert + j];
+    last_use[j] = (uint32_t)st[ll.last_use + j];
   }
-  *tick = (uint32_t)blk[ll.tick];
+  *tick = (uint32_t)st[ll.tick];
   *n_waves = blk[ll.n_waves];
   for (int w = 0; w < max_waves; ++w) counts[w] = w < *n_waves ? blk[ll.plan_count + w] : 0;
   memcpy(experts, blk.data() + ll.plan_expert, (size_t)max_waves * K * 4);

@@ -8,8 +8,9 @@ namespace pe {
 
 // Offsets of the layer block and the work arena, in int32 words, as kernel arguments.
 struct Offsets {
-  int tick, slot_expert, expert_slot, last_use, n_waves, plan_count, plan_expert, plan_slot,
-      plan_evicted, slot_of;
+  int tick, slot_expert, expert_slot, last_use;   // inside a state copy
+  int cur, state0, state_stride;                  // current copy, copies
+  int n_waves, plan_count, plan_expert, plan_slot, plan_evicted, slot_of;
   int hdr, used_expert, used_slot, used_off, gemv_u, tile_u, tile_row, entries;
 };
 
@@ -32,13 +33,25 @@ struct ExpertArgs {
   uint16_t* h;                // [max_entries, I] bf16, by sorted position
   float* merged;              // [T*k, H] fp32, by entry index
   int H, I, k;
+  // lean = 1 (device-planned steps, part 1): each workgroup finds its resident
+  // expert from the routed ids and the current LRU-state copy instead of the
+  // published work lists, so it can run alongside the planning + page-in kernel.
+  int lean;
+  int mfma_min;
+  const int32_t* ids;         // [T*k] routed ids
+  int T, E;
+  const int32_t* blk;         // the layer block
 };
 
-// Single-wave device planner (T*k <= K): LRU decision, plan, slot map, work
-// lists and counters for one layer, in one workgroup.
-void launch_plan_single_wave(int32_t* blk, const int32_t* ids, int n, const Dims& d,
-                             const Offsets& o, int mfma_min, int32_t* work,
-                             unsigned long long* stats, hipStream_t s);
+// Single-wave device-planned step (T*k <= K), planning and page-in in one launch:
+// every workgroup makes the same LRU decision in LDS from the current state copy
+// (no workgroup waits for another); workgroup 0 publishes the plan, slot map,
+// work lists, counters and the new state (into the other copy); then every
+// workgroup copies its share of the planned experts from the mapped host rows
+// (`grid` workgroups; with copy == false one workgroup, planning only).
+void launch_plan_page_in(int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
+                         int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
+                         uint8_t* slots, size_t stride, size_t copy_bytes, bool copy, int grid, hipStream_t s);
 
 // Copy the planned experts of wave `wave` from the mapped host rows into their
 // slots, reading the page-in count on the device.
@@ -59,9 +72,10 @@ void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipS
 void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);
 void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);
 
-// out[t] = bf16(sum_j merged[t,j]) over valid entries, j in order.
+// out[t] = bf16(sum_j merged[t,j]) over valid entries, j in order; if `flip` is
+// set, it toggles that word (the layer's current LRU-state copy).
 void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int E, int H,
-                     uint16_t* out, hipStream_t s);
+                     uint16_t* out, int32_t* flip, hipStream_t s);
 
 // Reset the LRU state of layers [l0, l1): empty, or the identity map.
 void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const Offsets& o,

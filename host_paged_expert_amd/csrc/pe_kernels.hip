@@ -24,7 +24,9 @@ namespace pe {
 Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl) {
   Offsets o;
   o.tick = (int)ll.tick; o.slot_expert = (int)ll.slot_expert; o.expert_slot = (int)ll.expert_slot;
-  o.last_use = (int)ll.last_use; o.n_waves = (int)ll.n_waves; o.plan_count = (int)ll.plan_count;
+  o.last_use = (int)ll.last_use;
+  o.cur = (int)ll.cur; o.state0 = (int)ll.state0; o.state_stride = (int)ll.state_stride;
+  o.n_waves = (int)ll.n_waves; o.plan_count = (int)ll.plan_count;
   o.plan_expert = (int)ll.plan_expert; o.plan_slot = (int)ll.plan_slot;
   o.plan_evicted = (int)ll.plan_evicted; o.slot_of = (int)ll.slot_of;
   o.hdr = (int)wl.hdr; o.used_expert = (int)wl.used_expert; o.used_slot = (int)wl.used_slot;
@@ -51,6 +53,27 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
   return __half2float(__ushort_as_half(b));
 }
 
+// out[t] = bf16(((m0 + m1) + ...) + m_{k-1}) over the valid entries of token t,
+// four columns per thread, threads tid, tid + nthreads, ...
+__device__ __forceinline__ void topk_sum_rows(const float* __restrict__ merged, const int32_t* __restrict__ ids,
+                                              int T, int k, int E, int H, uint16_t* __restrict__ out, size_t tid,
+                                              size_t nthreads) {
+  const int q4 = H / 4;
+  for (size_t i = tid; i < (size_t)T * q4; i += nthreads) {
+    const int t = (int)(i / q4), c = (int)(i - (size_t)t * q4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int id = ids[t * k + j];
+      if (id < 0 || id >= E) continue;
+      const float4 v = reinterpret_cast<const float4*>(merged + ((size_t)t * k + j) * H)[c];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    ushort4 o;
+    o.x = f32_to_bf16(acc.x); o.y = f32_to_bf16(acc.y); o.z = f32_to_bf16(acc.z); o.w = f32_to_bf16(acc.w);
+    reinterpret_cast<ushort4*>(out + (size_t)t * H)[c] = o;
+  }
+}
+
 // Inclusive scan across the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -61,37 +84,74 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// ------------------------------------------------------------------ planner
+// ------------------------------------------------------------------ page-in copy
 
 namespace {
-constexpr int kPlanThreads = 256;
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 2;
+}
+
+// Every thread of the grid takes 16-byte chunks gtid, gtid + gstride, ...,
+// kCopyUnroll loads in flight before the stores.
+__device__ __forceinline__ void copy_chunks(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                            size_t n16, size_t gtid, size_t gstride) {
+  for (size_t base = gtid; base < n16; base += kCopyUnroll * gstride) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q) {
+      size_t i = base + q * gstride;
+      if (i < n16) v[q] = src[i];
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q) {
+      size_t i = base + q * gstride;
+      if (i < n16) dst[i] = v[q];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ planning + page-in
+
+namespace {
+constexpr int kPlanThreads = kCopyThreads;
 constexpr int kPlanWaves = kPlanThreads / 64;
 // prefix values: missing, present, entries, GEMV hit/miss, MFMA tiles hit/miss
 constexpr int kScanVals = 7;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
-    int32_t* __restrict__ blk, const int32_t* __restrict__ ids, int n, int E, int K, int MW,
-    Offsets o, int mfma_min, int32_t* __restrict__ work, unsigned long long* __restrict__ stats) {
+// One device-planned wave (all routed experts of a step with T*k <= K), in LDS.
+// Every workgroup computes the same plan from state copy `cur`; workgroup 0
+// publishes it (plan, new state in the other copy, slot map, work lists,
+// counters), then all workgroups copy their share of the missing experts.
+__global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
+    int32_t* __restrict__ blk, const int32_t* __restrict__ ids, int n, int E, int K, int MW, Offsets o,
+    int mfma_min, int32_t* __restrict__ work, unsigned long long* __restrict__ stats,
+    const uint8_t* __restrict__ host_rows, uint8_t* __restrict__ slots, size_t stride, size_t copy_bytes,
+    int do_copy) {
   __shared__ int s_es[kMaxExperts];        // expert -> slot (updated in place)
   __shared__ int s_cnt[kMaxExperts];       // entries per expert
   __shared__ int s_se[kMaxExperts];        // slot -> expert
   __shared__ unsigned s_lu[kMaxExperts];   // slot last use
-  __shared__ int s_cand[kMaxExperts];      // slot is evictable in this wave
+  __shared__ unsigned char s_cand[kMaxExperts];   // slot is evictable in this wave
   __shared__ int s_victim[kMaxExperts];    // victims by rank
+  __shared__ int s_plan_e[kMaxExperts];    // r-th missing expert
   __shared__ int s_ids[kMaxExperts];       // valid id or -1
-  __shared__ int s_pref[kScanVals][kMaxExperts];   // exclusive prefixes per expert
+  __shared__ short s_pref[kScanVals][kMaxExperts];   // exclusive prefixes per expert (< 2^15)
   __shared__ int s_wtot[kScanVals][kPlanWaves];
   __shared__ int s_tot[kScanVals];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const unsigned tick = (unsigned)blk[o.tick];
+  const bool publish = blockIdx.x == 0;
+  const int cur = blk[o.cur] & 1;
+  const int32_t* st = blk + o.state0 + cur * o.state_stride;           // read: current copy
+  int32_t* nst = blk + o.state0 + (cur ^ 1) * o.state_stride;           // written by workgroup 0
+  const unsigned tick = (unsigned)st[o.tick];
   if (tid == 0) s_bad = 0;
-  for (int e = tid; e < E; e += kPlanThreads) { s_es[e] = blk[o.expert_slot + e]; s_cnt[e] = 0; }
+  for (int e = tid; e < E; e += kPlanThreads) { s_es[e] = st[o.expert_slot + e]; s_cnt[e] = 0; }
   for (int j = tid; j < K; j += kPlanThreads) {
-    s_se[j] = blk[o.slot_expert + j];
-    s_lu[j] = (unsigned)blk[o.last_use + j];
+    s_se[j] = st[o.slot_expert + j];
+    s_lu[j] = (unsigned)st[o.last_use + j];
   }
   __syncthreads();
   for (int i = tid; i < n; i += kPlanThreads) {
@@ -144,7 +204,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
       int e = e0 + q;
       if (e >= E) break;
 #pragma unroll
-      for (int v = 0; v < kScanVals; ++v) s_pref[v][e] = run[v];
+      for (int v = 0; v < kScanVals; ++v) s_pref[v][e] = (short)run[v];
       int c = s_cnt[e];
       if (c > 0) {
         const int miss = s_es[e] < 0;
@@ -175,119 +235,108 @@ __global__ __launch_bounds__(kPlanThreads) void plan_single_wave_kernel(
   }
   __syncthreads();
   // Place the i-th missing expert (ascending id) into the i-th victim.
-  int32_t* plan_e = blk + o.plan_expert;
-  int32_t* plan_s = blk + o.plan_slot;
-  int32_t* plan_v = blk + o.plan_evicted;
   for (int e = tid; e < E; e += kPlanThreads) {
     if (s_cnt[e] == 0 || s_es[e] >= 0) continue;
     int r = s_pref[0][e];
     int j = s_victim[r];
     int old = s_se[j];
-    plan_e[r] = e; plan_s[r] = j; plan_v[r] = old;
+    s_plan_e[r] = e;
+    if (publish) {
+      blk[o.plan_expert + r] = e; blk[o.plan_slot + r] = j; blk[o.plan_evicted + r] = old;
+    }
     s_se[j] = e;
     s_es[e] = j;
     if (old >= 0) s_es[old] = -1;      // old is outside the wave: no other thread reads it
   }
   __syncthreads();
-  // The wave is one use: stamp every routed expert's slot; emit work lists.
-  int32_t* used_expert = work + o.used_expert;
-  int32_t* used_slot = work + o.used_slot;
-  int32_t* used_off = work + o.used_off;
-  int32_t* gemv_u = work + o.gemv_u;
-  int32_t* tile_u = work + o.tile_u;
-  int32_t* tile_row = work + o.tile_row;
-  for (int e = tid; e < E; e += kPlanThreads) {
-    int c = s_cnt[e];
-    if (c == 0) continue;
-    int j = s_es[e];
-    s_lu[j] = tick;
-    int u = s_pref[1][e];
-    used_expert[u] = e;
-    used_slot[u] = j;
-    used_off[u] = s_pref[2][e];
-    // was this expert missing? (its missing-prefix steps up right after it)
-    const bool miss = (e + 1 < E ? s_pref[0][e + 1] : n_miss) > s_pref[0][e];
-    if (c < mfma_min) {
-      gemv_u[miss ? g_hit + s_pref[4][e] : s_pref[3][e]] = u;
-    } else {
-      int t0 = miss ? t_hit + s_pref[6][e] : s_pref[5][e];
-      for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
+  if (publish) {
+    // The wave is one use: stamp every routed expert's slot; emit work lists.
+    int32_t* used_expert = work + o.used_expert;
+    int32_t* used_slot = work + o.used_slot;
+    int32_t* used_off = work + o.used_off;
+    int32_t* gemv_u = work + o.gemv_u;
+    int32_t* tile_u = work + o.tile_u;
+    int32_t* tile_row = work + o.tile_row;
+    for (int e = tid; e < E; e += kPlanThreads) {
+      int c = s_cnt[e];
+      if (c == 0) continue;
+      int j = s_es[e];
+      s_lu[j] = tick;
+      int u = s_pref[1][e];
+      used_expert[u] = e;
+      used_slot[u] = j;
+      used_off[u] = s_pref[2][e];
+      // was this expert missing? (its missing-prefix steps up right after it)
+      const bool miss = (e + 1 < E ? (int)s_pref[0][e + 1] : n_miss) > (int)s_pref[0][e];
+      if (c < mfma_min) {
+        gemv_u[miss ? g_hit + s_pref[4][e] : s_pref[3][e]] = u;
+      } else {
+        int t0 = miss ? t_hit + s_pref[6][e] : s_pref[5][e];
+        for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
+      }
+    }
+    __syncthreads();
+    // Entries: ascending entry index inside each expert; slot map.
+    int32_t* entries = work + o.entries;
+    int32_t* slot_of = blk + o.slot_of;
+    for (int i = tid; i < n; i += kPlanThreads) {
+      int id = s_ids[i];
+      if (id < 0) { slot_of[i] = -1; continue; }
+      int r = 0;
+      for (int q = 0; q < i; ++q) r += s_ids[q] == id;
+      entries[s_pref[2][id] + r] = i;
+      slot_of[i] = s_es[id];
+    }
+    // The new LRU state goes into the other copy; a later kernel of the step flips `cur`.
+    for (int e = tid; e < E; e += kPlanThreads) nst[o.expert_slot + e] = s_es[e];
+    for (int j = tid; j < K; j += kPlanThreads) {
+      nst[o.slot_expert + j] = s_se[j];
+      nst[o.last_use + j] = (int32_t)s_lu[j];
+    }
+    if (tid == 0) {
+      const int nw = D > 0 ? 1 : 0;
+      nst[o.tick] = (int32_t)(tick + nw);
+      blk[o.n_waves] = nw;
+      blk[o.plan_count] = n_miss;
+      int32_t* hdr = work + o.hdr;
+      hdr[0] = nw;
+      hdr[hdr_wave_u(MW, 0)] = 0; hdr[hdr_wave_u(MW, 1)] = D;
+      hdr[hdr_gemv(MW, 0)] = 0;   hdr[hdr_gemv(MW, 1)] = n_gemv;
+      hdr[hdr_tile(MW, 0)] = 0;   hdr[hdr_tile(MW, 1)] = n_tiles;
+      hdr[hdr_gemv_split(MW, 0)] = g_hit;
+      hdr[hdr_tile_split(MW, 0)] = t_hit;
+      used_off[D] = n_valid;
+      atomicAdd(stats + ST_STEPS, 1ull);
+      atomicAdd(stats + ST_DEVICE_PLANNED, 1ull);
+      atomicAdd(stats + ST_WAVES, (unsigned long long)nw);
+      atomicAdd(stats + ST_PAGE_INS, (unsigned long long)n_miss);
+      atomicAdd(stats + ST_DISTINCT, (unsigned long long)D);
+      atomicAdd(stats + ST_ENTRIES, (unsigned long long)n_valid);
+      if (s_bad) atomicAdd(stats + ST_BAD_IDS, (unsigned long long)s_bad);
     }
   }
-  __syncthreads();
-  // Entries: ascending entry index inside each expert; slot map.
-  int32_t* entries = work + o.entries;
-  int32_t* slot_of = blk + o.slot_of;
-  for (int i = tid; i < n; i += kPlanThreads) {
-    int id = s_ids[i];
-    if (id < 0) { slot_of[i] = -1; continue; }
-    int r = 0;
-    for (int q = 0; q < i; ++q) r += s_ids[q] == id;
-    entries[s_pref[2][id] + r] = i;
-    slot_of[i] = s_es[id];
-  }
-  // Write back the LRU state.
-  for (int e = tid; e < E; e += kPlanThreads) blk[o.expert_slot + e] = s_es[e];
-  for (int j = tid; j < K; j += kPlanThreads) {
-    blk[o.slot_expert + j] = s_se[j];
-    blk[o.last_use + j] = (int32_t)s_lu[j];
-  }
-  if (tid == 0) {
-    const int nw = D > 0 ? 1 : 0;
-    blk[o.tick] = (int32_t)(tick + nw);
-    blk[o.n_waves] = nw;
-    blk[o.plan_count] = n_miss;
-    int32_t* hdr = work + o.hdr;
-    hdr[0] = nw;
-    hdr[hdr_wave_u(MW, 0)] = 0; hdr[hdr_wave_u(MW, 1)] = D;
-    hdr[hdr_gemv(MW, 0)] = 0;   hdr[hdr_gemv(MW, 1)] = n_gemv;
-    hdr[hdr_tile(MW, 0)] = 0;   hdr[hdr_tile(MW, 1)] = n_tiles;
-    hdr[hdr_gemv_split(MW, 0)] = g_hit;
-    hdr[hdr_tile_split(MW, 0)] = t_hit;
-    used_off[D] = n_valid;
-    atomicAdd(stats + ST_STEPS, 1ull);
-    atomicAdd(stats + ST_DEVICE_PLANNED, 1ull);
-    atomicAdd(stats + ST_WAVES, (unsigned long long)nw);
-    atomicAdd(stats + ST_PAGE_INS, (unsigned long long)n_miss);
-    atomicAdd(stats + ST_DISTINCT, (unsigned long long)D);
-    atomicAdd(stats + ST_ENTRIES, (unsigned long long)n_valid);
-    if (s_bad) atomicAdd(stats + ST_BAD_IDS, (unsigned long long)s_bad);
+  if (!do_copy) return;
+  // Page-in: the r-th missing expert's blob into its victim slot, every workgroup
+  // taking its share of the 16-byte chunks.
+  const size_t n16 = copy_bytes / 16;
+  const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t gstride = (size_t)gridDim.x * blockDim.x;
+  for (int r = 0; r < n_miss; ++r) {
+    const uint4* src = reinterpret_cast<const uint4*>(host_rows + (size_t)s_plan_e[r] * stride);
+    uint4* dst = reinterpret_cast<uint4*>(slots + (size_t)s_victim[r] * stride);
+    copy_chunks(dst, src, n16, gtid, gstride);
   }
 }
 
-void launch_plan_single_wave(int32_t* blk, const int32_t* ids, int n, const Dims& d,
-                             const Offsets& o, int mfma_min, int32_t* work,
-                             unsigned long long* stats, hipStream_t s) {
-  plan_single_wave_kernel<<<1, kPlanThreads, 0, s>>>(blk, ids, n, d.E, d.K, d.max_waves, o,
-                                                     mfma_min, work, stats);
+void launch_plan_page_in(int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
+                         int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
+                         uint8_t* slots, size_t stride, size_t copy_bytes, bool copy, int grid, hipStream_t s) {
+  plan_page_in_kernel<<<copy ? grid : 1, kPlanThreads, 0, s>>>(blk, ids, n, d.E, d.K, d.max_waves, o, mfma_min,
+                                                               work, stats, host_rows, slots, stride, copy_bytes,
+                                                               copy ? 1 : 0);
 }
 
-// ------------------------------------------------------------------ page-in
-
-namespace {
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 2;
-}
-
-// Every thread of the grid takes 16-byte chunks gtid, gtid + gstride, ...,
-// kCopyUnroll loads in flight before the stores.
-__device__ __forceinline__ void copy_chunks(uint4* __restrict__ dst, const uint4* __restrict__ src,
-                                            size_t n16, size_t gtid, size_t gstride) {
-  for (size_t base = gtid; base < n16; base += kCopyUnroll * gstride) {
-    uint4 v[kCopyUnroll];
-#pragma unroll
-    for (int q = 0; q < kCopyUnroll; ++q) {
-      size_t i = base + q * gstride;
-      if (i < n16) v[q] = src[i];
-    }
-#pragma unroll
-    for (int q = 0; q < kCopyUnroll; ++q) {
-      size_t i = base + q * gstride;
-      if (i < n16) dst[i] = v[q];
-    }
-  }
-}
-
+// Copy the planned experts of one host-planned wave (plan already in the layer block).
 __global__ __launch_bounds__(kCopyThreads) void page_in_kernel(
     const int32_t* __restrict__ blk, Offsets o, int wave, int K, const uint8_t* __restrict__ host_rows,
     uint8_t* __restrict__ slots, size_t stride, size_t copy_bytes) {
@@ -342,98 +391,90 @@ template <> struct Fmt<PE_W_FP8_B128> { static constexpr int VPC = 16; };
 template <> struct Fmt<PE_W_INT4_G128> { static constexpr int VPC = 32; };
 }  // namespace
 
-// Dot products of the chunks of one weight row with MB token vectors staged
-// in LDS as bf16 [MB][C].  `scale_at(col)` gives the multiplier of the block
-// or group containing column col (bf16: unused).
+// Loads of one row's chunks for one lane: chunks lig, lig + LG, ... (at most
+// kMaxChunksInFlight per call, starting at chunk c0).
+__device__ __forceinline__ void load_row(const uint4* __restrict__ row, int n_ch, int c0, int LG,
+                                         uint4 (&w)[kMaxChunksInFlight]) {
+#pragma unroll
+  for (int q = 0; q < kMaxChunksInFlight; ++q) {
+    const int c = c0 + q * LG;
+    if (c < n_ch) w[q] = row[c];
+  }
+}
+
+// Dot products of loaded chunks with MB token vectors staged in LDS as bf16
+// [MB][C].  fp32 FMA in a fixed order: chunk by chunk, element by element; the
+// FP8 block / int4 group scale multiplies each chunk's partial sum.
 template <int FMT, int MB>
-__device__ __forceinline__ void row_dot(const uint4* __restrict__ row, int n_ch, int lig, int LG,
+__device__ __forceinline__ void dot_row(const uint4 (&w)[kMaxChunksInFlight], int n_ch, int c0, int LG,
                                         const uint16_t* __restrict__ xs, int C, int m,
                                         const float* __restrict__ s_fp8_row,   // fp8: scales of this row's 128-row block
                                         const uint16_t* __restrict__ s_i4_row, // int4: scales of this row
                                         float (&acc)[MB]) {
   constexpr int VPC = Fmt<FMT>::VPC;
-  for (int c0 = lig; c0 < n_ch; c0 += LG * kMaxChunksInFlight) {
-    uint4 w[kMaxChunksInFlight];
 #pragma unroll
-    for (int q = 0; q < kMaxChunksInFlight; ++q) {
-      int c = c0 + q * LG;
-      if (c < n_ch) w[q] = row[c];
-    }
+  for (int q = 0; q < kMaxChunksInFlight; ++q) {
+    const int c = c0 + q * LG;
+    if (c >= n_ch) break;
+    const int col = c * VPC;
+    const uint32_t wd[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+    if constexpr (FMT == PE_W_BF16) {
 #pragma unroll
-    for (int q = 0; q < kMaxChunksInFlight; ++q) {
-      int c = c0 + q * LG;
-      if (c >= n_ch) break;
-      const int col = c * VPC;
-      const uint32_t wd[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
-      if constexpr (FMT == PE_W_BF16) {
+      for (int t = 0; t < MB; ++t) {
+        if (t >= m) break;
+        const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * C + col);
+        const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
+        float a = acc[t];
 #pragma unroll
-        for (int t = 0; t < MB; ++t) {
-          if (t >= m) break;
-          const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * C + col);
+        for (int p = 0; p < 4; ++p) {
+          a = __builtin_fmaf(bf16_lo(wd[p]), bf16_lo(xd[p]), a);
+          a = __builtin_fmaf(bf16_hi(wd[p]), bf16_hi(xd[p]), a);
+        }
+        acc[t] = a;
+      }
+    } else if constexpr (FMT == PE_W_FP8_B128) {
+      // 16 e4m3 codes, decoded exactly by the hardware conversion (OCP e4m3fn),
+      // word by word inside the token loop to keep few values live.
+      const float sc = s_fp8_row[col >> 7];
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        if (t >= m) break;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+        const uint4 x0 = xp[0], x1 = xp[1];
+        const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float part = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
+          part = __builtin_fmaf(lo[0], bf16_lo(xd[2 * p]), part);
+          part = __builtin_fmaf(lo[1], bf16_hi(xd[2 * p]), part);
+          part = __builtin_fmaf(hi[0], bf16_lo(xd[2 * p + 1]), part);
+          part = __builtin_fmaf(hi[1], bf16_hi(xd[2 * p + 1]), part);
+        }
+        acc[t] = __builtin_fmaf(sc, part, acc[t]);
+      }
+    } else {
+      // 32 nibbles; element 2i is the low nibble of byte i; value = nibble - 8
+      // (exact in fp32), decoded byte by byte inside the token loop.
+      const float sc = half_bits_to_f32(s_i4_row[col >> 7]);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        if (t >= m) break;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+        float part = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 xv = xp[v];
           const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
-          float a = acc[t];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            a = __builtin_fmaf(bf16_lo(wd[p]), bf16_lo(xd[p]), a);
-            a = __builtin_fmaf(bf16_hi(wd[p]), bf16_hi(xd[p]), a);
-          }
-          acc[t] = a;
-        }
-      } else if constexpr (FMT == PE_W_FP8_B128) {
-        // 16 e4m3 codes; the hardware conversion decodes OCP e4m3fn exactly.
-        float wf[16];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
-          auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
-          wf[4 * p + 0] = lo[0]; wf[4 * p + 1] = lo[1];
-          wf[4 * p + 2] = hi[0]; wf[4 * p + 3] = hi[1];
-        }
-        const float sc = s_fp8_row[col >> 7];
-#pragma unroll
-        for (int t = 0; t < MB; ++t) {
-          if (t >= m) break;
-          const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
-          const uint4 x0 = xp[0], x1 = xp[1];
-          const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          float part = 0.0f;
-#pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            part = __builtin_fmaf(wf[2 * p], bf16_lo(xd[p]), part);
-            part = __builtin_fmaf(wf[2 * p + 1], bf16_hi(xd[p]), part);
-          }
-          acc[t] = __builtin_fmaf(sc, part, acc[t]);
-        }
-      } else {
-        // 32 nibbles; element 2i is the low nibble of byte i; value = nibble - 8.
-        float wf[32];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            uint32_t byte = (wd[p] >> (8 * b)) & 0xFFu;
-            wf[8 * p + 2 * b] = (float)(int)(byte & 0xFu) - 8.0f;
-            wf[8 * p + 2 * b + 1] = (float)(int)(byte >> 4) - 8.0f;
+            const uint32_t byte = (wd[v] >> (8 * b)) & 0xFFu;
+            part = __builtin_fmaf((float)(int)(byte & 0xFu) - 8.0f, bf16_lo(xd[b]), part);
+            part = __builtin_fmaf((float)(int)(byte >> 4) - 8.0f, bf16_hi(xd[b]), part);
           }
         }
-        const float sc = half_bits_to_f32(s_i4_row[col >> 7]);
-#pragma unroll
-        for (int t = 0; t < MB; ++t) {
-          if (t >= m) break;
-          const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
-          float part = 0.0f;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint4 xv = xp[v];
-            const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              part = __builtin_fmaf(wf[8 * v + 2 * p], bf16_lo(xd[p]), part);
-              part = __builtin_fmaf(wf[8 * v + 2 * p + 1], bf16_hi(xd[p]), part);
-            }
-          }
-          acc[t] = __builtin_fmaf(sc, part, acc[t]);
-        }
+        acc[t] = __builtin_fmaf(sc, part, acc[t]);
       }
     }
   }
@@ -470,7 +511,8 @@ __device__ __forceinline__ void stage_consecutive(uint16_t* xs, const uint16_t* 
 }
 
 struct GemvItem {
-  int u, slot, off, m;
+  int slot, off, m;
+  const int32_t* ent;   // the expert's entries (t*k + j), ascending, at sorted positions off..off+m-1
 };
 
 // Range [b, e) of a wave's list selected by a.part: 0 all, 1 resident before
@@ -480,22 +522,86 @@ __device__ __forceinline__ void part_range(const ExpertArgs& a, int begin, int s
   e = a.part == 1 ? split : end;
 }
 
+// The item-th GEMV expert among those already resident, found from the routed
+// ids and the current LRU-state copy without the published plan, so it can run
+// while the planning + page-in kernel is still in flight.  Same numbering as the
+// planner: present experts by ascending id (sorted positions are the prefix of
+// their entry counts), GEMV hits in ascending id.  Block-wide; n = T*k <= K.
+__device__ bool lean_hit_item(const ExpertArgs& a, int item, GemvItem& it) {
+  __shared__ int s_id[kMaxExperts];
+  __shared__ int s_cnt[kMaxExperts];              // entries with this id (first occurrences only)
+  __shared__ unsigned char s_hitg[kMaxExperts];   // first occurrence of a resident GEMV expert
+  __shared__ int s_ent[kMaxExperts];
+  __shared__ int s_sel[4];
+  const int n = a.T * a.k, tid = threadIdx.x;
+  const int32_t* st = a.blk + a.o.state0 + (a.blk[a.o.cur] & 1) * a.o.state_stride;
+  if (tid == 0) s_sel[0] = -1;
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int id = a.ids[i];
+    s_id[i] = (id >= 0 && id < a.E) ? id : -1;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int id = s_id[i];
+    int cnt = 0;
+    bool first = id >= 0;
+    for (int j = 0; j < n; ++j) {
+      if (s_id[j] != id) continue;
+      ++cnt;
+      if (j < i) first = false;
+    }
+    s_cnt[i] = first ? cnt : 0;
+    s_hitg[i] = first && cnt < a.mfma_min && st[a.o.expert_slot + id] >= 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += blockDim.x) {
+    if (!s_hitg[i]) continue;
+    const int id = s_id[i];
+    int rank = 0, off = 0;
+    for (int j = 0; j < n; ++j) {
+      if (s_cnt[j] == 0 || s_id[j] >= id) continue;
+      off += s_cnt[j];
+      rank += s_hitg[j];
+    }
+    if (rank == item) { s_sel[0] = id; s_sel[1] = off; s_sel[2] = s_cnt[i]; s_sel[3] = st[a.o.expert_slot + id]; }
+  }
+  __syncthreads();
+  const int e = s_sel[0];
+  if (e < 0) return false;
+  for (int i = tid; i < n; i += blockDim.x) {
+    if (s_id[i] != e) continue;
+    int r = 0;
+    for (int j = 0; j < i; ++j) r += s_id[j] == e;
+    s_ent[r] = i;
+  }
+  __syncthreads();
+  it.off = s_sel[1];
+  it.m = s_sel[2];
+  it.slot = s_sel[3];
+  it.ent = s_ent;
+  return true;
+}
+
 __device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvItem& it) {
+  if (a.lean) return lean_hit_item(a, item, it);
   const int32_t* hdr = a.work + a.o.hdr;
   int g0, g1;
   part_range(a, hdr[hdr_gemv(a.MW, a.wave)], hdr[hdr_gemv_split(a.MW, a.wave)], hdr[hdr_gemv(a.MW, a.wave + 1)], g0, g1);
   if (item >= g1 - g0) return false;
-  it.u = a.work[a.o.gemv_u + g0 + item];
-  it.slot = a.work[a.o.used_slot + it.u];
-  it.off = a.work[a.o.used_off + it.u];
-  it.m = a.work[a.o.used_off + it.u + 1] - it.off;
+  const int u = a.work[a.o.gemv_u + g0 + item];
+  it.slot = a.work[a.o.used_slot + u];
+  it.off = a.work[a.o.used_off + u];
+  it.m = a.work[a.o.used_off + u + 1] - it.off;
+  it.ent = a.work + a.o.entries + it.off;
   return true;
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 // Gate/up projection + SwiGLU for one used expert (blockIdx.y) and a range of
-// intermediate rows (blockIdx.x).  h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).
+// intermediate rows (blockIdx.x): every lane group takes one row i and computes
+// h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).  The weight loads of both rows are
+// issued before the token vectors are staged.
 template <int FMT, int MB>
 __global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a, int LG, int rows_per_block) {
   extern __shared__ __align__(16) uint16_t xs[];   // [MB][H]
@@ -510,36 +616,46 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a
   const uint16_t* S13h = reinterpret_cast<const uint16_t*>(blob + a.off_s13);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int row_step = (kGemvThreads / 64) * groups;
-  const int r0 = blockIdx.x * rows_per_block;
-  const int r1 = min(I, r0 + rows_per_block);
-  const int32_t* ent = a.work + a.o.entries + it.off;
+  const int i = blockIdx.x * rows_per_block + wv * groups + grp;    // this group's row
+  const bool active = i < I;
+  const int ru = I + i;
+  const uint4* rg = W13 + (size_t)i * n_ch;
+  const uint4* rup = W13 + (size_t)ru * n_ch;
+  const int32_t* ent = it.ent;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
+    uint4 wg[kMaxChunksInFlight], wu[kMaxChunksInFlight];
+    if (active) { load_row(rg, n_ch, lig, LG, wg); load_row(rup, n_ch, lig, LG, wu); }
     __syncthreads();
     stage_rows(xs, a.x, H, ent + tb, mb, a.k);
     __syncthreads();
-    for (int i = r0 + wv * groups + grp; i < r1; i += row_step) {
-      float g[MB], u[MB];
+    if (!active) continue;
+    float g[MB], u[MB];
 #pragma unroll
-      for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
-      const int ru = I + i;
-      row_dot<FMT, MB>(W13 + (size_t)i * n_ch, n_ch, lig, LG, xs, H, mb,
-                       S13f + (size_t)(i >> 7) * (H / 128), S13h + (size_t)i * (H / 128), g);
-      row_dot<FMT, MB>(W13 + (size_t)ru * n_ch, n_ch, lig, LG, xs, H, mb,
-                       S13f + (size_t)(ru >> 7) * (H / 128), S13h + (size_t)ru * (H / 128), u);
-      group_reduce<MB>(g, LG);
-      group_reduce<MB>(u, LG);
+    for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
+    const float* sgf = S13f + (size_t)(i >> 7) * (H / 128);
+    const float* suf = S13f + (size_t)(ru >> 7) * (H / 128);
+    const uint16_t* sgh = S13h + (size_t)i * (H / 128);
+    const uint16_t* suh = S13h + (size_t)ru * (H / 128);
+    for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
+      dot_row<FMT, MB>(wg, n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
+      dot_row<FMT, MB>(wu, n_ch, c0, LG, xs, H, mb, suf, suh, u);
+      if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
+      load_row(rg, n_ch, c0 + LG * kMaxChunksInFlight, LG, wg);
+      load_row(rup, n_ch, c0 + LG * kMaxChunksInFlight, LG, wu);
+    }
+    group_reduce<MB>(g, LG);
+    group_reduce<MB>(u, LG);
 #pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        if (t < mb && lig == t)
-          a.h[(size_t)(it.off + tb + t) * I + i] = f32_to_bf16(silu_f(g[t]) * u[t]);
-      }
+    for (int t = 0; t < MB; ++t) {
+      if (t < mb && lig == t)
+        a.h[(size_t)(it.off + tb + t) * I + i] = f32_to_bf16(silu_f(g[t]) * u[t]);
     }
   }
 }
 
-// Down projection for one used expert: merged[entry, n] = w[entry] * (W2[n] . h[pos]).
+// Down projection for one used expert: every lane group takes two rows n, n+1
+// and writes merged[entry, n] = w[entry] * (W2[n] . h[pos]).
 template <int FMT, int MB>
 __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, int LG, int rows_per_block) {
   extern __shared__ __align__(16) uint16_t hs[];   // [MB][I]
@@ -554,39 +670,52 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, i
   const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int row_step = (kGemvThreads / 64) * groups;
-  const int r0 = blockIdx.x * rows_per_block;
-  const int r1 = min(H, r0 + rows_per_block);
-  const int32_t* ent = a.work + a.o.entries + it.off;
+  const int n0 = blockIdx.x * rows_per_block + 2 * (wv * groups + grp);   // rows n0, n0 + 1
+  const bool act0 = n0 < H, act1 = n0 + 1 < H;
+  const uint4* r0 = W2 + (size_t)n0 * n_ch;
+  const uint4* r1 = W2 + (size_t)(n0 + 1) * n_ch;
+  const int32_t* ent = it.ent;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
+    uint4 w0[kMaxChunksInFlight], w1[kMaxChunksInFlight];
+    if (act0) load_row(r0, n_ch, lig, LG, w0);
+    if (act1) load_row(r1, n_ch, lig, LG, w1);
     __syncthreads();
     stage_consecutive(hs, a.h, I, it.off + tb, mb);
     __syncthreads();
-    for (int n = r0 + wv * groups + grp; n < r1; n += row_step) {
-      float y[MB];
+    if (!act0) continue;
+    float y0[MB], y1[MB];
 #pragma unroll
-      for (int t = 0; t < MB; ++t) y[t] = 0.0f;
-      row_dot<FMT, MB>(W2 + (size_t)n * n_ch, n_ch, lig, LG, hs, I, mb,
-                       S2f + (size_t)(n >> 7) * (I / 128), S2h + (size_t)n * (I / 128), y);
-      group_reduce<MB>(y, LG);
+    for (int t = 0; t < MB; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
+    for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
+      dot_row<FMT, MB>(w0, n_ch, c0, LG, hs, I, mb, S2f + (size_t)(n0 >> 7) * (I / 128),
+                       S2h + (size_t)n0 * (I / 128), y0);
+      if (act1)
+        dot_row<FMT, MB>(w1, n_ch, c0, LG, hs, I, mb, S2f + (size_t)((n0 + 1) >> 7) * (I / 128),
+                         S2h + (size_t)(n0 + 1) * (I / 128), y1);
+      if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
+      load_row(r0, n_ch, c0 + LG * kMaxChunksInFlight, LG, w0);
+      if (act1) load_row(r1, n_ch, c0 + LG * kMaxChunksInFlight, LG, w1);
+    }
+    group_reduce<MB>(y0, LG);
+    group_reduce<MB>(y1, LG);
 #pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        if (t < mb && lig == t) {
-          const int e = ent[tb + t];
-          a.merged[(size_t)e * H + n] = a.topk_w[e] * y[t];
-        }
+    for (int t = 0; t < MB; ++t) {
+      if (t < mb && lig == t) {
+        const int e = ent[tb + t];
+        a.merged[(size_t)e * H + n0] = a.topk_w[e] * y0[t];
+        if (act1) a.merged[(size_t)e * H + n0 + 1] = a.topk_w[e] * y1[t];
       }
     }
   }
 }
 
-// Lanes per row: 64 when the row has a multiple of 64 chunks, else the largest
-// power of two (>= 8) dividing the chunk count, so every lane has work.
+// Lanes per row: the smallest power of two (8..64) that keeps a row at most
+// kMaxChunksInFlight chunks per lane, so a lane group issues a whole row in one
+// round of loads and short rows give a wave several rows at once.
 static int lanes_per_row(int n_ch) {
-  if (n_ch % 64 == 0 || n_ch >= 256) return 64;
-  int lg = 32;
-  while (lg > 8 && n_ch % lg) lg >>= 1;
+  int lg = 8;
+  while (lg < 64 && n_ch > lg * kMaxChunksInFlight) lg <<= 1;
   return lg;
 }
 
@@ -601,7 +730,7 @@ template <int FMT>
 static void gate_up_fmt(const ExpertArgs& a, int items, int mb, hipStream_t s) {
   const int n_ch = a.H / Fmt<FMT>::VPC;
   const int LG = lanes_per_row(n_ch);
-  const int rows_per_block = (kGemvThreads / 64) * (64 / LG) * 2;
+  const int rows_per_block = (kGemvThreads / 64) * (64 / LG);
   dim3 grid((a.I + rows_per_block - 1) / rows_per_block, items);
   size_t lds = (size_t)mb * a.H * 2;
   switch (mb) {
@@ -903,30 +1032,21 @@ void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) 
 
 // ------------------------------------------------------------------ top-k sum
 
+// `flip` (device-planned steps): the layer's current-state index, flipped to the
+// copy the planning kernel wrote; nothing reads it while this kernel runs.
 __global__ __launch_bounds__(256) void topk_sum_kernel(const float* __restrict__ merged,
                                                        const int32_t* __restrict__ ids, int T, int k,
-                                                       int E, int H, uint16_t* __restrict__ out) {
-  const int q4 = H / 4;
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)T * q4) return;
-  const int t = (int)(i / q4), c = (int)(i - (size_t)t * q4);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int id = ids[t * k + j];
-    if (id < 0 || id >= E) continue;
-    const float4 v = reinterpret_cast<const float4*>(merged + ((size_t)t * k + j) * H)[c];
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-  }
-  ushort4 o;
-  o.x = f32_to_bf16(acc.x); o.y = f32_to_bf16(acc.y); o.z = f32_to_bf16(acc.z); o.w = f32_to_bf16(acc.w);
-  reinterpret_cast<ushort4*>(out + (size_t)t * H)[c] = o;
+                                                       int E, int H, uint16_t* __restrict__ out, int32_t* flip) {
+  topk_sum_rows(merged, ids, T, k, E, H, out, (size_t)blockIdx.x * blockDim.x + threadIdx.x,
+                (size_t)gridDim.x * blockDim.x);
+  if (flip && blockIdx.x == 0 && threadIdx.x == 0) *flip ^= 1;
 }
 
 void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int E, int H,
-                     uint16_t* out, hipStream_t s) {
+                     uint16_t* out, int32_t* flip, hipStream_t s) {
   const size_t n = (size_t)T * (H / 4);
   const int grid = (int)((n + 255) / 256);
-  topk_sum_kernel<<<grid, 256, 0, s>>>(merged, ids, T, k, E, H, out);
+  topk_sum_kernel<<<grid, 256, 0, s>>>(merged, ids, T, k, E, H, out, flip);
 }
 
 // ------------------------------------------------------------------ LRU reset
@@ -934,12 +1054,16 @@ void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int 
 __global__ void reset_lru_kernel(int32_t* blocks, size_t layer_words, int l0, Offsets o, int E, int K,
                                  int identity) {
   int32_t* blk = blocks + (size_t)(l0 + blockIdx.x) * layer_words;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) blk[o.expert_slot + e] = identity ? e : -1;
-  for (int j = threadIdx.x; j < K; j += blockDim.x) {
-    blk[o.slot_expert + j] = identity ? j : -1;
-    blk[o.last_use + j] = 0;
+  for (int c = 0; c < 2; ++c) {
+    int32_t* st = blk + o.state0 + c * o.state_stride;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) st[o.expert_slot + e] = identity ? e : -1;
+    for (int j = threadIdx.x; j < K; j += blockDim.x) {
+      st[o.slot_expert + j] = identity ? j : -1;
+      st[o.last_use + j] = 0;
+    }
+    if (threadIdx.x == 0) st[o.tick] = 1;
   }
-  if (threadIdx.x == 0) { blk[o.tick] = 1; blk[o.n_waves] = 0; }
+  if (threadIdx.x == 0) { blk[o.cur] = 0; blk[o.n_waves] = 0; }
 }
 
 void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const Offsets& o,

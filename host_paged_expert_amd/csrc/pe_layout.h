@@ -41,30 +41,46 @@ inline Dims make_dims(int L, int E, int K, int k, int H, int I, int max_tokens) 
   return d;
 }
 
-// Per-layer block (int32 words): LRU state, the last step's plans and slot map.
+// Per-layer block (int32 words): two copies of the LRU state, the index of the
+// current one, the last step's plans and slot map.  A device-planned step reads
+// copy `cur` in every block of its planning kernel and writes the new state into
+// the other copy; a later kernel of the same step flips `cur`.  No block can
+// therefore read a half-written state.  Host-planned steps update copy `cur` in
+// place.  tick / slot_expert / expert_slot / last_use are offsets inside a copy.
 struct LayerLayout {
   size_t tick;          // [1]    uint32: tick of the next wave
   size_t slot_expert;   // [K]    expert in slot j, -1 = empty
   size_t expert_slot;   // [E]    slot of expert e, -1 = not resident
   size_t last_use;      // [K]    uint32: tick of the wave that last used slot j
+  size_t state_words;   // words of one state copy
+  size_t cur;           // [1]    current state copy (0 or 1)
+  size_t state0;        // first state copy; the second follows at state0 + state_stride
+  size_t state_stride;
   size_t n_waves;       // [1]    waves of the last step
   size_t plan_count;    // [MW]   page-ins of wave w
   size_t plan_expert;   // [MW*K] expert copied in
   size_t plan_slot;     // [MW*K] slot it went to
   size_t plan_evicted;  // [MW*K] previous occupant (-1 = empty)
   size_t slot_of;       // [max_entries] slot entry t*k+j ran in (-1 invalid id)
-  size_t state_words;   // words of the LRU-state prefix (tick..last_use)
+  size_t state_prefix;  // words from the block start through both state copies
   size_t total;         // words per layer (rounded to 64)
+
+  size_t state(int copy) const { return state0 + (size_t)copy * state_stride; }
 };
 
 inline LayerLayout make_layer_layout(const Dims& d) {
   LayerLayout l{};
+  l.tick = 0;
+  l.slot_expert = 1;
+  l.expert_slot = 1 + (size_t)d.K;
+  l.last_use = 1 + (size_t)d.K + d.E;
+  l.state_words = 1 + 2 * (size_t)d.K + d.E;
   size_t o = 0;
-  l.tick = o; o += 1;
-  l.slot_expert = o; o += d.K;
-  l.expert_slot = o; o += d.E;
-  l.last_use = o; o += d.K;
-  l.state_words = o;
+  l.cur = o; o += 1;
+  l.state0 = o;
+  l.state_stride = l.state_words;
+  o += 2 * l.state_words;
+  l.state_prefix = o;
   l.n_waves = o; o += 1;
   l.plan_count = o; o += d.max_waves;
   l.plan_expert = o; o += (size_t)d.max_waves * d.K;
@@ -135,8 +151,9 @@ struct HostPlanSummary {
 };
 
 // Plan one step of one layer on the host (the multi-wave path).  `blk` is a
-// host mirror of the layer block holding the current LRU state; on return it
-// holds the new state, the plans of every wave and the slot map.  `work` is a
+// host mirror of the layer block whose state copy `cur` is current; on return
+// that copy holds the new state, and the block the plans of every wave and the
+// slot map.  `work` is a
 // host mirror of the work arena, filled for the step.  Returns 0 or -1 if the
 // step needs more waves than the layout holds.
 int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,

@@ -25,10 +25,11 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
                    const int32_t* ids, int n_entries, int32_t* blk, int32_t* work,
                    HostPlanSummary* sum) {
   const int E = d.E, K = d.K, MW = d.max_waves;
-  uint32_t tick = (uint32_t)blk[ll.tick];
-  int32_t* slot_expert = blk + ll.slot_expert;
-  int32_t* expert_slot = blk + ll.expert_slot;
-  uint32_t* last_use = reinterpret_cast<uint32_t*>(blk + ll.last_use);
+  int32_t* st = blk + ll.state(blk[ll.cur] & 1);
+  uint32_t tick = (uint32_t)st[ll.tick];
+  int32_t* slot_expert = st + ll.slot_expert;
+  int32_t* expert_slot = st + ll.expert_slot;
+  uint32_t* last_use = reinterpret_cast<uint32_t*>(st + ll.last_use);
   int32_t* slot_of = blk + ll.slot_of;
 
   std::vector<int> cnt(E, 0);
@@ -143,7 +144,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     entries[used_off[uu] + seen[e]++] = i;
     slot_of[i] = used_slot[uu];
   }
-  blk[ll.tick] = (int32_t)tick;
+  st[ll.tick] = (int32_t)tick;
   blk[ll.n_waves] = n_waves;
 
   sum->n_waves = n_waves;
