@@ -462,44 +462,47 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   const bool device_plan = n <= d.K && !(c->cfg.flags & PE_FLAG_FORCE_HOST_PLAN);
 
   if (device_plan) {
-    // One wave.  Planning and page-in are one launch: every workgroup makes the
-    // same LRU decision in LDS from the current state copy (no workgroup waits for
-    // another) and workgroup 0 publishes it, writing the new state into the other
-    // copy.  Meanwhile a second stream runs the experts that were already resident,
-    // each workgroup finding its expert from the ids and the current copy.  The
-    // paged-in experts run after the page-in; the top-k sum joins both and makes
-    // the new state copy current.  No host synchronisation: capturable.
+    // One wave, on the caller's stream only (a second stream would put graph
+    // branches on other hardware queues, whose cross-queue dependencies cost more
+    // than they hide).  Launch A: planning + page-in workgroups (each makes the
+    // same LRU decision in LDS from the current state copy; workgroup 0 publishes
+    // it and writes the new state into the other copy) alongside the gate/up
+    // projection of the experts already resident, which find their expert from the
+    // ids and the current copy.  Launch B: gate/up of the paged-in experts
+    // alongside down of the resident ones.  Launch C: down of the paged-in
+    // experts.  Then the top-k sum, which makes the new state copy current.
+    // No host synchronisation: capturable.
     const int items = std::min(n, d.K);
     // an expert may hold T >= mfma_min entries: then launch the MFMA kernels over
     // the most tiles one wave can have; surplus blocks exit on the device count
     const int tiles = T >= c->mfma_min ? pe::ceil_div(n, pe::kTileM) + items : 0;
-    const bool overlap = !c->unpaged && tiles == 0;
-    if (overlap) {
-      PE_HIP(hipEventRecord(c->ev_fork, s));
-      PE_HIP(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-      pe::ExpertArgs h = expert_args(c, layer, 0, x, topk_w, 1);
-      h.lean = 1;
-      h.ids = topk_ids;
-      h.T = T;
-      h.E = d.E;
-      h.blk = blk;
+    if (!c->unpaged && tiles == 0) {
+      pe::ExpertArgs hit = expert_args(c, layer, 0, x, topk_w, 1);
+      hit.lean = 1;
+      hit.ids = topk_ids;
+      hit.T = T;
+      hit.E = d.E;
+      hit.blk = blk;
+      const pe::ExpertArgs miss = expert_args(c, layer, 0, x, topk_w, 2);
       {
-        StageTimer tm(c, PE_STAGE_GATE_UP, c->side);
-        pe::launch_gemv_gate_up(c->cfg.wtype, h, items, T, c->side);
+        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+        pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l,
+                          slots_l, c->b.stride, c->b.copied, kPageInGrid, hit, items, T, s);
       }
       {
-        StageTimer tm(c, PE_STAGE_DOWN, c->side);
-        pe::launch_gemv_down(c->cfg.wtype, h, items, T, c->side);
+        StageTimer tm(c, PE_STAGE_GATE_UP, s);
+        pe::launch_step_b(c->cfg.wtype, miss, hit, items, T, s);
       }
-      PE_HIP(hipEventRecord(c->ev_join, c->side));
+      StageTimer tm(c, PE_STAGE_DOWN, s);
+      pe::launch_gemv_down(c->cfg.wtype, miss, items, T, s);
+    } else {
+      {
+        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+        pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l, slots_l,
+                                c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
+      }
+      run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
     }
-    {
-      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-      pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l, slots_l,
-                              c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
-    }
-    run_experts(c, layer, 0, overlap ? 2 : 0, x, topk_w, items, T, tiles, s);
-    if (overlap) PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
     {
       StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
       pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out),

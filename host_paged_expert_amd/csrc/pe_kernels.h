@@ -67,6 +67,18 @@ void launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t
 void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
 void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
 
+// Device-planned step on one queue.  Launch A: `P` workgroups plan the wave and
+// page in its missing experts (as launch_plan_page_in) while the others run the
+// gate/up projection of the experts already resident (`hit`, lean discovery).
+// Launch B: the gate/up projection of the paged-in experts (`miss`, published
+// lists) alongside the down projection of the resident ones.  The paged-in
+// experts' down projection and the top-k sum follow as their own launches.
+void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
+                   int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
+                   uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& hit, int items,
+                   int max_m, hipStream_t s);
+void launch_step_b(int wtype, const ExpertArgs& miss, const ExpertArgs& hit, int items, int max_m, hipStream_t s);
+
 // MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
 // tokens).  Need H and I multiples of 128.
 void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 #include "../../include/pe.h"
 #include "pe_kernels.h"
 
@@ -117,32 +119,84 @@ constexpr int kPlanThreads = kCopyThreads;
 constexpr int kPlanWaves = kPlanThreads / 64;
 // prefix values: missing, present, entries, GEMV hit/miss, MFMA tiles hit/miss
 constexpr int kScanVals = 7;
+constexpr size_t al16(size_t b) { return (b + 15) / 16 * 16; }
+}  // namespace
+
+// LDS of one planning workgroup, sized by E experts, K slots and n entries.
+struct PlanLds {
+  int *es, *cnt, *se;
+  unsigned* lu;
+  int *victim, *plan_e, *ids, *wtot, *tot, *bad;
+  short* pref;
+  unsigned char* cand;
+};
+
+constexpr size_t plan_lds_bytes(int E, int K, int n) {
+  return 2 * al16(4 * (size_t)E) + 4 * al16(4 * (size_t)K) + al16(4 * (size_t)n) +
+         al16(4 * kScanVals * kPlanWaves) + al16(4 * kScanVals) + 16 + al16(2 * kScanVals * (size_t)E) +
+         al16((size_t)K);
 }
 
+__device__ __forceinline__ PlanLds carve_plan(char* p, int E, int K, int n) {
+  PlanLds L;
+  L.es = reinterpret_cast<int*>(p); p += al16(4 * (size_t)E);
+  L.cnt = reinterpret_cast<int*>(p); p += al16(4 * (size_t)E);
+  L.se = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.lu = reinterpret_cast<unsigned*>(p); p += al16(4 * (size_t)K);
+  L.victim = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.plan_e = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.ids = reinterpret_cast<int*>(p); p += al16(4 * (size_t)n);
+  L.wtot = reinterpret_cast<int*>(p); p += al16(4 * kScanVals * kPlanWaves);
+  L.tot = reinterpret_cast<int*>(p); p += al16(4 * kScanVals);
+  L.bad = reinterpret_cast<int*>(p); p += 16;
+  L.pref = reinterpret_cast<short*>(p); p += al16(2 * kScanVals * (size_t)E);
+  L.cand = reinterpret_cast<unsigned char*>(p);
+  return L;
+}
+
+struct PlanArgs {
+  int32_t* blk;
+  const int32_t* ids;
+  int n, E, K, MW;
+  Offsets o;
+  int mfma_min;
+  int32_t* work;
+  unsigned long long* stats;
+  const uint8_t* host_rows;
+  uint8_t* slots;
+  size_t stride, copy_bytes;
+  int do_copy;
+};
+
 // One device-planned wave (all routed experts of a step with T*k <= K), in LDS.
-// Every workgroup computes the same plan from state copy `cur`; workgroup 0
-// publishes it (plan, new state in the other copy, slot map, work lists,
-// counters), then all workgroups copy their share of the missing experts.
-__global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
-    int32_t* __restrict__ blk, const int32_t* __restrict__ ids, int n, int E, int K, int MW, Offsets o,
-    int mfma_min, int32_t* __restrict__ work, unsigned long long* __restrict__ stats,
-    const uint8_t* __restrict__ host_rows, uint8_t* __restrict__ slots, size_t stride, size_t copy_bytes,
-    int do_copy) {
-  __shared__ int s_es[kMaxExperts];        // expert -> slot (updated in place)
-  __shared__ int s_cnt[kMaxExperts];       // entries per expert
-  __shared__ int s_se[kMaxExperts];        // slot -> expert
-  __shared__ unsigned s_lu[kMaxExperts];   // slot last use
-  __shared__ unsigned char s_cand[kMaxExperts];   // slot is evictable in this wave
-  __shared__ int s_victim[kMaxExperts];    // victims by rank
-  __shared__ int s_plan_e[kMaxExperts];    // r-th missing expert
-  __shared__ int s_ids[kMaxExperts];       // valid id or -1
-  __shared__ short s_pref[kScanVals][kMaxExperts];   // exclusive prefixes per expert (< 2^15)
-  __shared__ int s_wtot[kScanVals][kPlanWaves];
-  __shared__ int s_tot[kScanVals];
-  __shared__ int s_bad;
+// Each of the `nblocks` planning workgroups computes the same plan from state
+// copy `cur`; workgroup 0 publishes it (plan, new state in the other copy, slot
+// map, work lists, counters); then every workgroup copies its share of the
+// missing experts.
+__device__ void plan_page_in_block(const PlanArgs& p, int block, int nblocks, char* lds) {
+  const int E = p.E, K = p.K, n = p.n, MW = p.MW;
+  const Offsets& o = p.o;
+  int32_t* __restrict__ blk = p.blk;
+  int32_t* __restrict__ work = p.work;
+  unsigned long long* __restrict__ stats = p.stats;
+  const int32_t* __restrict__ ids = p.ids;
+  const int mfma_min = p.mfma_min;
+  PlanLds L = carve_plan(lds, E, K, n);
+  int* s_es = L.es;            // expert -> slot (updated in place)
+  int* s_cnt = L.cnt;          // entries per expert
+  int* s_se = L.se;            // slot -> expert
+  unsigned* s_lu = L.lu;       // slot last use
+  unsigned char* s_cand = L.cand;   // slot is evictable in this wave
+  int* s_victim = L.victim;    // victims by rank
+  int* s_plan_e = L.plan_e;    // r-th missing expert
+  int* s_ids = L.ids;          // valid id or -1
+  int* s_tot = L.tot;
+  int& s_bad = *L.bad;
+  auto s_pref = [&](int v, int e) -> short& { return L.pref[v * E + e]; };
+  auto s_wtot = [&](int v, int w) -> int& { return L.wtot[v * kPlanWaves + w]; };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool publish = blockIdx.x == 0;
+  const bool publish = block == 0;
   const int cur = blk[o.cur] & 1;
   const int32_t* st = blk + o.state0 + cur * o.state_stride;           // read: current copy
   int32_t* nst = blk + o.state0 + (cur ^ 1) * o.state_stride;           // written by workgroup 0
@@ -185,14 +239,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
   for (int v = 0; v < kScanVals; ++v) inc[v] = wave_incl_scan(loc[v], lane);
   if (lane == 63) {
 #pragma unroll
-    for (int v = 0; v < kScanVals; ++v) s_wtot[v][wv] = inc[v];
+    for (int v = 0; v < kScanVals; ++v) s_wtot(v, wv) = inc[v];
   }
   __syncthreads();
   int base[kScanVals];
 #pragma unroll
   for (int v = 0; v < kScanVals; ++v) {
     int b = 0, t = 0;
-    for (int w = 0; w < kPlanWaves; ++w) { if (w < wv) b += s_wtot[v][w]; t += s_wtot[v][w]; }
+    for (int w = 0; w < kPlanWaves; ++w) { if (w < wv) b += s_wtot(v, w); t += s_wtot(v, w); }
     base[v] = b + inc[v] - loc[v];
     if (tid == 0) s_tot[v] = t;
   }
@@ -204,7 +258,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
       int e = e0 + q;
       if (e >= E) break;
 #pragma unroll
-      for (int v = 0; v < kScanVals; ++v) s_pref[v][e] = (short)run[v];
+      for (int v = 0; v < kScanVals; ++v) s_pref(v, e) = (short)run[v];
       int c = s_cnt[e];
       if (c > 0) {
         const int miss = s_es[e] < 0;
@@ -237,7 +291,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
   // Place the i-th missing expert (ascending id) into the i-th victim.
   for (int e = tid; e < E; e += kPlanThreads) {
     if (s_cnt[e] == 0 || s_es[e] >= 0) continue;
-    int r = s_pref[0][e];
+    int r = s_pref(0, e);
     int j = s_victim[r];
     int old = s_se[j];
     s_plan_e[r] = e;
@@ -262,16 +316,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
       if (c == 0) continue;
       int j = s_es[e];
       s_lu[j] = tick;
-      int u = s_pref[1][e];
+      int u = s_pref(1, e);
       used_expert[u] = e;
       used_slot[u] = j;
-      used_off[u] = s_pref[2][e];
+      used_off[u] = s_pref(2, e);
       // was this expert missing? (its missing-prefix steps up right after it)
-      const bool miss = (e + 1 < E ? (int)s_pref[0][e + 1] : n_miss) > (int)s_pref[0][e];
+      const bool miss = (e + 1 < E ? (int)s_pref(0, e + 1) : n_miss) > (int)s_pref(0, e);
       if (c < mfma_min) {
-        gemv_u[miss ? g_hit + s_pref[4][e] : s_pref[3][e]] = u;
+        gemv_u[miss ? g_hit + s_pref(4, e) : s_pref(3, e)] = u;
       } else {
-        int t0 = miss ? t_hit + s_pref[6][e] : s_pref[5][e];
+        int t0 = miss ? t_hit + s_pref(6, e) : s_pref(5, e);
         for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
       }
     }
@@ -284,7 +338,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
       if (id < 0) { slot_of[i] = -1; continue; }
       int r = 0;
       for (int q = 0; q < i; ++q) r += s_ids[q] == id;
-      entries[s_pref[2][id] + r] = i;
+      entries[s_pref(2, id) + r] = i;
       slot_of[i] = s_es[id];
     }
     // The new LRU state goes into the other copy; a later kernel of the step flips `cur`.
@@ -315,25 +369,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(
       if (s_bad) atomicAdd(stats + ST_BAD_IDS, (unsigned long long)s_bad);
     }
   }
-  if (!do_copy) return;
+  if (!p.do_copy) return;
   // Page-in: the r-th missing expert's blob into its victim slot, every workgroup
   // taking its share of the 16-byte chunks.
-  const size_t n16 = copy_bytes / 16;
-  const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t gstride = (size_t)gridDim.x * blockDim.x;
+  const size_t n16 = p.copy_bytes / 16;
+  const size_t gtid = (size_t)block * blockDim.x + threadIdx.x;
+  const size_t gstride = (size_t)nblocks * blockDim.x;
   for (int r = 0; r < n_miss; ++r) {
-    const uint4* src = reinterpret_cast<const uint4*>(host_rows + (size_t)s_plan_e[r] * stride);
-    uint4* dst = reinterpret_cast<uint4*>(slots + (size_t)s_victim[r] * stride);
+    const uint4* src = reinterpret_cast<const uint4*>(p.host_rows + (size_t)s_plan_e[r] * p.stride);
+    uint4* dst = reinterpret_cast<uint4*>(p.slots + (size_t)s_victim[r] * p.stride);
     copy_chunks(dst, src, n16, gtid, gstride);
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(PlanArgs p) {
+  extern __shared__ __align__(16) char lds[];
+  plan_page_in_block(p, blockIdx.x, gridDim.x, lds);
+}
+
+static PlanArgs plan_args(int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o, int mfma_min,
+                          int32_t* work, unsigned long long* stats, const uint8_t* host_rows, uint8_t* slots,
+                          size_t stride, size_t copy_bytes, bool copy) {
+  PlanArgs p;
+  p.blk = blk; p.ids = ids; p.n = n; p.E = d.E; p.K = d.K; p.MW = d.max_waves; p.o = o; p.mfma_min = mfma_min;
+  p.work = work; p.stats = stats; p.host_rows = host_rows; p.slots = slots; p.stride = stride;
+  p.copy_bytes = copy_bytes; p.do_copy = copy ? 1 : 0;
+  return p;
 }
 
 void launch_plan_page_in(int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
                          int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
                          uint8_t* slots, size_t stride, size_t copy_bytes, bool copy, int grid, hipStream_t s) {
-  plan_page_in_kernel<<<copy ? grid : 1, kPlanThreads, 0, s>>>(blk, ids, n, d.E, d.K, d.max_waves, o, mfma_min,
-                                                               work, stats, host_rows, slots, stride, copy_bytes,
-                                                               copy ? 1 : 0);
+  const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, copy);
+  plan_page_in_kernel<<<copy ? grid : 1, kPlanThreads, plan_lds_bytes(d.E, d.K, n), s>>>(p);
 }
 
 // Copy the planned experts of one host-planned wave (plan already in the layer block).
@@ -522,18 +590,21 @@ __device__ __forceinline__ void part_range(const ExpertArgs& a, int begin, int s
   e = a.part == 1 ? split : end;
 }
 
+// LDS of the lean expert discovery for n routed entries.
+constexpr size_t lean_lds_bytes(int n) { return 3 * al16(4 * (size_t)n) + 16 + al16((size_t)n); }
+
 // The item-th GEMV expert among those already resident, found from the routed
 // ids and the current LRU-state copy without the published plan, so it can run
-// while the planning + page-in kernel is still in flight.  Same numbering as the
-// planner: present experts by ascending id (sorted positions are the prefix of
-// their entry counts), GEMV hits in ascending id.  Block-wide; n = T*k <= K.
-__device__ bool lean_hit_item(const ExpertArgs& a, int item, GemvItem& it) {
-  __shared__ int s_id[kMaxExperts];
-  __shared__ int s_cnt[kMaxExperts];              // entries with this id (first occurrences only)
-  __shared__ unsigned char s_hitg[kMaxExperts];   // first occurrence of a resident GEMV expert
-  __shared__ int s_ent[kMaxExperts];
-  __shared__ int s_sel[4];
+// while the planning + page-in workgroups are still in flight.  Same numbering
+// as the planner: present experts by ascending id (sorted positions are the
+// prefix of their entry counts), GEMV hits in ascending id.  Block-wide; n = T*k.
+__device__ bool lean_hit_item(const ExpertArgs& a, int item, GemvItem& it, char* lds) {
   const int n = a.T * a.k, tid = threadIdx.x;
+  int* s_id = reinterpret_cast<int*>(lds);
+  int* s_cnt = reinterpret_cast<int*>(lds + al16(4 * (size_t)n));      // entries with this id, first occurrences
+  int* s_ent = reinterpret_cast<int*>(lds + 2 * al16(4 * (size_t)n));
+  int* s_sel = reinterpret_cast<int*>(lds + 3 * al16(4 * (size_t)n));
+  unsigned char* s_hitg = reinterpret_cast<unsigned char*>(lds + 3 * al16(4 * (size_t)n) + 16);
   const int32_t* st = a.blk + a.o.state0 + (a.blk[a.o.cur] & 1) * a.o.state_stride;
   if (tid == 0) s_sel[0] = -1;
   for (int i = tid; i < n; i += blockDim.x) {
@@ -582,8 +653,8 @@ __device__ bool lean_hit_item(const ExpertArgs& a, int item, GemvItem& it) {
   return true;
 }
 
-__device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvItem& it) {
-  if (a.lean) return lean_hit_item(a, item, it);
+__device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvItem& it, char* lds) {
+  if (a.lean) return lean_hit_item(a, item, it, lds);
   const int32_t* hdr = a.work + a.o.hdr;
   int g0, g1;
   part_range(a, hdr[hdr_gemv(a.MW, a.wave)], hdr[hdr_gemv_split(a.MW, a.wave)], hdr[hdr_gemv(a.MW, a.wave + 1)], g0, g1);
@@ -596,17 +667,22 @@ __device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvIte
   return true;
 }
 
+// LDS ahead of the staged token vectors: the lean discovery's arrays, if used.
+__device__ __forceinline__ size_t gemv_lds_head(const ExpertArgs& a) {
+  return a.lean ? lean_lds_bytes(a.T * a.k) : 0;
+}
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Gate/up projection + SwiGLU for one used expert (blockIdx.y) and a range of
-// intermediate rows (blockIdx.x): every lane group takes one row i and computes
+// Gate/up projection + SwiGLU of one workgroup: used expert `by`, intermediate
+// rows from bx * rows_per_block; every lane group takes one row i and computes
 // h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).  The weight loads of both rows are
-// issued before the token vectors are staged.
+// issued before the token vectors are staged in LDS.
 template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a, int LG, int rows_per_block) {
-  extern __shared__ __align__(16) uint16_t xs[];   // [MB][H]
+__device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds) {
   GemvItem it;
-  if (!gemv_item(a, blockIdx.y, it)) return;
+  if (!gemv_item(a, by, it, lds)) return;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + gemv_lds_head(a));   // [MB][H]
   constexpr int VPC = Fmt<FMT>::VPC;
   const int H = a.H, I = a.I;
   const int n_ch = H / VPC;
@@ -616,7 +692,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a
   const uint16_t* S13h = reinterpret_cast<const uint16_t*>(blob + a.off_s13);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int i = blockIdx.x * rows_per_block + wv * groups + grp;    // this group's row
+  const int i = bx * rows_per_block + wv * groups + grp;    // this group's row
   const bool active = i < I;
   const int ru = I + i;
   const uint4* rg = W13 + (size_t)i * n_ch;
@@ -654,13 +730,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a
   }
 }
 
-// Down projection for one used expert: every lane group takes two rows n, n+1
-// and writes merged[entry, n] = w[entry] * (W2[n] . h[pos]).
+// Down projection of one workgroup: used expert `by`, rows from bx *
+// rows_per_block; every lane group takes two rows n, n+1 and writes
+// merged[entry, n] = w[entry] * (W2[n] . h[pos]).
 template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, int LG, int rows_per_block) {
-  extern __shared__ __align__(16) uint16_t hs[];   // [MB][I]
+__device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds) {
   GemvItem it;
-  if (!gemv_item(a, blockIdx.y, it)) return;
+  if (!gemv_item(a, by, it, lds)) return;
+  uint16_t* hs = reinterpret_cast<uint16_t*>(lds + gemv_lds_head(a));   // [MB][I]
   constexpr int VPC = Fmt<FMT>::VPC;
   const int H = a.H, I = a.I;
   const int n_ch = I / VPC;
@@ -670,7 +747,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, i
   const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int n0 = blockIdx.x * rows_per_block + 2 * (wv * groups + grp);   // rows n0, n0 + 1
+  const int n0 = bx * rows_per_block + 2 * (wv * groups + grp);   // rows n0, n0 + 1
   const bool act0 = n0 < H, act1 = n0 + 1 < H;
   const uint4* r0 = W2 + (size_t)n0 * n_ch;
   const uint4* r1 = W2 + (size_t)(n0 + 1) * n_ch;
@@ -710,6 +787,53 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, i
   }
 }
 
+// Geometry of one GEMV launch: lanes per row, rows per workgroup, workgroups per
+// expert along the rows.
+struct GemvGeom {
+  int LG, rows_per_block, gx;
+};
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void gemv_gate_up_kernel(ExpertArgs a, GemvGeom g) {
+  extern __shared__ __align__(16) char lds[];
+  gate_up_block<FMT, MB>(a, blockIdx.x, blockIdx.y, g.LG, g.rows_per_block, lds);
+}
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, GemvGeom g) {
+  extern __shared__ __align__(16) char lds[];
+  down_block<FMT, MB>(a, blockIdx.x, blockIdx.y, g.LG, g.rows_per_block, lds);
+}
+
+// Device-planned step, launch A: workgroups [0, P) plan the wave and page in its
+// missing experts; the rest run the gate/up projection of the experts that
+// were already resident (lean discovery).  Launch B: workgroups [0, gate.gx *
+// items) run the gate/up projection of the paged-in experts (published lists),
+// the rest the down projection of the resident ones.  One queue, no waiting
+// between workgroups: each role depends only on earlier launches.
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs hit, GemvGeom g) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x < P) {
+    plan_page_in_block(p, blockIdx.x, P, lds);
+  } else {
+    const int b = blockIdx.x - P;
+    gate_up_block<FMT, MB>(hit, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
+  }
+}
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void step_b_kernel(ExpertArgs miss, GemvGeom gu, int n_gu, ExpertArgs hit,
+                                                              GemvGeom dn) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x < n_gu) {
+    gate_up_block<FMT, MB>(miss, blockIdx.x % gu.gx, blockIdx.x / gu.gx, gu.LG, gu.rows_per_block, lds);
+  } else {
+    const int b = blockIdx.x - n_gu;
+    down_block<FMT, MB>(hit, b % dn.gx, b / dn.gx, dn.LG, dn.rows_per_block, lds);
+  }
+}
+
 // Lanes per row: the smallest power of two (8..64) that keeps a row at most
 // kMaxChunksInFlight chunks per lane, so a lane group issues a whole row in one
 // round of loads and short rows give a wave several rows at once.
@@ -726,50 +850,90 @@ static int pick_mb(int max_m) {
   return 8;
 }
 
-template <int FMT>
-static void gate_up_fmt(const ExpertArgs& a, int items, int mb, hipStream_t s) {
-  const int n_ch = a.H / Fmt<FMT>::VPC;
-  const int LG = lanes_per_row(n_ch);
-  const int rows_per_block = (kGemvThreads / 64) * (64 / LG);
-  dim3 grid((a.I + rows_per_block - 1) / rows_per_block, items);
-  size_t lds = (size_t)mb * a.H * 2;
-  switch (mb) {
-    case 1: gemv_gate_up_kernel<FMT, 1><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-    case 2: gemv_gate_up_kernel<FMT, 2><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-    case 4: gemv_gate_up_kernel<FMT, 4><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-    default: gemv_gate_up_kernel<FMT, 8><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-  }
+static int vpc_of(int wtype) {
+  return wtype == PE_W_BF16 ? Fmt<PE_W_BF16>::VPC : wtype == PE_W_FP8_B128 ? Fmt<PE_W_FP8_B128>::VPC
+                                                                          : Fmt<PE_W_INT4_G128>::VPC;
 }
 
-template <int FMT>
-static void down_fmt(const ExpertArgs& a, int items, int mb, hipStream_t s) {
-  const int n_ch = a.I / Fmt<FMT>::VPC;
-  const int LG = lanes_per_row(n_ch);
-  const int rows_per_block = (kGemvThreads / 64) * (64 / LG) * 2;
-  dim3 grid((a.H + rows_per_block - 1) / rows_per_block, items);
-  size_t lds = (size_t)mb * a.I * 2;
-  switch (mb) {
-    case 1: gemv_down_kernel<FMT, 1><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-    case 2: gemv_down_kernel<FMT, 2><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-    case 4: gemv_down_kernel<FMT, 4><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-    default: gemv_down_kernel<FMT, 8><<<grid, kGemvThreads, lds, s>>>(a, LG, rows_per_block); break;
-  }
+static GemvGeom gate_up_geom(int wtype, const ExpertArgs& a) {
+  GemvGeom g;
+  g.LG = lanes_per_row(a.H / vpc_of(wtype));
+  g.rows_per_block = (kGemvThreads / 64) * (64 / g.LG);
+  g.gx = (a.I + g.rows_per_block - 1) / g.rows_per_block;
+  return g;
 }
+
+static GemvGeom down_geom(int wtype, const ExpertArgs& a) {
+  GemvGeom g;
+  g.LG = lanes_per_row(a.I / vpc_of(wtype));
+  g.rows_per_block = (kGemvThreads / 64) * (64 / g.LG) * 2;
+  g.gx = (a.H + g.rows_per_block - 1) / g.rows_per_block;
+  return g;
+}
+
+static size_t lean_head(const ExpertArgs& a) { return a.lean ? lean_lds_bytes(a.T * a.k) : 0; }
+
+// Instantiate a kernel template over the weight format and token batch.
+#define PE_DISPATCH(wtype, mb, CALL)                                              \
+  do {                                                                            \
+    if ((wtype) == PE_W_BF16) {                                                   \
+      constexpr int F_ = PE_W_BF16;                                               \
+      if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
+      else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
+      else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
+      else { constexpr int M_ = 8; CALL; }                                        \
+    } else if ((wtype) == PE_W_FP8_B128) {                                        \
+      constexpr int F_ = PE_W_FP8_B128;                                           \
+      if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
+      else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
+      else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
+      else { constexpr int M_ = 8; CALL; }                                        \
+    } else {                                                                      \
+      constexpr int F_ = PE_W_INT4_G128;                                          \
+      if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
+      else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
+      else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
+      else { constexpr int M_ = 8; CALL; }                                        \
+    }                                                                             \
+  } while (0)
 
 void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s) {
   if (items <= 0) return;
   const int mb = pick_mb(max_m);
-  if (wtype == PE_W_BF16) gate_up_fmt<PE_W_BF16>(a, items, mb, s);
-  else if (wtype == PE_W_FP8_B128) gate_up_fmt<PE_W_FP8_B128>(a, items, mb, s);
-  else gate_up_fmt<PE_W_INT4_G128>(a, items, mb, s);
+  const GemvGeom g = gate_up_geom(wtype, a);
+  const size_t lds = lean_head(a) + (size_t)mb * a.H * 2;
+  const dim3 grid(g.gx, items);
+  PE_DISPATCH(wtype, mb, (gemv_gate_up_kernel<F_, M_><<<grid, kGemvThreads, lds, s>>>(a, g)));
 }
 
 void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s) {
   if (items <= 0) return;
   const int mb = pick_mb(max_m);
-  if (wtype == PE_W_BF16) down_fmt<PE_W_BF16>(a, items, mb, s);
-  else if (wtype == PE_W_FP8_B128) down_fmt<PE_W_FP8_B128>(a, items, mb, s);
-  else down_fmt<PE_W_INT4_G128>(a, items, mb, s);
+  const GemvGeom g = down_geom(wtype, a);
+  const size_t lds = lean_head(a) + (size_t)mb * a.I * 2;
+  const dim3 grid(g.gx, items);
+  PE_DISPATCH(wtype, mb, (gemv_down_kernel<F_, M_><<<grid, kGemvThreads, lds, s>>>(a, g)));
+}
+
+void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
+                   int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
+                   uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& hit, int items,
+                   int max_m, hipStream_t s) {
+  const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, true);
+  const int mb = pick_mb(max_m);
+  const GemvGeom g = gate_up_geom(wtype, hit);
+  const size_t lds = std::max(plan_lds_bytes(d.E, d.K, n), lean_head(hit) + (size_t)mb * hit.H * 2);
+  const int blocks = P + g.gx * items;
+  PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, hit, g)));
+}
+
+void launch_step_b(int wtype, const ExpertArgs& miss, const ExpertArgs& hit, int items, int max_m, hipStream_t s) {
+  const int mb = pick_mb(max_m);
+  const GemvGeom gu = gate_up_geom(wtype, miss), dn = down_geom(wtype, hit);
+  const int n_gu = gu.gx * items;
+  const size_t lds = std::max((size_t)mb * miss.H * 2, lean_head(hit) + (size_t)mb * hit.I * 2);
+  const int blocks = n_gu + dn.gx * items;
+  PE_DISPATCH(wtype, mb, (step_b_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(miss, gu, n_gu, hit, dn)));
 }
 
 // ------------------------------------------------------------------ MFMA grouped GEMM
