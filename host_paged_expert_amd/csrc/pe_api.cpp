@@ -470,7 +470,9 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
     // projection of the experts already resident, which find their expert from the
     // ids and the current copy.  Launch B: gate/up of the paged-in experts
     // alongside down of the resident ones.  Launch C: down of the paged-in
-    // experts.  Then the top-k sum, which makes the new state copy current.
+    // experts and the fixed-order top-k sum by output-row ranges, which also
+    // makes the new state copy current (a separate top-k launch when its LDS
+    // would not fit).
     // No host synchronisation: capturable.
     const int items = std::min(n, d.K);
     // an expert may hold T >= mfma_min entries: then launch the MFMA kernels over
@@ -483,7 +485,11 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       hit.T = T;
       hit.E = d.E;
       hit.blk = blk;
-      const pe::ExpertArgs miss = expert_args(c, layer, 0, x, topk_w, 2);
+      pe::ExpertArgs miss = expert_args(c, layer, 0, x, topk_w, 2);
+      miss.ids = topk_ids;
+      miss.T = T;
+      miss.E = d.E;
+      miss.blk = blk;
       {
         StageTimer tm(c, PE_STAGE_PAGE_IN, s);
         pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l,
@@ -493,8 +499,16 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
         StageTimer tm(c, PE_STAGE_GATE_UP, s);
         pe::launch_step_b(c->cfg.wtype, miss, hit, items, T, s);
       }
-      StageTimer tm(c, PE_STAGE_DOWN, s);
-      pe::launch_gemv_down(c->cfg.wtype, miss, items, T, s);
+      bool fused;
+      {
+        StageTimer tm(c, PE_STAGE_DOWN, s);
+        fused = pe::launch_down_topk(c->cfg.wtype, miss, T, static_cast<uint16_t*>(out), blk + c->ll.cur, s);
+        if (!fused) pe::launch_gemv_down(c->cfg.wtype, miss, items, T, s);
+      }
+      if (fused) {
+        PE_HIP(hipGetLastError());
+        return PE_OK;
+      }
     } else {
       {
         StageTimer tm(c, PE_STAGE_PAGE_IN, s);

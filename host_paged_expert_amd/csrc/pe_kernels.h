@@ -78,6 +78,11 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
                    uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& hit, int items,
                    int max_m, hipStream_t s);
 void launch_step_b(int wtype, const ExpertArgs& miss, const ExpertArgs& hit, int items, int max_m, hipStream_t s);
+// Last launch of a device-planned step: down projection of the paged-in experts
+// (`miss`, which must carry ids, T and E) and the fixed-order top-k sum into
+// `out`, by output-row ranges; flips `flip`.  Returns false (nothing launched)
+// if its LDS would exceed 48 KiB; use launch_gemv_down + launch_topk_sum then.
+bool launch_down_topk(int wtype, const ExpertArgs& miss, int max_m, uint16_t* out, int32_t* flip, hipStream_t s);
 
 // MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
 // tokens).  Need H and I multiples of 128.

@@ -76,13 +76,17 @@ __device__ __forceinline__ void topk_sum_rows(const float* __restrict__ merged, 
   }
 }
 
-// Inclusive scan across the 64 lanes of a wavefront.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int n = __shfl_up(v, off, 64);
-    if (lane >= off) v += n;
-  }
+// Inclusive scan across the 64 lanes of a wavefront with DPP lane moves (no LDS
+// round trips): Kogge-Stone within each row of 16 lanes (row_shr 1, 2, 4, 8; a
+// lane with no source adds 0), then row 0's total into row 1 and row 2's into
+// row 3 (row_bcast:15), then rows 0-1's total into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -169,11 +173,11 @@ struct PlanArgs {
 };
 
 // One device-planned wave (all routed experts of a step with T*k <= K), in LDS.
-// Each of the `nblocks` planning workgroups computes the same plan from state
-// copy `cur`; workgroup 0 publishes it (plan, new state in the other copy, slot
-// map, work lists, counters); then every workgroup copies its share of the
-// missing experts.
-__device__ void plan_page_in_block(const PlanArgs& p, int block, int nblocks, char* lds) {
+// Each of the ncopy + 1 planning workgroups computes the same plan from state
+// copy `cur`; workgroup `ncopy` publishes it (plan, new state in the other copy,
+// slot map, work lists, counters) while workgroups [0, ncopy) copy their share
+// of the missing experts.
+__device__ void plan_page_in_block(const PlanArgs& p, int block, int ncopy, char* lds) {
   const int E = p.E, K = p.K, n = p.n, MW = p.MW;
   const Offsets& o = p.o;
   int32_t* __restrict__ blk = p.blk;
@@ -196,21 +200,44 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int nblocks, ch
   auto s_wtot = [&](int v, int w) -> int& { return L.wtot[v * kPlanWaves + w]; };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool publish = block == 0;
-  const int cur = blk[o.cur] & 1;
-  const int32_t* st = blk + o.state0 + cur * o.state_stride;           // read: current copy
-  int32_t* nst = blk + o.state0 + (cur ^ 1) * o.state_stride;           // written by workgroup 0
-  const unsigned tick = (unsigned)st[o.tick];
+  // Copier workgroups (block < ncopy) start copying as soon as they hold the plan;
+  // the one workgroup past them (block == ncopy) publishes it instead.
+  const bool publish = block == ncopy;
+  // One round of global loads: the current-copy index, the routed ids (n <= K <=
+  // kMaxExperts = 4 per thread) and both state copies; the current copy is picked
+  // once everything has arrived.
+  const int32_t* st0 = blk + o.state0;
+  const int32_t* st1 = blk + o.state0 + o.state_stride;
+  const int cur_word = blk[o.cur];
+  const unsigned tick0 = (unsigned)st0[o.tick], tick1 = (unsigned)st1[o.tick];
+  int idv[kMaxExperts / kPlanThreads];
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / kPlanThreads; ++q) {
+    const int i = tid + q * kPlanThreads;
+    idv[q] = i < n ? ids[i] : -1;
+  }
+  const int cur = cur_word & 1;
+  int32_t* nst = blk + o.state0 + (cur ^ 1) * o.state_stride;           // written by the publisher
+  const unsigned tick = cur ? tick1 : tick0;
   if (tid == 0) s_bad = 0;
-  for (int e = tid; e < E; e += kPlanThreads) { s_es[e] = st[o.expert_slot + e]; s_cnt[e] = 0; }
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int a0 = st0[o.expert_slot + e], a1 = st1[o.expert_slot + e];
+    s_es[e] = cur ? a1 : a0;
+    s_cnt[e] = 0;
+  }
   for (int j = tid; j < K; j += kPlanThreads) {
-    s_se[j] = st[o.slot_expert + j];
-    s_lu[j] = (unsigned)st[o.last_use + j];
+    const int a0 = st0[o.slot_expert + j], a1 = st1[o.slot_expert + j];
+    const int b0 = st0[o.last_use + j], b1 = st1[o.last_use + j];
+    s_se[j] = cur ? a1 : a0;
+    s_lu[j] = (unsigned)(cur ? b1 : b0);
   }
   __syncthreads();
-  for (int i = tid; i < n; i += kPlanThreads) {
-    int id = ids[i];
-    bool ok = id >= 0 && id < E;
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / kPlanThreads; ++q) {
+    const int i = tid + q * kPlanThreads;
+    if (i >= n) break;
+    const int id = idv[q];
+    const bool ok = id >= 0 && id < E;
     s_ids[i] = ok ? id : -1;
     if (ok) atomicAdd(&s_cnt[id], 1); else atomicAdd(&s_bad, 1);
   }
@@ -281,10 +308,13 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int nblocks, ch
   // Victims by ascending (last_use, slot): rank = candidates ordered before j.
   for (int j = tid; j < K; j += kPlanThreads) {
     if (!s_cand[j]) continue;
-    unsigned lj = s_lu[j];
+    const unsigned lj = s_lu[j];
     int r = 0;
-    for (int q = 0; q < K; ++q)
-      r += s_cand[q] && (s_lu[q] < lj || (s_lu[q] == lj && q < j));
+#pragma unroll 8
+    for (int q = 0; q < K; ++q) {     // branch-free, so the LDS reads pipeline
+      const unsigned lq = s_lu[q];
+      r += (int)s_cand[q] & ((int)(lq < lj) | ((int)(lq == lj) & (int)(q < j)));
+    }
     if (r < n_miss) s_victim[r] = j;
   }
   __syncthreads();
@@ -369,12 +399,12 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int nblocks, ch
       if (s_bad) atomicAdd(stats + ST_BAD_IDS, (unsigned long long)s_bad);
     }
   }
-  if (!p.do_copy) return;
-  // Page-in: the r-th missing expert's blob into its victim slot, every workgroup
-  // taking its share of the 16-byte chunks.
+  if (publish || !p.do_copy) return;
+  // Page-in: the r-th missing expert's blob into its victim slot, every copier
+  // workgroup taking its share of the 16-byte chunks.
   const size_t n16 = p.copy_bytes / 16;
   const size_t gtid = (size_t)block * blockDim.x + threadIdx.x;
-  const size_t gstride = (size_t)nblocks * blockDim.x;
+  const size_t gstride = (size_t)ncopy * blockDim.x;
   for (int r = 0; r < n_miss; ++r) {
     const uint4* src = reinterpret_cast<const uint4*>(p.host_rows + (size_t)s_plan_e[r] * p.stride);
     uint4* dst = reinterpret_cast<uint4*>(p.slots + (size_t)s_victim[r] * p.stride);
@@ -382,9 +412,9 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int nblocks, ch
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(PlanArgs p) {
+__global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(PlanArgs p, int ncopy) {
   extern __shared__ __align__(16) char lds[];
-  plan_page_in_block(p, blockIdx.x, gridDim.x, lds);
+  plan_page_in_block(p, blockIdx.x, ncopy, lds);
 }
 
 static PlanArgs plan_args(int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o, int mfma_min,
@@ -401,7 +431,8 @@ void launch_plan_page_in(int32_t* blk, const int32_t* ids, int n, const Dims& d,
                          int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
                          uint8_t* slots, size_t stride, size_t copy_bytes, bool copy, int grid, hipStream_t s) {
   const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, copy);
-  plan_page_in_kernel<<<copy ? grid : 1, kPlanThreads, plan_lds_bytes(d.E, d.K, n), s>>>(p);
+  const int ncopy = copy ? grid : 0;
+  plan_page_in_kernel<<<ncopy + 1, kPlanThreads, plan_lds_bytes(d.E, d.K, n), s>>>(p, ncopy);
 }
 
 // Copy the planned experts of one host-planned wave (plan already in the layer block).
@@ -733,10 +764,16 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
 // Down projection of one workgroup: used expert `by`, rows from bx *
 // rows_per_block; every lane group takes two rows n, n+1 and writes
 // merged[entry, n] = w[entry] * (W2[n] . h[pos]).
+// With y_lds set, the workgroup also keeps its results in LDS, y_lds[entry *
+// rows_per_block + row - bx * rows_per_block], and marks the entries in
+// mark[entry] (for the fused down + top-k launch).
 template <int FMT, int MB>
-__device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds) {
+__device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds,
+                           float* y_lds = nullptr, unsigned char* mark = nullptr) {
   GemvItem it;
   if (!gemv_item(a, by, it, lds)) return;
+  if (mark)
+    for (int t = threadIdx.x; t < it.m; t += blockDim.x) mark[it.ent[t]] = 1;
   uint16_t* hs = reinterpret_cast<uint16_t*>(lds + gemv_lds_head(a));   // [MB][I]
   constexpr int VPC = Fmt<FMT>::VPC;
   const int H = a.H, I = a.I;
@@ -780,8 +817,14 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
     for (int t = 0; t < MB; ++t) {
       if (t < mb && lig == t) {
         const int e = ent[tb + t];
-        a.merged[(size_t)e * H + n0] = a.topk_w[e] * y0[t];
-        if (act1) a.merged[(size_t)e * H + n0 + 1] = a.topk_w[e] * y1[t];
+        const float v0 = a.topk_w[e] * y0[t];
+        a.merged[(size_t)e * H + n0] = v0;
+        if (y_lds) y_lds[(size_t)e * rows_per_block + (n0 - bx * rows_per_block)] = v0;
+        if (act1) {
+          const float v1 = a.topk_w[e] * y1[t];
+          a.merged[(size_t)e * H + n0 + 1] = v1;
+          if (y_lds) y_lds[(size_t)e * rows_per_block + (n0 + 1 - bx * rows_per_block)] = v1;
+        }
       }
     }
   }
@@ -805,8 +848,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, G
   down_block<FMT, MB>(a, blockIdx.x, blockIdx.y, g.LG, g.rows_per_block, lds);
 }
 
-// Device-planned step, launch A: workgroups [0, P) plan the wave and page in its
-// missing experts; the rest run the gate/up projection of the experts that
+// Device-planned step, launch A: workgroups [0, P] plan the wave (P publishes it,
+// [0, P) page in its missing experts); the rest run the gate/up projection of the experts that
 // were already resident (lean discovery).  Launch B: workgroups [0, gate.gx *
 // items) run the gate/up projection of the paged-in experts (published lists),
 // the rest the down projection of the resident ones.  One queue, no waiting
@@ -814,10 +857,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, G
 template <int FMT, int MB>
 __global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs hit, GemvGeom g) {
   extern __shared__ __align__(16) char lds[];
-  if ((int)blockIdx.x < P) {
+  if ((int)blockIdx.x <= P) {
     plan_page_in_block(p, blockIdx.x, P, lds);
   } else {
-    const int b = blockIdx.x - P;
+    const int b = blockIdx.x - P - 1;
     gate_up_block<FMT, MB>(hit, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
   }
 }
@@ -832,6 +875,46 @@ __global__ __launch_bounds__(kGemvThreads) void step_b_kernel(ExpertArgs miss, G
     const int b = blockIdx.x - n_gu;
     down_block<FMT, MB>(hit, b % dn.gx, b / dn.gx, dn.LG, dn.rows_per_block, lds);
   }
+}
+
+// Device-planned step, last launch: the down projection of the paged-in experts
+// and the fixed-order top-k sum, partitioned by output rows so no workgroup
+// needs another's results.  Workgroup bx owns rows [bx*R, bx*R + R): it computes
+// those rows for every paged-in expert (keeping them in LDS as well as in the
+// merged buffer), then for each token sums all k entries of its rows in j order
+// (resident experts' entries from the merged buffer, written by the previous
+// launch), rounds once to bf16, and workgroup 0 makes the new LRU-state copy
+// current.
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void down_topk_kernel(ExpertArgs miss, GemvGeom g, uint16_t* out,
+                                                                 int32_t* flip) {
+  extern __shared__ __align__(16) char lds[];
+  const int T = miss.T, k = miss.k, n = T * k, R = g.rows_per_block, H = miss.H;
+  float* s_y = reinterpret_cast<float*>(lds);                                        // [n][R]
+  unsigned char* s_miss = reinterpret_cast<unsigned char*>(lds + al16(4 * (size_t)n * R));
+  char* rest = lds + al16(4 * (size_t)n * R) + al16((size_t)n);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s_miss[i] = 0;
+  __syncthreads();
+  const int32_t* hdr = miss.work + miss.o.hdr;
+  const int items = hdr[hdr_gemv(miss.MW, 1)] - hdr[hdr_gemv_split(miss.MW, 0)];
+  for (int item = 0; item < items; ++item) {
+    down_block<FMT, MB>(miss, blockIdx.x, item, g.LG, R, rest, s_y, s_miss);
+    __syncthreads();
+  }
+  const int r0 = blockIdx.x * R;
+  for (int idx = threadIdx.x; idx < T * R; idx += blockDim.x) {
+    const int t = idx / R, r = idx - t * R, row = r0 + r;
+    if (row >= H) continue;
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int e = t * k + j;
+      const int id = miss.ids[e];
+      if (id < 0 || id >= miss.E) continue;
+      acc += s_miss[e] ? s_y[(size_t)e * R + r] : miss.merged[(size_t)e * H + row];
+    }
+    out[(size_t)t * H + row] = f32_to_bf16(acc);
+  }
+  if (flip && blockIdx.x == 0 && threadIdx.x == 0) *flip ^= 1;
 }
 
 // Lanes per row: the smallest power of two (8..64) that keeps a row at most
@@ -923,8 +1006,18 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, hit);
   const size_t lds = std::max(plan_lds_bytes(d.E, d.K, n), lean_head(hit) + (size_t)mb * hit.H * 2);
-  const int blocks = P + g.gx * items;
+  const int blocks = P + 1 + g.gx * items;
   PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, hit, g)));
+}
+
+bool launch_down_topk(int wtype, const ExpertArgs& miss, int max_m, uint16_t* out, int32_t* flip, hipStream_t s) {
+  const int mb = pick_mb(max_m);
+  const GemvGeom g = down_geom(wtype, miss);
+  const int n = miss.T * miss.k;
+  const size_t lds = al16(4 * (size_t)n * g.rows_per_block) + al16((size_t)n) + (size_t)mb * miss.I * 2;
+  if (lds > 48 * 1024) return false;
+  PE_DISPATCH(wtype, mb, (down_topk_kernel<F_, M_><<<g.gx, kGemvThreads, lds, s>>>(miss, g, out, flip)));
+  return true;
 }
 
 void launch_step_b(int wtype, const ExpertArgs& miss, const ExpertArgs& hit, int items, int max_m, hipStream_t s) {
