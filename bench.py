@@ -128,38 +128,17 @@ def main():
         for l in range(L):
             m.forward(l, xp, idsp[l], wp[l], outp[l], stream=stream)
 
-    graph = None
-    sidx = torch.zeros(1, dtype=torch.long, device=dev)
+    runner = harness.DecodeRunner(m, wl, x_all, ids_all, w_all, out, stream, capture=captured)
     if captured:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                xs = torch.index_select(x_all, 0, sidx)[0]
-                ids_s = torch.index_select(ids_all, 0, sidx)[0]
-                w_s = torch.index_select(w_all, 0, sidx)[0]
-                cs = torch.cuda.current_stream()
-                for l in range(L):
-                    m.forward(l, xs, ids_s[l], w_s[l], out[l], stream=cs)
-                sidx.add_(1)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
         log("captured one %d-layer decode step as a hipGraph" % L)
 
     def run(n):
-        if captured:
-            for _ in range(n):
-                graph.replay()
-        else:
-            for s in range(n):
-                for l in range(L):
-                    m.forward(l, x_all[s], ids_all[s, l], w_all[s, l], out[l], stream=stream)
+        runner.run(n)
 
     def cold():
         torch.cuda.synchronize()
         m.reset_lru(-1, stream)
-        sidx.zero_()
+        runner.rewind()
         torch.cuda.synchronize()
         m.reset_stats()
 
@@ -219,7 +198,7 @@ def main():
     sample_steps = []
     samples = {}
     if not args.no_cpu_baseline:
-        n_samp = args.cpu_samples or 4
+        n_samp = args.cpu_samples or 16
         sample_steps = sorted(set(int(round(v)) for v in np.linspace(0, steps - 1, n_samp)))
     prefill_kernel = None
     if not args.no_timing_pass:
@@ -352,26 +331,32 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
     plan_ok = (misses == M and distinct == D)
     log("oracle LRU simulator: %d layer-steps in %.2fs, plans %s" % (L * steps, t_sim,
                                                                      "match" if plan_ok else "DIFFER"))
-    # (step, layer) pairs: layers interleaved across the sample steps so a cut-off
-    # sample still spans the window
-    pairs = [(s, l) for l in range(L) for s in sample_steps]
+    # (step, layer) pairs, layer by layer so a cut-off sample still spans the
+    # window's steps; a layer's expert tensors are generated once, untimed (they
+    # are inputs), in parallel threads
+    from concurrent.futures import ThreadPoolExecutor
     t_moe, worst, done = 0.0, 0.0, []
     wall0 = time.perf_counter()
     xs = {s: formats.bf16_to_f32(synth.hidden_states(wl, s, B)) for s in sample_steps}
-    for s, l in pairs:
+    pool = ThreadPoolExecutor(harness.host_threads())
+    for l in range(L):
         if t_moe >= budget_s or time.perf_counter() - wall0 >= 4 * budget_s:
             break
-        ids, w = routing["decode_ids"][s, l], routing["decode_w"][s, l]
-        canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(ids)}
-        t1 = time.perf_counter()
-        ref = moe.moe_layer(xs[s], ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
-        t_moe += time.perf_counter() - t1
-        done.append((s, l))
-        if s in samples:
-            got = harness.bf16_to_f32(samples[s][l])
-            worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
-        if len(done) % 8 == 0:
-            log("oracle: %d (step, layer) pairs, %.1fs of oracle time" % (len(done), t_moe))
+        used = sorted({int(e) for s in sample_steps for e in np.unique(routing["decode_ids"][s, l])})
+        canon = dict(zip(used, pool.map(lambda e: synth.expert_tensors(wl, l, e), used)))
+        for s in sample_steps:
+            if t_moe >= budget_s:
+                break
+            ids, w = routing["decode_ids"][s, l], routing["decode_w"][s, l]
+            t1 = time.perf_counter()
+            ref = moe.moe_layer(xs[s], ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+            t_moe += time.perf_counter() - t1
+            done.append((s, l))
+            if s in samples:
+                got = harness.bf16_to_f32(samples[s][l])
+                worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+        log("oracle: %d (step, layer) pairs, %.1fs of oracle time" % (len(done), t_moe))
+    pool.shutdown()
     pre_worst = None
     if has_prefill and "prefill" in samples:
         xp = formats.bf16_to_f32(synth.hidden_states(wl, -1, wl.prefill_tokens))

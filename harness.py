@@ -31,7 +31,9 @@ def make_moe(wl, flags=0, max_tokens=None, device=0):
 
 
 def load_store(moe, wl, threads=None, layers=None, experts=None, progress=None):
-    """Generate every expert of the workload and write it with pe_load_expert."""
+    """Generate every expert of the workload and write it with pe_load_expert
+    into `moe`, or into each context of a list (one generation per expert)."""
+    moes = list(moe) if isinstance(moe, (list, tuple)) else [moe]
     layers = range(wl.layers) if layers is None else layers
     experts = range(wl.experts) if experts is None else experts
     jobs = [(l, e) for l in layers for e in experts]
@@ -41,7 +43,8 @@ def load_store(moe, wl, threads=None, layers=None, experts=None, progress=None):
     def one(job):
         l, e = job
         t13, t2, s13, s2 = synth.expert_tensors(wl, l, e)
-        moe.load_expert(l, e, t13, t2, s13, s2)
+        for m in moes:
+            m.load_expert(l, e, t13, t2, s13, s2)
         if progress is not None:
             with lock:
                 done[0] += 1
@@ -63,6 +66,59 @@ def decode_inputs(wl, routing, device, steps=None):
     ids = torch.from_numpy(np.ascontiguousarray(routing["decode_ids"][:steps])).to(device)
     w = torch.from_numpy(np.ascontiguousarray(routing["decode_w"][:steps])).to(device)
     return xt, ids, w
+
+
+class DecodeRunner:
+    """Decode steps of a workload, launched the way bench.py times them.
+
+    When every step fits one device-planned wave (batch x top_k <= K) and
+    `capture` is set, one step through every layer is captured once as a
+    hipGraph and replayed; the graph picks its step's inputs from x_all /
+    ids_all / w_all on the device with a step counter that it advances itself.
+    Otherwise pe_forward runs eagerly per layer.  The latest step's output is
+    in `out` [L, B, H].  `rewind()` makes the next step step 0 again.
+    """
+
+    def __init__(self, moe, wl, x_all, ids_all, w_all, out, stream, capture=True):
+        import torch
+        self.moe, self.wl, self.out, self.stream = moe, wl, out, stream
+        self.x_all, self.ids_all, self.w_all = x_all, ids_all, w_all
+        self.captured = bool(capture) and wl.batch * wl.top_k <= moe.K
+        self.s = 0
+        self.sidx = torch.zeros(1, dtype=torch.long, device=out.device)
+        self.graph = None
+        if self.captured:
+            side = torch.cuda.Stream(device=out.device)
+            side.wait_stream(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    xs = torch.index_select(x_all, 0, self.sidx)[0]
+                    ids_s = torch.index_select(ids_all, 0, self.sidx)[0]
+                    w_s = torch.index_select(w_all, 0, self.sidx)[0]
+                    cs = torch.cuda.current_stream()
+                    for l in range(wl.layers):
+                        moe.forward(l, xs, ids_s[l], w_s[l], out[l], stream=cs)
+                    self.sidx.add_(1)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            self.graph = g
+
+    def run(self, n):
+        if self.captured:
+            for _ in range(n):
+                self.graph.replay()
+        else:
+            for i in range(n):
+                s = self.s + i
+                for l in range(self.wl.layers):
+                    self.moe.forward(l, self.x_all[s], self.ids_all[s, l], self.w_all[s, l], self.out[l],
+                                     stream=self.stream)
+        self.s += n
+
+    def rewind(self):
+        self.sidx.zero_()
+        self.s = 0
 
 
 def bf16_bits(t) -> np.ndarray:
