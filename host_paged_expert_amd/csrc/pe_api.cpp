@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -81,6 +82,10 @@ bool blob_layout(int wtype, int H, int I, BlobLayout* b) {
 // loads in flight per thread (about 169 us, 56 GB/s, back to back), and a small grid
 // leaves most CUs to the expert kernels that overlap it.
 constexpr int kPageInGrid = 128;
+// Copier workgroups of a device-planned step, which page in the missing experts
+// and compute their gate/up projection on the way (96 divides the gate/up row
+// blocks of every format at hidden 2048 / inter 768: 192, 96 and 48).
+constexpr int kStreamWgs = 96;
 
 }  // namespace
 
@@ -92,7 +97,8 @@ struct pe_ctx {
   pe::Offsets o{};
   BlobLayout b{};
   bool unpaged = false;
-  int mfma_min = 1 << 30;             // = d.mfma_min
+  int mfma_min = pe::kNoMfma;         // = d.mfma_min
+  int stream_wgs = kStreamWgs;        // copier workgroups of a device-planned step
   uint8_t* host_store = nullptr;       // page-locked, mapped: [L][E][stride]
   uint8_t* host_store_dev = nullptr;   // its device-visible address
   uint8_t* slots = nullptr;            // device: [L][K][stride]
@@ -325,7 +331,8 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   c->o = pe::make_offsets(c->ll, c->wl);
   blob_layout(g.wtype, g.hidden, g.inter, &c->b);
   // The MFMA kernels stage K in blocks of 128 and tile weight rows by 64.
-  c->mfma_min = (g.hidden % 128 == 0 && g.inter % 128 == 0) ? pe::kMfmaMinTokens : (1 << 30);
+  c->mfma_min = (g.hidden % 128 == 0 && g.inter % 128 == 0) ? pe::kMfmaMinTokens : pe::kNoMfma;
+  if (const char* v = getenv("PE_STREAM_WGS")) c->stream_wgs = std::max(1, atoi(v));
   c->d.mfma_min = c->mfma_min;
   c->sum = new pe::HostPlanSummary;
   int rc = use_device(c);
@@ -461,62 +468,58 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   const uint8_t* host_l = c->unpaged ? nullptr : c->host_store_dev + (size_t)layer * d.E * c->b.stride;
   const bool device_plan = n <= d.K && !(c->cfg.flags & PE_FLAG_FORCE_HOST_PLAN);
 
+  // An expert's entries take the MFMA kernels iff the step has at least
+  // mfma_min tokens and the expert at least mfma_min entries: the choice depends
+  // only on the step's size and the expert's entry count, never on K or the wave
+  // split, so paged and unpaged runs share every expert's arithmetic.
+  const int mfma_min = T >= c->mfma_min ? c->mfma_min : pe::kNoMfma;
+
   if (device_plan) {
     // One wave, on the caller's stream only (a second stream would put graph
     // branches on other hardware queues, whose cross-queue dependencies cost more
-    // than they hide).  Launch A: planning + page-in workgroups (each makes the
-    // same LRU decision in LDS from the current state copy; workgroup 0 publishes
-    // it and writes the new state into the other copy) alongside the gate/up
-    // projection of the experts already resident, which find their expert from the
-    // ids and the current copy.  Launch B: gate/up of the paged-in experts
-    // alongside down of the resident ones.  Launch C: down of the paged-in
-    // experts and the fixed-order top-k sum by output-row ranges, which also
-    // makes the new state copy current (a separate top-k launch when its LDS
-    // would not fit).
-    // No host synchronisation: capturable.
+    // than they hide).  No host synchronisation: capturable.
     const int items = std::min(n, d.K);
-    // an expert may hold T >= mfma_min entries: then launch the MFMA kernels over
-    // the most tiles one wave can have; surplus blocks exit on the device count
-    const int tiles = T >= c->mfma_min ? pe::ceil_div(n, pe::kTileM) + items : 0;
-    if (!c->unpaged && tiles == 0) {
-      pe::ExpertArgs hit = expert_args(c, layer, 0, x, topk_w, 1);
-      hit.lean = 1;
-      hit.ids = topk_ids;
-      hit.T = T;
-      hit.E = d.E;
-      hit.blk = blk;
-      pe::ExpertArgs miss = expert_args(c, layer, 0, x, topk_w, 2);
-      miss.ids = topk_ids;
-      miss.T = T;
-      miss.E = d.E;
-      miss.blk = blk;
+    if (!c->unpaged && mfma_min == pe::kNoMfma) {
+      // Launch A: planning + page-in workgroups (each makes the same LRU decision
+      // in LDS from the current state copy; one publishes it and writes the new
+      // state into the other copy) that compute the missing experts' gate/up
+      // projection from the rows as they stream in, alongside the gate/up
+      // projection of the experts already resident.  Launch B: every expert's
+      // down projection and the fixed-order top-k sum, which also makes the new
+      // state copy current.
+      pe::ExpertArgs a = expert_args(c, layer, 0, x, topk_w, 1);
+      a.lean = 1;
+      a.ids = topk_ids;
+      a.T = T;
+      a.E = d.E;
+      a.blk = blk;
+      a.mfma_min = mfma_min;
       {
         StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-        pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l,
-                          slots_l, c->b.stride, c->b.copied, kPageInGrid, hit, items, T, s);
+        pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, mfma_min, c->work, c->stats, host_l,
+                          slots_l, c->b.stride, c->b.copied, c->stream_wgs, a, items, T, s);
       }
-      {
-        StageTimer tm(c, PE_STAGE_GATE_UP, s);
-        pe::launch_step_b(c->cfg.wtype, miss, hit, items, T, s);
-      }
-      bool fused;
+      pe::ExpertArgs all = expert_args(c, layer, 0, x, topk_w, 0);
+      all.ids = topk_ids;
+      all.T = T;
+      all.E = d.E;
       {
         StageTimer tm(c, PE_STAGE_DOWN, s);
-        fused = pe::launch_down_topk(c->cfg.wtype, miss, T, static_cast<uint16_t*>(out), blk + c->ll.cur, s);
-        if (!fused) pe::launch_gemv_down(c->cfg.wtype, miss, items, T, s);
+        pe::launch_down_sum(c->cfg.wtype, all, T, static_cast<uint16_t*>(out), blk + c->ll.cur, s);
       }
-      if (fused) {
-        PE_HIP(hipGetLastError());
-        return PE_OK;
-      }
-    } else {
-      {
-        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-        pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, c->mfma_min, c->work, c->stats, host_l, slots_l,
-                                c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
-      }
-      run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
+      PE_HIP(hipGetLastError());
+      return PE_OK;
     }
+    // Unpaged, or experts with many entries: plan (+ plain page-in), then the
+    // GEMV and MFMA expert kernels over the published lists, then the top-k sum.
+    // Surplus MFMA workgroups exit on the device tile count.
+    const int tiles = mfma_min != pe::kNoMfma ? pe::ceil_div(n, pe::kTileM) + items : 0;
+    {
+      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+      pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, mfma_min, c->work, c->stats, host_l, slots_l,
+                              c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
+    }
+    run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
     {
       StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
       pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out),
@@ -537,7 +540,9 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   PE_HIP(hipMemcpyAsync(c->st_blk, blk, c->ll.state_prefix * 4, hipMemcpyDeviceToHost, s));
   PE_HIP(hipStreamSynchronize(s));
   pe::HostPlanSummary& sm = *c->sum;
-  if (pe::host_plan_step(d, c->ll, c->wl, c->st_ids, n, c->st_blk, c->st_work, &sm) != 0)
+  pe::Dims dp = d;
+  dp.mfma_min = mfma_min;
+  if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, c->st_blk, c->st_work, &sm) != 0)
     return fail(PE_ERR_INVALID_ARG, "step needs more waves than the context holds");
   PE_HIP(hipMemcpyAsync(blk, c->st_blk, (c->ll.slot_of + n) * 4, hipMemcpyHostToDevice, s));
   PE_HIP(hipMemcpyAsync(c->work, c->st_work, (c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));

@@ -11,7 +11,7 @@ struct Offsets {
   int tick, slot_expert, expert_slot, last_use;   // inside a state copy
   int cur, state0, state_stride;                  // current copy, copies
   int n_waves, plan_count, plan_expert, plan_slot, plan_evicted, slot_of;
-  int hdr, used_expert, used_slot, used_off, gemv_u, tile_u, tile_row, entries;
+  int hdr, used_expert, used_slot, used_off, gemv_u, gemv_desc, tile_u, tile_row, entries;
 };
 
 Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl);
@@ -67,22 +67,20 @@ void launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t
 void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
 void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipStream_t s);
 
-// Device-planned step on one queue.  Launch A: `P` workgroups plan the wave and
-// page in its missing experts (as launch_plan_page_in) while the others run the
-// gate/up projection of the experts already resident (`hit`, lean discovery).
-// Launch B: the gate/up projection of the paged-in experts (`miss`, published
-// lists) alongside the down projection of the resident ones.  The paged-in
-// experts' down projection and the top-k sum follow as their own launches.
+// Device-planned step with no many-token expert, two launches on one queue.
+// Launch A: `P` workgroups plan the wave (as launch_plan_page_in) and page in its
+// missing experts, computing their gate/up projection from the rows as they
+// arrive from the host; one more workgroup publishes the plan; the others run
+// the gate/up projection of the experts already resident (`a`: lean = 1, ids, T,
+// E, blk set).  Launch B (launch_down_sum): the down projection of every expert
+// of the wave and the fixed-order top-k sum into `out` by output-row blocks
+// (`a`: ids, T, E set); it toggles `flip` (the layer's current LRU-state copy).
+// The merged buffer is not used.
 void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
                    int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
-                   uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& hit, int items,
+                   uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& a, int items,
                    int max_m, hipStream_t s);
-void launch_step_b(int wtype, const ExpertArgs& miss, const ExpertArgs& hit, int items, int max_m, hipStream_t s);
-// Last launch of a device-planned step: down projection of the paged-in experts
-// (`miss`, which must carry ids, T and E) and the fixed-order top-k sum into
-// `out`, by output-row ranges; flips `flip`.  Returns false (nothing launched)
-// if its LDS would exceed 48 KiB; use launch_gemv_down + launch_topk_sum then.
-bool launch_down_topk(int wtype, const ExpertArgs& miss, int max_m, uint16_t* out, int32_t* flip, hipStream_t s);
+void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s);
 
 // MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
 // tokens).  Need H and I multiples of 128.

@@ -32,7 +32,8 @@ Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl) {
   o.plan_expert = (int)ll.plan_expert; o.plan_slot = (int)ll.plan_slot;
   o.plan_evicted = (int)ll.plan_evicted; o.slot_of = (int)ll.slot_of;
   o.hdr = (int)wl.hdr; o.used_expert = (int)wl.used_expert; o.used_slot = (int)wl.used_slot;
-  o.used_off = (int)wl.used_off; o.gemv_u = (int)wl.gemv_u; o.tile_u = (int)wl.tile_u;
+  o.used_off = (int)wl.used_off; o.gemv_u = (int)wl.gemv_u; o.gemv_desc = (int)wl.gemv_desc;
+  o.tile_u = (int)wl.tile_u;
   o.tile_row = (int)wl.tile_row; o.entries = (int)wl.entries;
   return o;
 }
@@ -94,25 +95,20 @@ __device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
 
 namespace {
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 2;
 }
 
 // Every thread of the grid takes 16-byte chunks gtid, gtid + gstride, ...,
-// kCopyUnroll loads in flight before the stores.
+// two loads in flight before the stores (named registers, no private array).
 __device__ __forceinline__ void copy_chunks(uint4* __restrict__ dst, const uint4* __restrict__ src,
                                             size_t n16, size_t gtid, size_t gstride) {
-  for (size_t base = gtid; base < n16; base += kCopyUnroll * gstride) {
-    uint4 v[kCopyUnroll];
-#pragma unroll
-    for (int q = 0; q < kCopyUnroll; ++q) {
-      size_t i = base + q * gstride;
-      if (i < n16) v[q] = src[i];
-    }
-#pragma unroll
-    for (int q = 0; q < kCopyUnroll; ++q) {
-      size_t i = base + q * gstride;
-      if (i < n16) dst[i] = v[q];
-    }
+  for (size_t i0 = gtid; i0 < n16; i0 += 2 * gstride) {
+    const size_t i1 = i0 + gstride;
+    const bool two = i1 < n16;
+    const uint4 v0 = src[i0];
+    uint4 v1 = make_uint4(0, 0, 0, 0);
+    if (two) v1 = src[i1];
+    dst[i0] = v0;
+    if (two) dst[i1] = v1;
   }
 }
 
@@ -175,9 +171,11 @@ struct PlanArgs {
 // One device-planned wave (all routed experts of a step with T*k <= K), in LDS.
 // Each of the ncopy + 1 planning workgroups computes the same plan from state
 // copy `cur`; workgroup `ncopy` publishes it (plan, new state in the other copy,
-// slot map, work lists, counters) while workgroups [0, ncopy) copy their share
-// of the missing experts.
-__device__ void plan_page_in_block(const PlanArgs& p, int block, int ncopy, char* lds) {
+// slot map, work lists, counters) while workgroups [0, ncopy) go on to copy
+// their share of the missing experts.  Returns the number of missing experts;
+// the plan stays in LDS (carve_plan): the r-th missing expert plan_e[r] goes to
+// slot victim[r].
+__device__ int plan_page_in_block(const PlanArgs& p, int block, int ncopy, char* lds) {
   const int E = p.E, K = p.K, n = p.n, MW = p.MW;
   const Offsets& o = p.o;
   int32_t* __restrict__ blk = p.blk;
@@ -258,7 +256,12 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int ncopy, char
       loc[0] += miss;
       loc[1] += 1;
       loc[2] += c;
-      if (c < mfma_min) loc[3 + miss] += 1; else loc[5 + miss] += (c + kTileM - 1) / kTileM;
+      const int tl = (c + kTileM - 1) / kTileM;
+      const bool gv = c < mfma_min;
+      loc[3] += gv && !miss;
+      loc[4] += gv && miss;
+      loc[5] += gv || miss ? 0 : tl;
+      loc[6] += !gv && miss ? tl : 0;
     }
   }
   int inc[kScanVals];
@@ -292,7 +295,12 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int ncopy, char
         run[0] += miss;
         run[1] += 1;
         run[2] += c;
-        if (c < mfma_min) run[3 + miss] += 1; else run[5 + miss] += (c + kTileM - 1) / kTileM;
+        const int tl = (c + kTileM - 1) / kTileM;
+        const bool gv = c < mfma_min;
+        run[3] += gv && !miss;
+        run[4] += gv && miss;
+        run[5] += gv || miss ? 0 : tl;
+        run[6] += !gv && miss ? tl : 0;
       }
     }
   }
@@ -353,7 +361,9 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int ncopy, char
       // was this expert missing? (its missing-prefix steps up right after it)
       const bool miss = (e + 1 < E ? (int)s_pref(0, e + 1) : n_miss) > (int)s_pref(0, e);
       if (c < mfma_min) {
-        gemv_u[miss ? g_hit + s_pref(4, e) : s_pref(3, e)] = u;
+        const int g = miss ? g_hit + s_pref(4, e) : s_pref(3, e);
+        gemv_u[g] = u;
+        reinterpret_cast<int4*>(work + o.gemv_desc)[g] = make_int4(j, s_pref(2, e), c, u);
       } else {
         int t0 = miss ? t_hit + s_pref(6, e) : s_pref(5, e);
         for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
@@ -399,22 +409,28 @@ __device__ void plan_page_in_block(const PlanArgs& p, int block, int ncopy, char
       if (s_bad) atomicAdd(stats + ST_BAD_IDS, (unsigned long long)s_bad);
     }
   }
-  if (publish || !p.do_copy) return;
-  // Page-in: the r-th missing expert's blob into its victim slot, every copier
-  // workgroup taking its share of the 16-byte chunks.
+  return n_miss;
+}
+
+// Page-in of a planned wave: the r-th missing expert's blob into its victim
+// slot, copier workgroup `block` of `ncopy` taking its share of the 16-byte
+// chunks.
+__device__ void copy_planned(const PlanArgs& p, int block, int ncopy, const char* lds, int n_miss) {
+  const PlanLds L = carve_plan(const_cast<char*>(lds), p.E, p.K, p.n);
   const size_t n16 = p.copy_bytes / 16;
   const size_t gtid = (size_t)block * blockDim.x + threadIdx.x;
   const size_t gstride = (size_t)ncopy * blockDim.x;
   for (int r = 0; r < n_miss; ++r) {
-    const uint4* src = reinterpret_cast<const uint4*>(p.host_rows + (size_t)s_plan_e[r] * p.stride);
-    uint4* dst = reinterpret_cast<uint4*>(p.slots + (size_t)s_victim[r] * p.stride);
+    const uint4* src = reinterpret_cast<const uint4*>(p.host_rows + (size_t)L.plan_e[r] * p.stride);
+    uint4* dst = reinterpret_cast<uint4*>(p.slots + (size_t)L.victim[r] * p.stride);
     copy_chunks(dst, src, n16, gtid, gstride);
   }
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_page_in_kernel(PlanArgs p, int ncopy) {
   extern __shared__ __align__(16) char lds[];
-  plan_page_in_block(p, blockIdx.x, ncopy, lds);
+  const int n_miss = plan_page_in_block(p, blockIdx.x, ncopy, lds);
+  if ((int)blockIdx.x < ncopy && p.do_copy) copy_planned(p, blockIdx.x, ncopy, lds, n_miss);
 }
 
 static PlanArgs plan_args(int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o, int mfma_min,
@@ -501,9 +517,88 @@ __device__ __forceinline__ void load_row(const uint4* __restrict__ row, int n_ch
   }
 }
 
-// Dot products of loaded chunks with MB token vectors staged in LDS as bf16
-// [MB][C].  fp32 FMA in a fixed order: chunk by chunk, element by element; the
-// FP8 block / int4 group scale multiplies each chunk's partial sum.
+// The scale of the 16-byte chunk starting at column `col` of a row: the FP8
+// block scale (one per 128 x 128 block) or the int4 group scale (one per row
+// and 128 columns); 1 for bf16 (unused).
+template <int FMT>
+__device__ __forceinline__ float chunk_scale(const float* __restrict__ s_fp8_row,
+                                             const uint16_t* __restrict__ s_i4_row, int col) {
+  if constexpr (FMT == PE_W_FP8_B128) return s_fp8_row[col >> 7];
+  else if constexpr (FMT == PE_W_INT4_G128) return half_bits_to_f32(s_i4_row[col >> 7]);
+  else return 1.0f;
+}
+
+// Dot product of one 16-byte weight chunk (columns col .. col + VPC - 1) with m
+// <= MB token vectors [MB][C] (bf16; in LDS or global memory), accumulated into
+// acc in fp32 in a fixed order: element by element; for FP8 and int4 the
+// chunk's partial sum is multiplied by its scale `sc` before it is added.
+// Every GEMV path runs a row as these chunk steps in ascending chunk order per
+// lane, so a (token, row) dot product never depends on the launch it ran in.
+template <int FMT, int MB>
+__device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t* __restrict__ xs, int C, int m,
+                                          float sc, float (&acc)[MB]) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (FMT == PE_W_BF16) {
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t >= m) break;
+      const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * C + col);
+      const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
+      float a = acc[t];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        a = __builtin_fmaf(bf16_lo(wd[p]), bf16_lo(xd[p]), a);
+        a = __builtin_fmaf(bf16_hi(wd[p]), bf16_hi(xd[p]), a);
+      }
+      acc[t] = a;
+    }
+  } else if constexpr (FMT == PE_W_FP8_B128) {
+    // 16 e4m3 codes, decoded exactly by the hardware conversion (OCP e4m3fn),
+    // word by word inside the token loop to keep few values live.
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t >= m) break;
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+      const uint4 x0 = xp[0], x1 = xp[1];
+      const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float part = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
+        part = __builtin_fmaf(lo[0], bf16_lo(xd[2 * p]), part);
+        part = __builtin_fmaf(lo[1], bf16_hi(xd[2 * p]), part);
+        part = __builtin_fmaf(hi[0], bf16_lo(xd[2 * p + 1]), part);
+        part = __builtin_fmaf(hi[1], bf16_hi(xd[2 * p + 1]), part);
+      }
+      acc[t] = __builtin_fmaf(sc, part, acc[t]);
+    }
+  } else {
+    // 32 nibbles; element 2i is the low nibble of byte i; value = nibble - 8
+    // (exact in fp32), decoded byte by byte inside the token loop.
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t >= m) break;
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+      float part = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 xv = xp[v];
+        const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t byte = (wd[v] >> (8 * b)) & 0xFFu;
+          part = __builtin_fmaf((float)(int)(byte & 0xFu) - 8.0f, bf16_lo(xd[b]), part);
+          part = __builtin_fmaf((float)(int)(byte >> 4) - 8.0f, bf16_hi(xd[b]), part);
+        }
+      }
+      acc[t] = __builtin_fmaf(sc, part, acc[t]);
+    }
+  }
+}
+
+// Dot products of the loaded chunks c0, c0 + LG, ... (at most
+// kMaxChunksInFlight, below n_ch) of one row with m token vectors.
 template <int FMT, int MB>
 __device__ __forceinline__ void dot_row(const uint4 (&w)[kMaxChunksInFlight], int n_ch, int c0, int LG,
                                         const uint16_t* __restrict__ xs, int C, int m,
@@ -516,66 +611,7 @@ __device__ __forceinline__ void dot_row(const uint4 (&w)[kMaxChunksInFlight], in
     const int c = c0 + q * LG;
     if (c >= n_ch) break;
     const int col = c * VPC;
-    const uint32_t wd[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
-    if constexpr (FMT == PE_W_BF16) {
-#pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        if (t >= m) break;
-        const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * C + col);
-        const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
-        float a = acc[t];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          a = __builtin_fmaf(bf16_lo(wd[p]), bf16_lo(xd[p]), a);
-          a = __builtin_fmaf(bf16_hi(wd[p]), bf16_hi(xd[p]), a);
-        }
-        acc[t] = a;
-      }
-    } else if constexpr (FMT == PE_W_FP8_B128) {
-      // 16 e4m3 codes, decoded exactly by the hardware conversion (OCP e4m3fn),
-      // word by word inside the token loop to keep few values live.
-      const float sc = s_fp8_row[col >> 7];
-#pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        if (t >= m) break;
-        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
-        const uint4 x0 = xp[0], x1 = xp[1];
-        const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        float part = 0.0f;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
-          part = __builtin_fmaf(lo[0], bf16_lo(xd[2 * p]), part);
-          part = __builtin_fmaf(lo[1], bf16_hi(xd[2 * p]), part);
-          part = __builtin_fmaf(hi[0], bf16_lo(xd[2 * p + 1]), part);
-          part = __builtin_fmaf(hi[1], bf16_hi(xd[2 * p + 1]), part);
-        }
-        acc[t] = __builtin_fmaf(sc, part, acc[t]);
-      }
-    } else {
-      // 32 nibbles; element 2i is the low nibble of byte i; value = nibble - 8
-      // (exact in fp32), decoded byte by byte inside the token loop.
-      const float sc = half_bits_to_f32(s_i4_row[col >> 7]);
-#pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        if (t >= m) break;
-        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
-        float part = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 xv = xp[v];
-          const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = (wd[v] >> (8 * b)) & 0xFFu;
-            part = __builtin_fmaf((float)(int)(byte & 0xFu) - 8.0f, bf16_lo(xd[b]), part);
-            part = __builtin_fmaf((float)(int)(byte >> 4) - 8.0f, bf16_hi(xd[b]), part);
-          }
-        }
-        acc[t] = __builtin_fmaf(sc, part, acc[t]);
-      }
-    }
+    dot_chunk<FMT, MB>(w[q], col, xs, C, m, chunk_scale<FMT>(s_fp8_row, s_i4_row, col), acc);
   }
 }
 
@@ -690,10 +726,10 @@ __device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvIte
   int g0, g1;
   part_range(a, hdr[hdr_gemv(a.MW, a.wave)], hdr[hdr_gemv_split(a.MW, a.wave)], hdr[hdr_gemv(a.MW, a.wave + 1)], g0, g1);
   if (item >= g1 - g0) return false;
-  const int u = a.work[a.o.gemv_u + g0 + item];
-  it.slot = a.work[a.o.used_slot + u];
-  it.off = a.work[a.o.used_off + u];
-  it.m = a.work[a.o.used_off + u + 1] - it.off;
+  const int4 dsc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc)[g0 + item];
+  it.slot = dsc.x;
+  it.off = dsc.y;
+  it.m = dsc.z;
   it.ent = a.work + a.o.entries + it.off;
   return true;
 }
@@ -848,69 +884,277 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, G
   down_block<FMT, MB>(a, blockIdx.x, blockIdx.y, g.LG, g.rows_per_block, lds);
 }
 
-// Device-planned step, launch A: workgroups [0, P] plan the wave (P publishes it,
-// [0, P) page in its missing experts); the rest run the gate/up projection of the experts that
-// were already resident (lean discovery).  Launch B: workgroups [0, gate.gx *
-// items) run the gate/up projection of the paged-in experts (published lists),
-// the rest the down projection of the resident ones.  One queue, no waiting
-// between workgroups: each role depends only on earlier launches.
+// Gate/up row block gi of a missing expert, paged in and projected in one pass:
+// rows i of the block (gemv_gate_up_kernel's geometry) are read from the mapped
+// host row `src`, stored into the slot `dst` and, as each 16-byte chunk arrives,
+// dotted with the expert's m token vectors (entries `ent`, staged in LDS `xs`),
+// one chunk per row in flight ahead of the arithmetic.  The lane's chunk order
+// and the reduction are those of gate_up_block, so h is bit-identical to a
+// gate/up projection read back from the slot.  FP8 / int4 scales are read from
+// the host row too.
 template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs hit, GemvGeom g) {
+__device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, const uint8_t* __restrict__ src,
+                                    uint8_t* __restrict__ dst, int gi, const int* ent, int m, int off,
+                                    uint16_t* xs) {
+  constexpr int VPC = Fmt<FMT>::VPC;
+  const int H = a.H, I = a.I, n_ch = H / VPC, LG = g.LG;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
+  const int i = gi * g.rows_per_block + wv * groups + grp;    // this group's gate row; up row I + i
+  const bool active = i < I;
+  const uint4* sg = reinterpret_cast<const uint4*>(src + a.off_w13) + (size_t)i * n_ch;
+  const uint4* su = reinterpret_cast<const uint4*>(src + a.off_w13) + (size_t)(I + i) * n_ch;
+  uint4* dg = reinterpret_cast<uint4*>(dst + a.off_w13) + (size_t)i * n_ch;
+  uint4* du = reinterpret_cast<uint4*>(dst + a.off_w13) + (size_t)(I + i) * n_ch;
+  const float* sgf = reinterpret_cast<const float*>(src + a.off_s13) + (size_t)(i >> 7) * (H / 128);
+  const float* suf = reinterpret_cast<const float*>(src + a.off_s13) + (size_t)((I + i) >> 7) * (H / 128);
+  const uint16_t* sgh = reinterpret_cast<const uint16_t*>(src + a.off_s13) + (size_t)i * (H / 128);
+  const uint16_t* suh = reinterpret_cast<const uint16_t*>(src + a.off_s13) + (size_t)(I + i) * (H / 128);
+  // the first token batch also stores the rows (tb == 0 runs even for m == 0)
+  for (int tb = 0; tb == 0 || tb < m; tb += MB) {
+    const int mb = max(0, min(MB, m - tb));
+    __syncthreads();
+    stage_rows(xs, a.x, H, ent + tb, mb, a.k);
+    __syncthreads();
+    if (!active) continue;
+    float gacc[MB], uacc[MB];
+#pragma unroll
+    for (int t = 0; t < MB; ++t) { gacc[t] = 0.0f; uacc[t] = 0.0f; }
+    int c = lig;
+    uint4 wg = make_uint4(0, 0, 0, 0), wu = wg;
+    float scg = 1.0f, scu = 1.0f;
+    if (c < n_ch) {
+      wg = sg[c]; wu = su[c];
+      scg = chunk_scale<FMT>(sgf, sgh, c * VPC); scu = chunk_scale<FMT>(suf, suh, c * VPC);
+    }
+    while (c < n_ch) {
+      const int cn = c + LG;
+      uint4 ng = make_uint4(0, 0, 0, 0), nu = ng;
+      float nsg = 1.0f, nsu = 1.0f;
+      if (cn < n_ch) {
+        ng = sg[cn]; nu = su[cn];
+        nsg = chunk_scale<FMT>(sgf, sgh, cn * VPC); nsu = chunk_scale<FMT>(suf, suh, cn * VPC);
+      }
+      if (tb == 0) { dg[c] = wg; du[c] = wu; }
+      dot_chunk<FMT, MB>(wg, c * VPC, xs, H, mb, scg, gacc);
+      dot_chunk<FMT, MB>(wu, c * VPC, xs, H, mb, scu, uacc);
+      c = cn; wg = ng; wu = nu; scg = nsg; scu = nsu;
+    }
+    group_reduce<MB>(gacc, LG);
+    group_reduce<MB>(uacc, LG);
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t < mb && lig == t)
+        a.h[(size_t)(off + tb + t) * I + i] = f32_to_bf16(silu_f(gacc[t]) * uacc[t]);
+    }
+  }
+}
+
+// Page-in of a device-planned wave's missing experts with their gate/up
+// projection fused in (copier workgroup w of P): the gate/up row blocks of all
+// missing experts are dealt round-robin, block gi of the r-th missing expert
+// being item r * gx + gi; then the rest of every blob (down weights, scales) is
+// copied plainly.  The missing experts' weights cross the host link once and are
+// never read back from HBM in this step's gate/up.
+template <int FMT, int MB>
+__device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom& g, int w, int P, char* lds,
+                          int n_miss) {
+  const PlanLds L = carve_plan(lds, p.E, p.K, p.n);
+  const size_t plan_b = plan_lds_bytes(p.E, p.K, p.n);
+  int* s_ent = reinterpret_cast<int*>(lds + plan_b);                                    // [n]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + plan_b + al16(4 * (size_t)p.n));     // [MB][H]
+  for (int r = 0; r < n_miss; ++r) {
+    int gi = ((w - (r * g.gx) % P) % P + P) % P;     // this workgroup's first block of expert r
+    if (gi >= g.gx) continue;
+    const int e = L.plan_e[r];
+    for (int i = threadIdx.x; i < p.n; i += blockDim.x) {     // entries of e, ascending
+      if (L.ids[i] != e) continue;
+      int rank = 0;
+      for (int q = 0; q < i; ++q) rank += L.ids[q] == e;
+      s_ent[rank] = i;
+    }
+    const int m = L.cnt[e], off = L.pref[2 * p.E + e];
+    const uint8_t* src = p.host_rows + (size_t)e * p.stride;
+    uint8_t* dst = p.slots + (size_t)L.victim[r] * p.stride;
+    for (; gi < g.gx; gi += P) stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, s_ent, m, off, xs);
+    __syncthreads();     // s_ent is rebuilt for the next expert
+  }
+  const size_t rest16 = (p.copy_bytes - a.off_w2) / 16;
+  for (int r = 0; r < n_miss; ++r) {
+    const uint4* src = reinterpret_cast<const uint4*>(p.host_rows + (size_t)L.plan_e[r] * p.stride + a.off_w2);
+    uint4* dst = reinterpret_cast<uint4*>(p.slots + (size_t)L.victim[r] * p.stride + a.off_w2);
+    copy_chunks(dst, src, rest16, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
+  }
+}
+
+// Device-planned step with no many-token expert, launch A: workgroups [0, P)
+// plan the wave and page in its missing experts with their gate/up projection
+// (stream_in); workgroup P plans it and publishes the plan, the new LRU state,
+// the work lists and the counters; the rest run the gate/up projection of the
+// experts that were already resident (lean discovery, `a.lean` set).  No
+// workgroup waits for another.
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs a, GemvGeom g) {
   extern __shared__ __align__(16) char lds[];
   if ((int)blockIdx.x <= P) {
-    plan_page_in_block(p, blockIdx.x, P, lds);
+    const int n_miss = plan_page_in_block(p, blockIdx.x, P, lds);
+    if ((int)blockIdx.x < P) stream_in<FMT, MB>(p, a, g, blockIdx.x, P, lds, n_miss);
   } else {
     const int b = blockIdx.x - P - 1;
-    gate_up_block<FMT, MB>(hit, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
+    gate_up_block<FMT, MB>(a, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
   }
 }
 
-template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void step_b_kernel(ExpertArgs miss, GemvGeom gu, int n_gu, ExpertArgs hit,
-                                                              GemvGeom dn) {
-  extern __shared__ __align__(16) char lds[];
-  if ((int)blockIdx.x < n_gu) {
-    gate_up_block<FMT, MB>(miss, blockIdx.x % gu.gx, blockIdx.x / gu.gx, gu.LG, gu.rows_per_block, lds);
-  } else {
-    const int b = blockIdx.x - n_gu;
-    down_block<FMT, MB>(hit, b % dn.gx, b / dn.gx, dn.LG, dn.rows_per_block, lds);
+// First round of one down-projection lane group's loads for rows n0 and n0 + 1
+// of expert blob `blob`: chunks lig, lig + LG, ... (kMaxChunksInFlight at most)
+// and each chunk's scale.
+struct DownRows {
+  uint4 w0[kMaxChunksInFlight], w1[kMaxChunksInFlight];
+  float s0[kMaxChunksInFlight], s1[kMaxChunksInFlight];
+};
+
+template <int FMT>
+__device__ __forceinline__ void fetch_down_rows(const ExpertArgs& a, const uint8_t* blob, int n0, bool act0,
+                                                bool act1, int c0, int LG, int n_ch, DownRows& r) {
+  constexpr int VPC = Fmt<FMT>::VPC;
+  const int I = a.I;
+  const uint4* W2 = reinterpret_cast<const uint4*>(blob + a.off_w2);
+  const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
+  const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
+  if (act0) load_row(W2 + (size_t)n0 * n_ch, n_ch, c0, LG, r.w0);
+  if (act1) load_row(W2 + (size_t)(n0 + 1) * n_ch, n_ch, c0, LG, r.w1);
+#pragma unroll
+  for (int q = 0; q < kMaxChunksInFlight; ++q) {
+    const int c = c0 + q * LG;
+    r.s0[q] = r.s1[q] = 1.0f;
+    if (c >= n_ch) continue;
+    if (act0) r.s0[q] = chunk_scale<FMT>(S2f + (size_t)(n0 >> 7) * (I / 128), S2h + (size_t)n0 * (I / 128), c * VPC);
+    if (act1)
+      r.s1[q] = chunk_scale<FMT>(S2f + (size_t)((n0 + 1) >> 7) * (I / 128), S2h + (size_t)(n0 + 1) * (I / 128),
+                                 c * VPC);
   }
 }
 
-// Device-planned step, last launch: the down projection of the paged-in experts
-// and the fixed-order top-k sum, partitioned by output rows so no workgroup
-// needs another's results.  Workgroup bx owns rows [bx*R, bx*R + R): it computes
-// those rows for every paged-in expert (keeping them in LDS as well as in the
-// merged buffer), then for each token sums all k entries of its rows in j order
-// (resident experts' entries from the merged buffer, written by the previous
-// launch), rounds once to bf16, and workgroup 0 makes the new LRU-state copy
-// current.
+// One GEMV expert's down projection for rows n0, n0 + 1 of one lane group:
+// s_y[e * RB + row - r0] = w[e] * (W2[row] . h[pos]) for each of its entries e.
+// `r` holds the first round of loads of token batch 0.  Per lane the chunks run
+// in ascending order and the group reduces by the xor butterfly, as in
+// down_block.
 template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void down_topk_kernel(ExpertArgs miss, GemvGeom g, uint16_t* out,
-                                                                 int32_t* flip) {
+__device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 dsc, DownRows& r, int n0,
+                                               bool act0, bool act1, int lig, int LG, int n_ch,
+                                               const uint16_t* hbase, float* s_y, int RB, int r0) {
+  constexpr int VPC = Fmt<FMT>::VPC;
+  const int I = a.I, off = dsc.y, m = dsc.z;
+  const uint8_t* blob = a.slots + (size_t)dsc.x * a.slot_stride;
+  const int32_t* ent = a.work + a.o.entries + off;
+  for (int tb = 0; tb < m; tb += MB) {
+    const int mb = min(MB, m - tb);
+    if (tb > 0) fetch_down_rows<FMT>(a, blob, n0, act0, act1, lig, LG, n_ch, r);
+    const uint16_t* hs = hbase + (size_t)(off + tb) * I;
+    float y0[MB], y1[MB];
+#pragma unroll
+    for (int t = 0; t < MB; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
+    if (act0) {
+      for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
+#pragma unroll
+        for (int q = 0; q < kMaxChunksInFlight; ++q) {
+          const int c = c0 + q * LG;
+          if (c >= n_ch) break;
+          dot_chunk<FMT, MB>(r.w0[q], c * VPC, hs, I, mb, r.s0[q], y0);
+          if (act1) dot_chunk<FMT, MB>(r.w1[q], c * VPC, hs, I, mb, r.s1[q], y1);
+        }
+        if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
+        fetch_down_rows<FMT>(a, blob, n0, act0, act1, c0 + LG * kMaxChunksInFlight, LG, n_ch, r);
+      }
+    }
+    group_reduce<MB>(y0, LG);
+    group_reduce<MB>(y1, LG);
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t < mb && lig == t && act0) {
+        const int e = ent[tb + t];
+        const float we = a.topk_w[e];
+        s_y[(size_t)e * RB + n0 - r0] = we * y0[t];
+        if (act1) s_y[(size_t)e * RB + n0 + 1 - r0] = we * y1[t];
+      }
+    }
+  }
+}
+
+// Device-planned step, launch B: the down projection of every expert of the
+// wave and the fixed-order top-k sum, by output rows.  Workgroup b owns the RB
+// rows [b*RB, b*RB + RB) that one wavefront covers in gemv_down_kernel's
+// geometry (two rows per lane group).  Its NW (4..8) wavefronts take the wave's
+// GEMV experts round-robin; each issues the weight loads of its first expert
+// (its descriptor is one load away) before the workgroup stages the step's h
+// rows (if STAGE) and routed ids in LDS, and the loads of its next expert
+// before it computes the current one.  Every entry's w[e] * (W2
+// h)[row] goes to LDS; then each token's k entries are summed in j order
+// (invalid ids skipped) and rounded once to bf16: the arithmetic of down_block +
+// topk_sum_rows.  Workgroup 0 makes the new LRU-state copy current.
+template <int FMT, int MB, bool STAGE>
+__global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uint16_t* __restrict__ out,
+                                                        int32_t* flip) {
   extern __shared__ __align__(16) char lds[];
-  const int T = miss.T, k = miss.k, n = T * k, R = g.rows_per_block, H = miss.H;
-  float* s_y = reinterpret_cast<float*>(lds);                                        // [n][R]
-  unsigned char* s_miss = reinterpret_cast<unsigned char*>(lds + al16(4 * (size_t)n * R));
-  char* rest = lds + al16(4 * (size_t)n * R) + al16((size_t)n);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) s_miss[i] = 0;
+  constexpr int VPC = Fmt<FMT>::VPC;
+  const int T = a.T, k = a.k, n = T * k, H = a.H, I = a.I, n_ch = I / VPC;
+  const int NW = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
+  const int RB = 2 * groups, r0 = blockIdx.x * RB;
+  float* s_y = reinterpret_cast<float*>(lds);                                          // [n][RB]
+  int* s_id = reinterpret_cast<int*>(lds + al16(4 * (size_t)n * RB));                  // [n]
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(lds + al16(4 * (size_t)n * RB) + al16(4 * (size_t)n));  // [n][I]
+  const int32_t* hdr = a.work + a.o.hdr;
+  const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
+  const int n_items = hdr[hdr_gemv(a.MW, 1)];               // wave 0's GEMV items start at 0
+  const int n0 = r0 + 2 * grp;
+  const bool act0 = n0 < H, act1 = n0 + 1 < H;
+  // this wavefront's experts it, it + NW, ...: the next one's first round of
+  // weight loads is in flight while the current one is computed
+  int it = wv;
+  int4 d = it < a.E ? desc[it] : make_int4(0, 0, 0, 0);
+  DownRows rA, rB;      // ping-pong buffers (named, so they stay in registers)
+  if (it < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s_id[i] = a.ids[i];
+  if constexpr (STAGE) {
+    const int n16 = n * I / 8;
+    for (int i = threadIdx.x; i < n16; i += blockDim.x)
+      reinterpret_cast<uint4*>(s_h)[i] = reinterpret_cast<const uint4*>(a.h)[i];
+  }
   __syncthreads();
-  const int32_t* hdr = miss.work + miss.o.hdr;
-  const int items = hdr[hdr_gemv(miss.MW, 1)] - hdr[hdr_gemv_split(miss.MW, 0)];
-  for (int item = 0; item < items; ++item) {
-    down_block<FMT, MB>(miss, blockIdx.x, item, g.LG, R, rest, s_y, s_miss);
-    __syncthreads();
+  const uint16_t* hbase = STAGE ? s_h : a.h;
+  while (it < n_items) {
+    int nx = it + NW;
+    int4 dn = make_int4(0, 0, 0, 0);
+    if (nx < n_items) {
+      dn = desc[nx];
+      fetch_down_rows<FMT>(a, a.slots + (size_t)dn.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
+    }
+    down_rows_item<FMT, MB>(a, d, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
+    it = nx;
+    d = dn;
+    if (it >= n_items) break;
+    nx = it + NW;
+    if (nx < n_items) {
+      dn = desc[nx];
+      fetch_down_rows<FMT>(a, a.slots + (size_t)dn.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
+    }
+    down_rows_item<FMT, MB>(a, d, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
+    it = nx;
+    d = dn;
   }
-  const int r0 = blockIdx.x * R;
-  for (int idx = threadIdx.x; idx < T * R; idx += blockDim.x) {
-    const int t = idx / R, r = idx - t * R, row = r0 + r;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * RB; idx += blockDim.x) {
+    const int t = idx / RB, r = idx - t * RB, row = r0 + r;
     if (row >= H) continue;
-    float acc = 0.f;
+    float acc = 0.0f;
     for (int j = 0; j < k; ++j) {
       const int e = t * k + j;
-      const int id = miss.ids[e];
-      if (id < 0 || id >= miss.E) continue;
-      acc += s_miss[e] ? s_y[(size_t)e * R + r] : miss.merged[(size_t)e * H + row];
+      const int id = s_id[e];
+      if (id < 0 || id >= a.E) continue;
+      acc += s_y[(size_t)e * RB + r];
     }
     out[(size_t)t * H + row] = f32_to_bf16(acc);
   }
@@ -1000,33 +1244,32 @@ void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipS
 
 void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dims& d, const Offsets& o,
                    int mfma_min, int32_t* work, unsigned long long* stats, const uint8_t* host_rows,
-                   uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& hit, int items,
+                   uint8_t* slots, size_t stride, size_t copy_bytes, int P, const ExpertArgs& a, int items,
                    int max_m, hipStream_t s) {
   const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, true);
   const int mb = pick_mb(max_m);
-  const GemvGeom g = gate_up_geom(wtype, hit);
-  const size_t lds = std::max(plan_lds_bytes(d.E, d.K, n), lean_head(hit) + (size_t)mb * hit.H * 2);
+  const GemvGeom g = gate_up_geom(wtype, a);
+  const size_t copier = plan_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + (size_t)mb * a.H * 2;
+  const size_t lds = std::max(copier, lean_head(a) + (size_t)mb * a.H * 2);
   const int blocks = P + 1 + g.gx * items;
-  PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, hit, g)));
+  PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g)));
 }
 
-bool launch_down_topk(int wtype, const ExpertArgs& miss, int max_m, uint16_t* out, int32_t* flip, hipStream_t s) {
+void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s) {
   const int mb = pick_mb(max_m);
-  const GemvGeom g = down_geom(wtype, miss);
-  const int n = miss.T * miss.k;
-  const size_t lds = al16(4 * (size_t)n * g.rows_per_block) + al16((size_t)n) + (size_t)mb * miss.I * 2;
-  if (lds > 48 * 1024) return false;
-  PE_DISPATCH(wtype, mb, (down_topk_kernel<F_, M_><<<g.gx, kGemvThreads, lds, s>>>(miss, g, out, flip)));
-  return true;
-}
-
-void launch_step_b(int wtype, const ExpertArgs& miss, const ExpertArgs& hit, int items, int max_m, hipStream_t s) {
-  const int mb = pick_mb(max_m);
-  const GemvGeom gu = gate_up_geom(wtype, miss), dn = down_geom(wtype, hit);
-  const int n_gu = gu.gx * items;
-  const size_t lds = std::max((size_t)mb * miss.H * 2, lean_head(hit) + (size_t)mb * hit.I * 2);
-  const int blocks = n_gu + dn.gx * items;
-  PE_DISPATCH(wtype, mb, (step_b_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(miss, gu, n_gu, hit, dn)));
+  const int LG = lanes_per_row(a.I / vpc_of(wtype));
+  const int RB = 2 * (64 / LG);
+  const int n = a.T * a.k;
+  // one wavefront per expert the wave can hold, 4..8
+  const int nw = std::max(4, std::min(8, n));
+  const size_t head = al16(4 * (size_t)n * RB) + al16(4 * (size_t)n);
+  const size_t staged = head + (size_t)n * a.I * 2;
+  const dim3 grid(ceil_div(a.H, RB)), block(64 * nw);
+  if (staged <= 64 * 1024) {
+    PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, true><<<grid, block, staged, s>>>(a, LG, out, flip)));
+  } else {
+    PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, false><<<grid, block, head, s>>>(a, LG, out, flip)));
+  }
 }
 
 // ------------------------------------------------------------------ MFMA grouped GEMM

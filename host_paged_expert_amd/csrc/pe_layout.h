@@ -8,11 +8,13 @@
 namespace pe {
 
 constexpr int kMaxExperts = 1024;
-// An expert whose entries in one step number at least this many runs on the
-// MFMA grouped-GEMM kernels, otherwise on the GEMV kernels.  The choice depends
-// only on that count, which no wave split changes, so a paged step and an
+// In a step of at least this many tokens, an expert whose entries number at
+// least this many runs on the MFMA grouped-GEMM kernels, otherwise on the GEMV
+// kernels.  The choice depends only on the step's token count and the expert's
+// entry count, which no wave split and no K changes, so a paged step and an
 // unpaged step run every expert through the same arithmetic.
 constexpr int kMfmaMinTokens = 16;
+constexpr int kNoMfma = 1 << 30;   // threshold that sends every expert to the GEMV kernels
 constexpr int kTileM = 32;   // token rows per MFMA tile
 
 // Device statistic counters (uint64 each).
@@ -101,6 +103,8 @@ struct WorkLayout {
   size_t used_slot;     // [E]
   size_t used_off;      // [E+1]
   size_t gemv_u;        // [E]          used experts on the GEMV kernels, per wave
+  size_t gemv_desc;     // [E][4]       the same GEMV items as {slot, first sorted position,
+                        //              entry count, used-expert index}, 16-byte aligned
   size_t tile_u;        // [max_tiles]  MFMA tiles: used expert
   size_t tile_row;      // [max_tiles]  MFMA tiles: first row inside the expert
   size_t entries;       // [max_entries] entry index t*k+j at each sorted position
@@ -128,6 +132,8 @@ inline WorkLayout make_work_layout(const Dims& d) {
   w.used_slot = o; o += d.E;
   w.used_off = o; o += d.E + 1;
   w.gemv_u = o; o += d.E;
+  o = (o + 3) / 4 * 4;
+  w.gemv_desc = o; o += 4 * (size_t)d.E;
   w.tile_u = o; o += d.max_tiles;
   w.tile_row = o; o += d.max_tiles;
   w.entries = o; o += d.max_entries;

@@ -52,6 +52,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
   int32_t* used_slot = work + wl.used_slot;
   int32_t* used_off = work + wl.used_off;
   int32_t* gemv_u = work + wl.gemv_u;
+  int32_t* gemv_desc = work + wl.gemv_desc;
   int32_t* tile_u = work + wl.tile_u;
   int32_t* tile_row = work + wl.tile_row;
   int32_t* entries = work + wl.entries;
@@ -115,6 +116,8 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
         const int e = used_expert[uu];
         if (was_hit[e] != (pass == 0)) continue;
         if (cnt[e] < d.mfma_min) {
+          int32_t* dsc = gemv_desc + 4 * (size_t)ng;
+          dsc[0] = used_slot[uu]; dsc[1] = used_off[uu]; dsc[2] = cnt[e]; dsc[3] = uu;
           gemv_u[ng++] = uu;
           max_gemv = std::max(max_gemv, cnt[e]);
         } else {
