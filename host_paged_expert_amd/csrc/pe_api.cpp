@@ -108,7 +108,8 @@ struct pe_ctx {
   float* merged = nullptr;             // device: [max_entries][H] fp32
   unsigned long long* stats = nullptr; // device: [ST_COUNT]
   int32_t* st_ids = nullptr;           // pinned staging: [max_entries]
-  int32_t* st_blk = nullptr;           // pinned staging: [ll.total]
+  int32_t* st_blk = nullptr;           // pinned: per layer [L][ll.total], the host mirror of its block
+  std::vector<char> mirror_ok;         // per layer: st_blk holds the device block's LRU state
   int32_t* st_work = nullptr;          // pinned staging: [wl.total]
   pe::HostPlanSummary* sum = nullptr;
   unsigned long long host_counts[pe::ST_COUNT] = {};
@@ -371,7 +372,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     }
   }
   struct { int32_t** p; size_t words; } pin[] = {
-      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, c->ll.total}, {&c->st_work, c->wl.total}};
+      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, (size_t)d.L * c->ll.total}, {&c->st_work, c->wl.total}};
   for (auto& a : pin) {
     if (hipHostMalloc(reinterpret_cast<void**>(a.p), a.words * 4, hipHostMallocDefault) != hipSuccess) {
       *a.p = nullptr;
@@ -392,6 +393,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "creating the side stream and its events failed");
   }
+  c->mirror_ok.assign(d.L, 0);
   pe::launch_reset_lru(c->blocks, c->ll.total, 0, d.L, c->o, d.E, d.K, unpaged, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
     free_ctx(c);
@@ -445,6 +447,7 @@ int pe_reset_lru(pe_ctx* c, int layer, void* stream) {
   int rc = use_device(c);
   if (rc) return rc;
   const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->d.L : layer + 1;
+  for (int l = l0; l < l1; ++l) c->mirror_ok[l] = 0;
   pe::launch_reset_lru(c->blocks, c->ll.total, l0, l1, c->o, c->d.E, c->d.K, c->unpaged,
                        static_cast<hipStream_t>(stream));
   PE_HIP(hipGetLastError());
@@ -475,6 +478,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   const int mfma_min = T >= c->mfma_min ? c->mfma_min : pe::kNoMfma;
 
   if (device_plan) {
+    c->mirror_ok[layer] = 0;     // the device updates this layer's LRU state
     // One wave, on the caller's stream only (a second stream would put graph
     // branches on other hardware queues, whose cross-queue dependencies cost more
     // than they hide).  No host synchronisation: capturable.
@@ -534,23 +538,45 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   if (cap != hipStreamCaptureStatusNone)
     return fail(PE_ERR_NOT_CAPTURABLE, "T*top_k=%d > K=%d needs host planning, which cannot be captured", n, d.K);
 
-  // Host-planned step: read ids and LRU state back (the one synchronisation),
-  // plan every wave, upload plans and work lists, then run the waves in order.
+  // Host-planned step: read the ids back, and the layer's LRU state unless the
+  // host's mirror of it is current (a host-planned step was the last to change
+  // it); that is the one synchronisation.  Plan every wave on the host, upload
+  // the block (state, plans, slot map) and the work lists, then run the waves in
+  // order.
+  int32_t* mirror = c->st_blk + (size_t)layer * c->ll.total;
   PE_HIP(hipMemcpyAsync(c->st_ids, topk_ids, (size_t)n * 4, hipMemcpyDeviceToHost, s));
-  PE_HIP(hipMemcpyAsync(c->st_blk, blk, c->ll.state_prefix * 4, hipMemcpyDeviceToHost, s));
+  if (!c->mirror_ok[layer])
+    PE_HIP(hipMemcpyAsync(mirror, blk, c->ll.state_prefix * 4, hipMemcpyDeviceToHost, s));
   PE_HIP(hipStreamSynchronize(s));
+  c->mirror_ok[layer] = 0;
   pe::HostPlanSummary& sm = *c->sum;
   pe::Dims dp = d;
   dp.mfma_min = mfma_min;
-  if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, c->st_blk, c->st_work, &sm) != 0)
+  if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, mirror, c->st_work, &sm) != 0)
     return fail(PE_ERR_INVALID_ARG, "step needs more waves than the context holds");
-  PE_HIP(hipMemcpyAsync(blk, c->st_blk, (c->ll.slot_of + n) * 4, hipMemcpyHostToDevice, s));
+  PE_HIP(hipMemcpyAsync(blk, mirror, (c->ll.slot_of + n) * 4, hipMemcpyHostToDevice, s));
   PE_HIP(hipMemcpyAsync(c->work, c->st_work, (c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));
+  c->mirror_ok[layer] = 1;
   const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
   for (int w = 0; w < sm.n_waves; ++w) {
-    const int cnt = c->st_blk[c->ll.plan_count + w];
+    const int cnt = mirror[c->ll.plan_count + w];
     const int g_all = sm.gemv_items[w], g_hit = sm.gemv_hits[w];
     const int t_all = sm.tiles[w], t_hit = sm.tile_hits[w];
+    if (!c->unpaged && !dma && t_all == 0) {
+      // GEMV experts only: one launch pages in the missing experts with their
+      // gate/up projection fused in while the resident ones run theirs, then
+      // one launch runs the wave's down projection.
+      pe::ExpertArgs a = expert_args(c, layer, w, x, topk_w, 1);
+      {
+        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+        pe::launch_wave_a(c->cfg.wtype, a, g_hit, sm.max_gemv_tokens, c->stream_wgs, host_l, c->b.stride,
+                          c->b.copied, s);
+      }
+      a.part = 0;
+      StageTimer tm(c, PE_STAGE_DOWN, s);
+      pe::launch_gemv_down(c->cfg.wtype, a, g_all, sm.max_gemv_tokens, s);
+      continue;
+    }
     const bool fork = !c->unpaged && cnt > 0 && (g_hit > 0 || t_hit > 0);
     if (fork) {
       PE_HIP(hipEventRecord(c->ev_fork, s));
@@ -561,8 +587,8 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
     if (!c->unpaged && cnt > 0) {
       StageTimer tm(c, PE_STAGE_PAGE_IN, s);
       if (dma) {
-        const int32_t* pe_ = c->st_blk + c->ll.plan_expert + (size_t)w * d.K;
-        const int32_t* ps_ = c->st_blk + c->ll.plan_slot + (size_t)w * d.K;
+        const int32_t* pe_ = mirror + c->ll.plan_expert + (size_t)w * d.K;
+        const int32_t* ps_ = mirror + c->ll.plan_slot + (size_t)w * d.K;
         for (int r = 0; r < cnt; ++r)
           PE_HIP(hipMemcpyAsync(slots_l + (size_t)ps_[r] * c->b.stride,
                                 c->host_store + ((size_t)layer * d.E + pe_[r]) * c->b.stride, c->b.copied,

@@ -82,6 +82,14 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
                    int max_m, hipStream_t s);
 void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s);
 
+// Host-planned wave with no MFMA tiles (work lists uploaded, `a` = the wave,
+// part 1): `P` workgroups page in the wave's missing experts from the mapped
+// host rows with their gate/up projection computed on the way; the others run
+// the gate/up projection of its `hit_items` resident experts.  Follow with
+// launch_gemv_down over all of the wave's GEMV items (part 0).
+void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int P, const uint8_t* host_rows,
+                   size_t stride, size_t copy_bytes, hipStream_t s);
+
 // MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
 // tokens).  Need H and I multiples of 128.
 void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);

@@ -987,6 +987,48 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
   }
 }
 
+// Host-planned wave with no MFMA tiles, launch A: workgroups [0, P) page in the
+// wave's missing experts (its GEMV items past the hit split, descriptors from
+// the uploaded work lists), computing their gate/up projection from the rows as
+// they arrive (stream_gate_up_rows), then copy the rest of each blob; the others
+// run the gate/up projection of the wave's experts that were already resident
+// (`a.part` = 1).  The wave's down projection follows as its own launch.
+template <int FMT, int MB>
+__global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, GemvGeom g, int P,
+                                                              const uint8_t* __restrict__ host_rows,
+                                                              size_t stride, size_t copy_bytes) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x >= P) {
+    const int b = blockIdx.x - P;
+    gate_up_block<FMT, MB>(a, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
+    return;
+  }
+  const int w = blockIdx.x;
+  const int32_t* hdr = a.work + a.o.hdr;
+  const int split = hdr[hdr_gemv_split(a.MW, a.wave)], g1 = hdr[hdr_gemv(a.MW, a.wave + 1)];
+  const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+  const int n_miss = g1 - split;
+  for (int r = 0; r < n_miss; ++r) {
+    int gi = ((w - (r * g.gx) % P) % P + P) % P;
+    if (gi >= g.gx) continue;
+    const int4 d = desc[split + r];
+    const int e = a.work[a.o.used_expert + d.w];
+    const uint8_t* src = host_rows + (size_t)e * stride;
+    uint8_t* dst = const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride;
+    for (; gi < g.gx; gi += P)
+      stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, a.work + a.o.entries + d.y, d.z, d.y, xs);
+  }
+  const size_t rest16 = (copy_bytes - a.off_w2) / 16;
+  for (int r = 0; r < n_miss; ++r) {
+    const int4 d = desc[split + r];
+    const int e = a.work[a.o.used_expert + d.w];
+    const uint4* src = reinterpret_cast<const uint4*>(host_rows + (size_t)e * stride + a.off_w2);
+    uint4* dst = reinterpret_cast<uint4*>(const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride + a.off_w2);
+    copy_chunks(dst, src, rest16, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
+  }
+}
+
 // Device-planned step with no many-token expert, launch A: workgroups [0, P)
 // plan the wave and page in its missing experts with their gate/up projection
 // (stream_in); workgroup P plans it and publishes the plan, the new LRU state,
@@ -1253,6 +1295,15 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const size_t lds = std::max(copier, lean_head(a) + (size_t)mb * a.H * 2);
   const int blocks = P + 1 + g.gx * items;
   PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g)));
+}
+
+void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int P, const uint8_t* host_rows,
+                   size_t stride, size_t copy_bytes, hipStream_t s) {
+  const int mb = pick_mb(max_m);
+  const GemvGeom g = gate_up_geom(wtype, a);
+  const size_t lds = (size_t)mb * a.H * 2;
+  const int blocks = P + g.gx * hit_items;
+  PE_DISPATCH(wtype, mb, (wave_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(a, g, P, host_rows, stride, copy_bytes)));
 }
 
 void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s) {
