@@ -528,12 +528,30 @@ __device__ __forceinline__ float chunk_scale(const float* __restrict__ s_fp8_row
   else return 1.0f;
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// a.lo * b.lo + a.hi * b.hi + c, a and b packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// Two fp32 values that bf16 holds exactly, packed as a bf16 pair (lo, hi).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 // Dot product of one 16-byte weight chunk (columns col .. col + VPC - 1) with m
 // <= MB token vectors [MB][C] (bf16; in LDS or global memory), accumulated into
-// acc in fp32 in a fixed order: element by element; for FP8 and int4 the
-// chunk's partial sum is multiplied by its scale `sc` before it is added.
-// Every GEMV path runs a row as these chunk steps in ascending chunk order per
-// lane, so a (token, row) dot product never depends on the launch it ran in.
+// acc in fp32 in a fixed order.  The chunk is decoded once into bf16 pairs
+// (exact for all three formats) and each token takes one v_dot2 per pair, pair
+// by pair; for FP8 and int4 the chunk's partial sum is then multiplied by its
+// scale `sc` and added.  int4 nibbles are decoded as (q - 8) / 16 (exact), so
+// their partial sum is 1/16 of the true one and the scale is taken times 16:
+// the product is the same number.  Every GEMV path runs a row as these chunk
+// steps in ascending chunk order per lane, so a (token, row) dot product never
+// depends on the launch it ran in.
 template <int FMT, int MB>
 __device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t* __restrict__ xs, int C, int m,
                                           float sc, float (&acc)[MB]) {
@@ -543,18 +561,23 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t
     for (int t = 0; t < MB; ++t) {
       if (t >= m) break;
       const uint4 xv = *reinterpret_cast<const uint4*>(xs + t * C + col);
-      const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
       float a = acc[t];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        a = __builtin_fmaf(bf16_lo(wd[p]), bf16_lo(xd[p]), a);
-        a = __builtin_fmaf(bf16_hi(wd[p]), bf16_hi(xd[p]), a);
-      }
+      a = dot2_bf16(wd[0], xv.x, a);
+      a = dot2_bf16(wd[1], xv.y, a);
+      a = dot2_bf16(wd[2], xv.z, a);
+      a = dot2_bf16(wd[3], xv.w, a);
       acc[t] = a;
     }
   } else if constexpr (FMT == PE_W_FP8_B128) {
-    // 16 e4m3 codes, decoded exactly by the hardware conversion (OCP e4m3fn),
-    // word by word inside the token loop to keep few values live.
+    // 16 e4m3 codes (OCP e4m3fn, hardware conversion), element pairs in order
+    uint32_t wb[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
+      wb[2 * p] = pack_bf16x2(lo[0], lo[1]);
+      wb[2 * p + 1] = pack_bf16x2(hi[0], hi[1]);
+    }
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
       if (t >= m) break;
@@ -563,19 +586,22 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t
       const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       float part = 0.0f;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
-        part = __builtin_fmaf(lo[0], bf16_lo(xd[2 * p]), part);
-        part = __builtin_fmaf(lo[1], bf16_hi(xd[2 * p]), part);
-        part = __builtin_fmaf(hi[0], bf16_lo(xd[2 * p + 1]), part);
-        part = __builtin_fmaf(hi[1], bf16_hi(xd[2 * p + 1]), part);
-      }
+      for (int p = 0; p < 8; ++p) part = dot2_bf16(wb[p], xd[p], part);
       acc[t] = __builtin_fmaf(sc, part, acc[t]);
     }
   } else {
-    // 32 nibbles; element 2i is the low nibble of byte i; value = nibble - 8
-    // (exact in fp32), decoded byte by byte inside the token loop.
+    // 32 nibbles, element 2i the low nibble of byte i; q ^ 8 read as a signed
+    // 4-bit value is q - 8, which v_cvt_off_f32_i4 turns into (q - 8) / 16
+    uint32_t wb[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tw = (int)(wd[v] ^ 0x88888888u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        wb[4 * v + b] = pack_bf16x2(__builtin_amdgcn_cvt_off_f32_i4(tw >> (8 * b)),
+                                    __builtin_amdgcn_cvt_off_f32_i4(tw >> (8 * b + 4)));
+    }
+    const float sc16 = 16.0f * sc;
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
       if (t >= m) break;
@@ -584,15 +610,12 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const uint4 xv = xp[v];
-        const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t byte = (wd[v] >> (8 * b)) & 0xFFu;
-          part = __builtin_fmaf((float)(int)(byte & 0xFu) - 8.0f, bf16_lo(xd[b]), part);
-          part = __builtin_fmaf((float)(int)(byte >> 4) - 8.0f, bf16_hi(xd[b]), part);
-        }
+        part = dot2_bf16(wb[4 * v], xv.x, part);
+        part = dot2_bf16(wb[4 * v + 1], xv.y, part);
+        part = dot2_bf16(wb[4 * v + 2], xv.z, part);
+        part = dot2_bf16(wb[4 * v + 3], xv.w, part);
       }
-      acc[t] = __builtin_fmaf(sc, part, acc[t]);
+      acc[t] = __builtin_fmaf(sc16, part, acc[t]);
     }
   }
 }
