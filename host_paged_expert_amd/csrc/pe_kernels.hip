@@ -907,61 +907,86 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, G
   down_block<FMT, MB>(a, blockIdx.x, blockIdx.y, g.LG, g.rows_per_block, lds);
 }
 
+// LDS for the gate/up scales one stream_gate_up_rows block stages (gate rows in
+// the first half, up rows in the second): at most 512 bytes each for hidden <=
+// 4096 (int4: rows_per_block * hidden / 128 fp16; FP8: one 128-row block row).
+constexpr size_t kStreamScaleLds = 1024;
+
 // Gate/up row block gi of a missing expert, paged in and projected in one pass:
 // rows i of the block (gemv_gate_up_kernel's geometry) are read from the mapped
 // host row `src`, stored into the slot `dst` and, as each 16-byte chunk arrives,
 // dotted with the expert's m token vectors (entries `ent`, staged in LDS `xs`),
-// one chunk per row in flight ahead of the arithmetic.  The lane's chunk order
-// and the reduction are those of gate_up_block, so h is bit-identical to a
-// gate/up projection read back from the slot.  FP8 / int4 scales are read from
-// the host row too.
+// one chunk per row in flight ahead of the arithmetic.  The block's FP8 / int4
+// scales are staged once through LDS `s_sc` (one contiguous read per side) and
+// stored into the slot as well.  The lane's chunk order and the reduction are
+// those of gate_up_block, so h is bit-identical to a gate/up projection read
+// back from the slot.
 template <int FMT, int MB>
 __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, const uint8_t* __restrict__ src,
                                     uint8_t* __restrict__ dst, int gi, const int* ent, int m, int off,
-                                    uint16_t* xs) {
+                                    uint16_t* xs, char* s_sc) {
   constexpr int VPC = Fmt<FMT>::VPC;
   const int H = a.H, I = a.I, n_ch = H / VPC, LG = g.LG;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int i = gi * g.rows_per_block + wv * groups + grp;    // this group's gate row; up row I + i
+  const int i0 = gi * g.rows_per_block;
+  const int i = i0 + wv * groups + grp;    // this group's gate row; up row I + i
   const bool active = i < I;
   const uint4* sg = reinterpret_cast<const uint4*>(src + a.off_w13) + (size_t)i * n_ch;
   const uint4* su = reinterpret_cast<const uint4*>(src + a.off_w13) + (size_t)(I + i) * n_ch;
   uint4* dg = reinterpret_cast<uint4*>(dst + a.off_w13) + (size_t)i * n_ch;
   uint4* du = reinterpret_cast<uint4*>(dst + a.off_w13) + (size_t)(I + i) * n_ch;
-  const float* sgf = reinterpret_cast<const float*>(src + a.off_s13) + (size_t)(i >> 7) * (H / 128);
-  const float* suf = reinterpret_cast<const float*>(src + a.off_s13) + (size_t)((I + i) >> 7) * (H / 128);
-  const uint16_t* sgh = reinterpret_cast<const uint16_t*>(src + a.off_s13) + (size_t)i * (H / 128);
-  const uint16_t* suh = reinterpret_cast<const uint16_t*>(src + a.off_s13) + (size_t)(I + i) * (H / 128);
+  // the block's scale bytes [og, og + nb) (gate) and [ou, ou + nb) (up) of the S13 region
+  size_t og = 0, ou = 0;
+  int nb = 0;
+  if constexpr (FMT == PE_W_INT4_G128) {
+    og = (size_t)i0 * (H / 128) * 2;
+    ou = (size_t)(I + i0) * (H / 128) * 2;
+    nb = min(g.rows_per_block, I - i0) * (H / 128) * 2;
+  } else if constexpr (FMT == PE_W_FP8_B128) {
+    og = (size_t)(i0 >> 7) * (H / 128) * 4;
+    ou = (size_t)((I + i0) >> 7) * (H / 128) * 4;
+    nb = (H / 128) * 4;
+  }
+  const bool store_sc = FMT == PE_W_INT4_G128 || (i0 & 127) == 0;   // one block per FP8 block row
+  const float* sgf = reinterpret_cast<const float*>(s_sc);
+  const float* suf = reinterpret_cast<const float*>(s_sc + kStreamScaleLds / 2);
+  const uint16_t* sgh = reinterpret_cast<const uint16_t*>(s_sc) + (size_t)(i - i0) * (H / 128);
+  const uint16_t* suh = reinterpret_cast<const uint16_t*>(s_sc + kStreamScaleLds / 2) + (size_t)(i - i0) * (H / 128);
   // the first token batch also stores the rows (tb == 0 runs even for m == 0)
   for (int tb = 0; tb == 0 || tb < m; tb += MB) {
     const int mb = max(0, min(MB, m - tb));
+    int c = lig;
+    uint4 wg = make_uint4(0, 0, 0, 0), wu = wg;
+    if (active && c < n_ch) { wg = sg[c]; wu = su[c]; }     // in flight during the staging
     __syncthreads();
     stage_rows(xs, a.x, H, ent + tb, mb, a.k);
+    if (FMT != PE_W_BF16 && tb == 0) {
+      const uint16_t* hs = reinterpret_cast<const uint16_t*>(src + a.off_s13);
+      uint16_t* ds = reinterpret_cast<uint16_t*>(dst + a.off_s13);
+      uint16_t* ls = reinterpret_cast<uint16_t*>(s_sc);
+      const int nu = nb / 2;
+      for (int q = threadIdx.x; q < 2 * nu; q += blockDim.x) {
+        const bool up = q >= nu;
+        const size_t at = (up ? ou : og) / 2 + (q - (up ? nu : 0));
+        const uint16_t v = hs[at];
+        ls[(up ? kStreamScaleLds / 4 : 0) + (q - (up ? nu : 0))] = v;
+        if (store_sc) ds[at] = v;
+      }
+    }
     __syncthreads();
     if (!active) continue;
     float gacc[MB], uacc[MB];
 #pragma unroll
     for (int t = 0; t < MB; ++t) { gacc[t] = 0.0f; uacc[t] = 0.0f; }
-    int c = lig;
-    uint4 wg = make_uint4(0, 0, 0, 0), wu = wg;
-    float scg = 1.0f, scu = 1.0f;
-    if (c < n_ch) {
-      wg = sg[c]; wu = su[c];
-      scg = chunk_scale<FMT>(sgf, sgh, c * VPC); scu = chunk_scale<FMT>(suf, suh, c * VPC);
-    }
     while (c < n_ch) {
       const int cn = c + LG;
       uint4 ng = make_uint4(0, 0, 0, 0), nu = ng;
-      float nsg = 1.0f, nsu = 1.0f;
-      if (cn < n_ch) {
-        ng = sg[cn]; nu = su[cn];
-        nsg = chunk_scale<FMT>(sgf, sgh, cn * VPC); nsu = chunk_scale<FMT>(suf, suh, cn * VPC);
-      }
+      if (cn < n_ch) { ng = sg[cn]; nu = su[cn]; }
       if (tb == 0) { dg[c] = wg; du[c] = wu; }
-      dot_chunk<FMT, MB>(wg, c * VPC, xs, H, mb, scg, gacc);
-      dot_chunk<FMT, MB>(wu, c * VPC, xs, H, mb, scu, uacc);
-      c = cn; wg = ng; wu = nu; scg = nsg; scu = nsu;
+      dot_chunk<FMT, MB>(wg, c * VPC, xs, H, mb, chunk_scale<FMT>(sgf, sgh, c * VPC), gacc);
+      dot_chunk<FMT, MB>(wu, c * VPC, xs, H, mb, chunk_scale<FMT>(suf, suh, c * VPC), uacc);
+      c = cn; wg = ng; wu = nu;
     }
     group_reduce<MB>(gacc, LG);
     group_reduce<MB>(uacc, LG);
@@ -971,6 +996,17 @@ __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, cons
         a.h[(size_t)(off + tb + t) * I + i] = f32_to_bf16(silu_f(gacc[t]) * uacc[t]);
     }
   }
+}
+
+// The part of an expert blob a streamed page-in copies plainly: the down
+// weights [off_w2, off_s13) and their scales [off_s2, copy_bytes) (the gate/up
+// rows and scales are stored by stream_gate_up_rows).
+__device__ __forceinline__ void copy_blob_rest(const ExpertArgs& a, const uint8_t* src, uint8_t* dst,
+                                               size_t copy_bytes, size_t gtid, size_t gstride) {
+  copy_chunks(reinterpret_cast<uint4*>(dst + a.off_w2), reinterpret_cast<const uint4*>(src + a.off_w2),
+              (a.off_s13 - a.off_w2) / 16, gtid, gstride);
+  copy_chunks(reinterpret_cast<uint4*>(dst + a.off_s2), reinterpret_cast<const uint4*>(src + a.off_s2),
+              (copy_bytes - a.off_s2) / 16, gtid, gstride);
 }
 
 // Page-in of a device-planned wave's missing experts with their gate/up
@@ -985,7 +1021,8 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
   const PlanLds L = carve_plan(lds, p.E, p.K, p.n);
   const size_t plan_b = plan_lds_bytes(p.E, p.K, p.n);
   int* s_ent = reinterpret_cast<int*>(lds + plan_b);                                    // [n]
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + plan_b + al16(4 * (size_t)p.n));     // [MB][H]
+  char* s_sc = lds + plan_b + al16(4 * (size_t)p.n);                                    // scales
+  uint16_t* xs = reinterpret_cast<uint16_t*>(s_sc + kStreamScaleLds);                   // [MB][H]
   for (int r = 0; r < n_miss; ++r) {
     int gi = ((w - (r * g.gx) % P) % P + P) % P;     // this workgroup's first block of expert r
     if (gi >= g.gx) continue;
@@ -999,15 +1036,12 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
     const int m = L.cnt[e], off = L.pref[2 * p.E + e];
     const uint8_t* src = p.host_rows + (size_t)e * p.stride;
     uint8_t* dst = p.slots + (size_t)L.victim[r] * p.stride;
-    for (; gi < g.gx; gi += P) stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, s_ent, m, off, xs);
+    for (; gi < g.gx; gi += P) stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, s_ent, m, off, xs, s_sc);
     __syncthreads();     // s_ent is rebuilt for the next expert
   }
-  const size_t rest16 = (p.copy_bytes - a.off_w2) / 16;
-  for (int r = 0; r < n_miss; ++r) {
-    const uint4* src = reinterpret_cast<const uint4*>(p.host_rows + (size_t)L.plan_e[r] * p.stride + a.off_w2);
-    uint4* dst = reinterpret_cast<uint4*>(p.slots + (size_t)L.victim[r] * p.stride + a.off_w2);
-    copy_chunks(dst, src, rest16, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
-  }
+  for (int r = 0; r < n_miss; ++r)
+    copy_blob_rest(a, p.host_rows + (size_t)L.plan_e[r] * p.stride, p.slots + (size_t)L.victim[r] * p.stride,
+                   p.copy_bytes, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
 }
 
 // Host-planned wave with no MFMA tiles, launch A: workgroups [0, P) page in the
@@ -1030,7 +1064,8 @@ __global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, Gemv
   const int32_t* hdr = a.work + a.o.hdr;
   const int split = hdr[hdr_gemv_split(a.MW, a.wave)], g1 = hdr[hdr_gemv(a.MW, a.wave + 1)];
   const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+  char* s_sc = lds;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + kStreamScaleLds);
   const int n_miss = g1 - split;
   for (int r = 0; r < n_miss; ++r) {
     int gi = ((w - (r * g.gx) % P) % P + P) % P;
@@ -1040,15 +1075,13 @@ __global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, Gemv
     const uint8_t* src = host_rows + (size_t)e * stride;
     uint8_t* dst = const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride;
     for (; gi < g.gx; gi += P)
-      stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, a.work + a.o.entries + d.y, d.z, d.y, xs);
+      stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, a.work + a.o.entries + d.y, d.z, d.y, xs, s_sc);
   }
-  const size_t rest16 = (copy_bytes - a.off_w2) / 16;
   for (int r = 0; r < n_miss; ++r) {
     const int4 d = desc[split + r];
     const int e = a.work[a.o.used_expert + d.w];
-    const uint4* src = reinterpret_cast<const uint4*>(host_rows + (size_t)e * stride + a.off_w2);
-    uint4* dst = reinterpret_cast<uint4*>(const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride + a.off_w2);
-    copy_chunks(dst, src, rest16, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
+    copy_blob_rest(a, host_rows + (size_t)e * stride, const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride,
+                   copy_bytes, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
   }
 }
 
@@ -1314,7 +1347,7 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, true);
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t copier = plan_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + (size_t)mb * a.H * 2;
+  const size_t copier = plan_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds + (size_t)mb * a.H * 2;
   const size_t lds = std::max(copier, lean_head(a) + (size_t)mb * a.H * 2);
   const int blocks = P + 1 + g.gx * items;
   PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g)));
@@ -1324,7 +1357,7 @@ void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int
                    size_t stride, size_t copy_bytes, hipStream_t s) {
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t lds = (size_t)mb * a.H * 2;
+  const size_t lds = kStreamScaleLds + (size_t)mb * a.H * 2;
   const int blocks = P + g.gx * hit_items;
   PE_DISPATCH(wtype, mb, (wave_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(a, g, P, host_rows, stride, copy_bytes)));
 }
