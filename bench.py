@@ -58,7 +58,7 @@ def parse():
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
-        pmc_summary(*sys.argv[2:5])
+        pmc_summary(*sys.argv[2:6])
         return
     args = parse()
     if args.gpus != 1:
@@ -221,18 +221,25 @@ def main():
         st2 = diff(m.stats(), before)
         if st2["page_ins"] != M or st2["distinct"] != D:
             raise RuntimeError("timing pass planned differently from the timed run")
-        w13b = 2 * wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5}[wl.wtype]
-        s13b = {"bf16": 0, "fp8": (2 * wl.inter // 128) * (wl.hidden // 128) * 4,
-                "int4": 2 * wl.inter * (wl.hidden // 128) * 2}[wl.wtype]
+        w2b = wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5}[wl.wtype]
+        s2b = {"bf16": 0, "fp8": (wl.hidden // 128) * (wl.inter // 128) * 4,
+               "int4": wl.hidden * (wl.inter // 128) * 2}[wl.wtype]
         n_pi, ms_pi = tm["page_in"]
-        n_gu, ms_gu = tm["gate_up"]
+        n_dn, ms_dn = tm["down"]
+        # the launches each stage brackets on this path
+        if device_planned:
+            pi_name, dn_name = "step_a_kernel", "down_sum_kernel"
+        elif args.dma:
+            pi_name, dn_name = "hipMemcpyAsync page-in", "gemv_down_kernel"
+        else:
+            pi_name, dn_name = "wave_a_kernel", "gemv_down_kernel"
         kernel = {
-            "page_in": {"launches": n_pi, "avg_us": 1e3 * ms_pi / max(n_pi, 1),
+            "page_in": {"name": pi_name, "launches": n_pi, "avg_us": 1e3 * ms_pi / max(n_pi, 1),
                         "bytes_per_launch": M * S_alg / max(n_pi, 1),
                         "gbs": (M * S_alg / 1e9) / (ms_pi / 1e3) if ms_pi > 0 else None},
-            "gate_up": {"launches": n_gu, "avg_us": 1e3 * ms_gu / max(n_gu, 1),
-                        "bytes_per_launch": D * (w13b + s13b) / max(n_gu, 1),
-                        "gbs": (D * (w13b + s13b) / 1e9) / (ms_gu / 1e3) if ms_gu > 0 else None},
+            "down": {"name": dn_name, "launches": n_dn, "avg_us": 1e3 * ms_dn / max(n_dn, 1),
+                     "bytes_per_launch": D * (w2b + s2b) / max(n_dn, 1),
+                     "gbs": (D * (w2b + s2b) / 1e9) / (ms_dn / 1e3) if ms_dn > 0 else None},
             "stages_ms": {k: v[1] for k, v in tm.items()},
         }
         log("stage totals (ms): %s" % ", ".join("%s %.1f" % (k, v[1]) for k, v in tm.items()))
@@ -264,19 +271,23 @@ def main():
     }
     if kernel:
         pi = kernel["page_in"]
-        result["roofline"] = {"kernel": "page_in_kernel", "bound": "link",
+        result["roofline"] = {"kernel": pi["name"], "bound": "link",
                               "achieved": round(pi["gbs"], 2) if pi["gbs"] else None,
                               "peak": round(PCIE5_X16_GBS, 2), "unit": "GB/s",
                               "frac": round(pi["gbs"] / PCIE5_X16_GBS, 4) if pi["gbs"] else None,
-                              "traffic": traffic_for(pi["bytes_per_launch"]), "avg_launch_us": round(pi["avg_us"], 2),
+                              "traffic": traffic_for(pi["name"], wl.name, alg_bytes(
+                                  pi["name"], wl.wtype, H, wl.inter, D, M, pi["launches"])),
+                              "avg_launch_us": round(pi["avg_us"], 2),
                               "launches": pi["launches"], "bytes_per_launch": round(pi["bytes_per_launch"])}
-        gu = kernel["gate_up"]
-        result["roofline_hbm"] = {"kernel": "gemv_gate_up_kernel", "bound": "hbm",
-                                  "achieved": round(gu["gbs"], 2) if gu["gbs"] else None,
+        dn = kernel["down"]
+        result["roofline_hbm"] = {"kernel": dn["name"], "bound": "hbm",
+                                  "achieved": round(dn["gbs"], 2) if dn["gbs"] else None,
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(gu["gbs"] / HBM_PEAK_GBS, 4) if gu["gbs"] else None,
-                                  "traffic": None, "avg_launch_us": round(gu["avg_us"], 2),
-                                  "launches": gu["launches"], "bytes_per_launch": round(gu["bytes_per_launch"])}
+                                  "frac": round(dn["gbs"] / HBM_PEAK_GBS, 4) if dn["gbs"] else None,
+                                  "traffic": traffic_for(dn["name"], wl.name, alg_bytes(
+                                      dn["name"], wl.wtype, H, wl.inter, D, M, dn["launches"])),
+                                  "avg_launch_us": round(dn["avg_us"], 2),
+                                  "launches": dn["launches"], "bytes_per_launch": round(dn["bytes_per_launch"])}
         result["stages_ms"] = {k: round(v, 2) for k, v in kernel["stages_ms"].items()}
 
     if has_prefill:
@@ -388,34 +399,46 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
     return cpu, parity
 
 
-def page_in_source_hash():
-    """Hash of the page-in kernel's source (its copy routine, the kernel and their
-    launch constants): memory-traffic counters stay valid while it is unchanged."""
+PMC_KERNELS = ("step_a_kernel", "down_sum_kernel", "wave_a_kernel", "gemv_down_kernel", "page_in_kernel")
+
+
+def source_hash():
+    """Hash of the library's kernel and orchestration sources: memory-traffic
+    counters taken on one build stay valid only while this is unchanged."""
+    import glob
     import hashlib
-    import re
-    src = open(os.path.join(ROOT, "host_paged_expert_amd", "csrc", "pe_kernels.hip")).read()
-    api = open(os.path.join(ROOT, "host_paged_expert_amd", "csrc", "pe_api.cpp")).read()
-
-    def body(name):
-        i = src.index(name)
-        start = src.rfind("\n\n", 0, i) + 2
-        depth, j = 0, src.index("{", i)
-        for k in range(j, len(src)):
-            depth += {"{": 1, "}": -1}.get(src[k], 0)
-            if depth == 0:
-                return src[start:k + 1]
-        raise ValueError(name)
-    consts = re.findall(r"constexpr int kCopy\w+ = \d+;", src) + re.findall(r"constexpr int kPageInGrid = \d+;", api)
-    text = body("__device__ __forceinline__ void copy_chunks(") + body("void page_in_kernel(") + "".join(consts)
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "host_paged_expert_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def pmc_summary(fetch_csv, write_csv, out_json):
-    """Per-launch memory traffic of the page-in kernel from two rocprofv3 --pmc
-    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
-    counter reads for a plain 256 MiB device-to-device copy (--copy-reference 256),
-    relative to the planned bytes (page-ins x expert bytes / launches) of that run,
-    which the run's log line gives."""
+def alg_bytes(kernel, wtype, hidden, inter, D, M, launches):
+    """Algorithmic memory bytes (reads + writes) per launch of a kernel over a
+    window with D distinct and M paged-in experts: the page-in launches read M
+    expert blobs over the link, write them into slots and read the resident
+    experts' gate/up weights; the down launches read every distinct expert's
+    down weights.  Activations (< 1%) are left out."""
+    S = {"bf16": 2, "fp8": 1, "int4": 0.5}[wtype]
+    w13, w2 = 2 * inter * hidden * S, inter * hidden * S
+    s13 = {"bf16": 0, "fp8": (2 * inter // 128) * (hidden // 128) * 4, "int4": 2 * inter * (hidden // 128) * 2}[wtype]
+    s2 = {"bf16": 0, "fp8": (hidden // 128) * (inter // 128) * 4, "int4": hidden * (inter // 128) * 2}[wtype]
+    blob = w13 + w2 + s13 + s2
+    if kernel in ("step_a_kernel", "wave_a_kernel"):
+        tot = 2 * M * blob + (D - M) * (w13 + s13)
+    elif kernel == "page_in_kernel":
+        tot = 2 * M * blob
+    else:
+        tot = D * (w2 + s2)
+    return tot / max(launches, 1)
+
+
+def pmc_summary(fetch_csv, write_csv, bench_json, out_json):
+    """Per-launch memory traffic of the path's kernels from two rocprofv3 --pmc
+    runs of the same bench command (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for a plain 256 MiB
+    device-to-device copy run first (--copy-reference 256), against the
+    algorithmic bytes of that run's window (bench_json: its JSON line)."""
     import collections
     import csv
 
@@ -428,35 +451,39 @@ def pmc_summary(fetch_csv, write_csv, out_json):
     ref = 256 * 1024.0
     fs = ref / max(f["__amd_rocclr_copyBuffer"])
     ws = ref / max(w["__amd_rocclr_copyBuffer"])
-    key = [k for k in f if "page_in_kernel" in k][0]
-    rd = sum(f[key]) / len(f[key]) * fs
-    wr = sum(w[key]) / len(w[key]) * ws
-    log_lines = open(fetch_csv.replace(".csv", ".log")).read()
-    import re
-    m = re.search(r"(\d+) page-ins", log_lines)
-    page_ins = int(m.group(1))
-    alg = page_ins * int(re.search(r"expert_bytes\D+(\d+)", open(fetch_csv.replace(".csv", ".json")).read()).group(1)) \
-        / len(f[key]) / 1024.0
-    out = {"page_in_kernel": {"source_sha256_16": page_in_source_hash(), "fetch_scale": round(fs, 4),
-                              "write_scale": round(ws, 4), "read_kib_per_launch": round(rd, 1),
-                              "write_kib_per_launch": round(wr, 1),
-                              "algorithmic_kib_per_launch_each_way": round(alg, 1),
-                              "traffic_over_algorithmic": round((rd + wr) / (2 * alg), 4),
-                              "launches": len(f[key]), "page_ins": page_ins}}
+    run = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    cfg, win = run["config"], run["window"]
+    out = {"source_sha256_16": source_hash(), "workload": cfg["workload"], "fetch_scale": round(fs, 4),
+           "write_scale": round(ws, 4), "window": {"distinct": win["distinct"], "page_ins": win["page_ins"]},
+           "kernels": {}}
+    for name in PMC_KERNELS:
+        keys = [k for k in f if name in k]
+        if not keys:
+            continue
+        fv = [v for k in keys for v in f[k]]
+        wv = [v for k in keys for v in w.get(k, [])]
+        rd = sum(fv) / len(fv) * fs * 1024
+        wr = sum(wv) / max(len(wv), 1) * ws * 1024
+        alg = alg_bytes(name, cfg["wtype"], cfg["hidden"], cfg["inter"], win["distinct"], win["page_ins"], len(fv))
+        out["kernels"][name] = {"launches": len(fv), "read_bytes_per_launch": round(rd),
+                                "write_bytes_per_launch": round(wr), "alg_bytes_per_launch": round(alg),
+                                "traffic_over_alg": round((rd + wr) / alg, 4) if alg else None}
     json.dump(out, open(out_json, "w"), indent=1)
     print(json.dumps(out, indent=1))
 
 
-def traffic_for(bytes_per_launch):
-    """Read+write bytes per page-in launch implied by the committed counter
-    summary, or None if the page-in kernel changed since it was taken."""
+def traffic_for(kernel, workload, alg_per_launch):
+    """Read + write bytes per launch implied by the committed counter summary
+    for this workload (its traffic / algorithmic ratio times this run's
+    algorithmic bytes), or None if there is none or the sources changed."""
     try:
-        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["page_in_kernel"]
-    except (OSError, KeyError, ValueError):
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)))
+    except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != page_in_source_hash():
+    k = t.get("kernels", {}).get(kernel)
+    if not k or t.get("source_sha256_16") != source_hash() or not k.get("traffic_over_alg"):
         return None
-    return round(2 * bytes_per_launch * t["traffic_over_algorithmic"])
+    return round(alg_per_launch * k["traffic_over_alg"])
 
 
 def cpu_model():
