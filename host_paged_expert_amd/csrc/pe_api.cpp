@@ -483,7 +483,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
     // branches on other hardware queues, whose cross-queue dependencies cost more
     // than they hide).  No host synchronisation: capturable.
     const int items = std::min(n, d.K);
-    if (!c->unpaged && mfma_min == pe::kNoMfma) {
+    if (!c->unpaged && mfma_min == pe::kNoMfma && d.E <= 256) {
       // Launch A: planning + page-in workgroups (each makes the same LRU decision
       // in LDS from the current state copy; one publishes it and writes the new
       // state into the other copy) that compute the missing experts' gate/up

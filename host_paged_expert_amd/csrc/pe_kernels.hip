@@ -313,17 +313,47 @@ __device__ int plan_page_in_block(const PlanArgs& p, int block, int ncopy, char*
   __syncthreads();
   const int n_miss = s_tot[0], D = s_tot[1], n_valid = s_tot[2];
   const int g_hit = s_tot[3], n_gemv = s_tot[3] + s_tot[4], t_hit = s_tot[5], n_tiles = s_tot[5] + s_tot[6];
-  // Victims by ascending (last_use, slot): rank = candidates ordered before j.
-  for (int j = tid; j < K; j += kPlanThreads) {
-    if (!s_cand[j]) continue;
-    const unsigned lj = s_lu[j];
-    int r = 0;
-#pragma unroll 8
-    for (int q = 0; q < K; ++q) {     // branch-free, so the LDS reads pipeline
-      const unsigned lq = s_lu[q];
-      r += (int)s_cand[q] & ((int)(lq < lj) | ((int)(lq == lj) & (int)(q < j)));
+  // Victims: the n_miss evictable slots of smallest (last_use, slot).  Up to 256
+  // slots, wavefront 0 selects them in registers, one per round: the wavefront
+  // minimum of 64-bit keys (last_use << 32 | slot) by an xor butterfly, which its
+  // owner lane then retires.  Larger tables rank every candidate against all.
+  if (K <= 4 * 64) {
+    if (wv == 0 && n_miss > 0) {
+      unsigned long long key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = lane + 64 * q;
+        key[q] = (j < K && s_cand[j]) ? ((unsigned long long)s_lu[j] << 32 | (unsigned)j) : ~0ull;
+      }
+      for (int r = 0; r < n_miss; ++r) {
+        unsigned long long m = key[0] < key[1] ? key[0] : key[1];
+        const unsigned long long m2 = key[2] < key[3] ? key[2] : key[3];
+        m = m < m2 ? m : m2;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          const unsigned long long o = __shfl_xor(m, off, 64);
+          m = o < m ? o : m;
+        }
+        const int j = (int)(unsigned)(m & 0xFFFFFFFFull);
+        if (lane == 0) s_victim[r] = j;
+        if (lane == (j & 63)) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == (j >> 6)) key[q] = ~0ull;
+        }
+      }
     }
-    if (r < n_miss) s_victim[r] = j;
+  } else {
+    for (int j = tid; j < K; j += kPlanThreads) {
+      if (!s_cand[j]) continue;
+      const unsigned lj = s_lu[j];
+      int r = 0;
+      for (int q = 0; q < K; ++q) {
+        const unsigned lq = s_lu[q];
+        r += (int)s_cand[q] & ((int)(lq < lj) | ((int)(lq == lj) & (int)(q < j)));
+      }
+      if (r < n_miss) s_victim[r] = j;
+    }
   }
   __syncthreads();
   // Place the i-th missing expert (ascending id) into the i-th victim.
@@ -410,6 +440,119 @@ __device__ int plan_page_in_block(const PlanArgs& p, int block, int ncopy, char*
     }
   }
   return n_miss;
+}
+
+// LDS of the copiers' planner (copier_plan), sized by E experts, K slots and n
+// entries.
+struct CopierLds {
+  int *es, *cnt, *se;
+  unsigned* lu;
+  int *ids, *plan_e, *victim, *off, *nm;
+};
+
+constexpr size_t copier_lds_bytes(int E, int K, int n) {
+  return 2 * al16(4 * (size_t)E) + 5 * al16(4 * (size_t)K) + al16(4 * (size_t)n) + 16;
+}
+
+__device__ __forceinline__ CopierLds carve_copier(char* p, int E, int K, int n) {
+  CopierLds L;
+  L.es = reinterpret_cast<int*>(p); p += al16(4 * (size_t)E);
+  L.cnt = reinterpret_cast<int*>(p); p += al16(4 * (size_t)E);
+  L.se = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.lu = reinterpret_cast<unsigned*>(p); p += al16(4 * (size_t)K);
+  L.plan_e = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.victim = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.off = reinterpret_cast<int*>(p); p += al16(4 * (size_t)K);
+  L.ids = reinterpret_cast<int*>(p); p += al16(4 * (size_t)n);
+  L.nm = reinterpret_cast<int*>(p);
+  return L;
+}
+
+// The part of a device-planned wave's plan that a copier workgroup needs, made
+// by one wavefront from the current state copy: the missing experts in
+// ascending id (plan_e), the first sorted position of each (off: the prefix of
+// entry counts over experts by id, where the planner puts its entries) and its
+// victim slot (victim) -- the decisions plan_page_in_block makes, without the
+// work lists, counters and new state that the publishing workgroup writes.
+// Victims are the evictable slots (empty, or holding an expert outside the
+// wave) of smallest (last_use, slot), one per round: the wavefront minimum of
+// 64-bit keys by an xor butterfly, retired by its owner lane.  Needs E, K <=
+// 256.  Returns the number of missing experts.
+__device__ int copier_plan(const PlanArgs& p, char* lds) {
+  const int E = p.E, K = p.K, n = p.n;
+  const Offsets& o = p.o;
+  const int32_t* __restrict__ blk = p.blk;
+  const CopierLds L = carve_copier(lds, E, K, n);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // one round of global loads: current-copy index, both state copies, the ids
+  const int32_t* st0 = blk + o.state0;
+  const int32_t* st1 = blk + o.state0 + o.state_stride;
+  const int cur = blk[o.cur] & 1;
+  const int id = tid < n ? p.ids[tid] : -1;      // n <= K <= 256 = blockDim.x
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int a0 = st0[o.expert_slot + e], a1 = st1[o.expert_slot + e];
+    L.es[e] = cur ? a1 : a0;
+    L.cnt[e] = 0;
+  }
+  for (int j = tid; j < K; j += blockDim.x) {
+    const int a0 = st0[o.slot_expert + j], a1 = st1[o.slot_expert + j];
+    const int b0 = st0[o.last_use + j], b1 = st1[o.last_use + j];
+    L.se[j] = cur ? a1 : a0;
+    L.lu[j] = (unsigned)(cur ? b1 : b0);
+  }
+  __syncthreads();
+  if (tid < n) {
+    const bool ok = id >= 0 && id < E;
+    L.ids[tid] = ok ? id : -1;
+    if (ok) atomicAdd(&L.cnt[id], 1);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    int nm = 0, base = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {                  // experts 64q + lane, ascending
+      const int e = 64 * q + lane;
+      const int c = e < E ? L.cnt[e] : 0;
+      const bool miss = c > 0 && L.es[e] < 0;
+      const int inc = wave_incl_scan(c, lane);
+      const unsigned long long mask = __ballot(miss);
+      if (miss) {
+        const int r = nm + __popcll(mask & ((1ull << lane) - 1ull));
+        L.plan_e[r] = e;
+        L.off[r] = base + inc - c;
+      }
+      nm += __popcll(mask);
+      base += __shfl(inc, 63, 64);
+    }
+    unsigned long long key[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = lane + 64 * q;
+      const int occ = j < K ? L.se[j] : 0;
+      const bool cand = j < K && (occ < 0 || L.cnt[occ] == 0);
+      key[q] = cand ? ((unsigned long long)L.lu[j] << 32 | (unsigned)j) : ~0ull;
+    }
+    for (int r = 0; r < nm; ++r) {
+      unsigned long long m = key[0] < key[1] ? key[0] : key[1];
+      const unsigned long long m2 = key[2] < key[3] ? key[2] : key[3];
+      m = m < m2 ? m : m2;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long v = __shfl_xor(m, off, 64);
+        m = v < m ? v : m;
+      }
+      const int j = (int)(unsigned)(m & 0xFFFFFFFFull);
+      if (lane == 0) L.victim[r] = j;
+      if (lane == (j & 63)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q == (j >> 6)) key[q] = ~0ull;
+      }
+    }
+    if (lane == 0) *L.nm = nm;
+  }
+  __syncthreads();
+  return *L.nm;
 }
 
 // Page-in of a planned wave: the r-th missing expert's blob into its victim
@@ -764,11 +907,13 @@ __device__ __forceinline__ size_t gemv_lds_head(const ExpertArgs& a) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Gate/up projection + SwiGLU of one workgroup: used expert `by`, intermediate
-// rows from bx * rows_per_block; every lane group takes one row i and computes
-// h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).  The weight loads of both rows are
-// issued before the token vectors are staged in LDS.
-template <int FMT, int MB>
+// Gate/up projection + SwiGLU of one workgroup: used expert `by`, NR blocks of
+// intermediate rows from bx * NR * rows_per_block; every lane group takes one
+// row i of each block and computes h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).
+// The weight loads of all the group's rows are issued before the token vectors
+// are staged in LDS.  NR only changes how many rows a workgroup covers, not a
+// row's arithmetic.
+template <int FMT, int MB, int NR = 1>
 __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds) {
   GemvItem it;
   if (!gemv_item(a, by, it, lds)) return;
@@ -782,40 +927,51 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
   const uint16_t* S13h = reinterpret_cast<const uint16_t*>(blob + a.off_s13);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int i = bx * rows_per_block + wv * groups + grp;    // this group's row
-  const bool active = i < I;
-  const int ru = I + i;
-  const uint4* rg = W13 + (size_t)i * n_ch;
-  const uint4* rup = W13 + (size_t)ru * n_ch;
+  int i[NR];
+  bool active[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    i[r] = (bx * NR + r) * rows_per_block + wv * groups + grp;    // this group's rows
+    active[r] = i[r] < I;
+  }
   const int32_t* ent = it.ent;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
-    uint4 wg[kMaxChunksInFlight], wu[kMaxChunksInFlight];
-    if (active) { load_row(rg, n_ch, lig, LG, wg); load_row(rup, n_ch, lig, LG, wu); }
+    uint4 wg[NR][kMaxChunksInFlight], wu[NR][kMaxChunksInFlight];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (active[r]) {
+        load_row(W13 + (size_t)i[r] * n_ch, n_ch, lig, LG, wg[r]);
+        load_row(W13 + (size_t)(I + i[r]) * n_ch, n_ch, lig, LG, wu[r]);
+      }
     __syncthreads();
     stage_rows(xs, a.x, H, ent + tb, mb, a.k);
     __syncthreads();
-    if (!active) continue;
-    float g[MB], u[MB];
 #pragma unroll
-    for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
-    const float* sgf = S13f + (size_t)(i >> 7) * (H / 128);
-    const float* suf = S13f + (size_t)(ru >> 7) * (H / 128);
-    const uint16_t* sgh = S13h + (size_t)i * (H / 128);
-    const uint16_t* suh = S13h + (size_t)ru * (H / 128);
-    for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
-      dot_row<FMT, MB>(wg, n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
-      dot_row<FMT, MB>(wu, n_ch, c0, LG, xs, H, mb, suf, suh, u);
-      if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
-      load_row(rg, n_ch, c0 + LG * kMaxChunksInFlight, LG, wg);
-      load_row(rup, n_ch, c0 + LG * kMaxChunksInFlight, LG, wu);
-    }
-    group_reduce<MB>(g, LG);
-    group_reduce<MB>(u, LG);
+    for (int r = 0; r < NR; ++r) {
+      if (!active[r]) continue;
+      const int ir = i[r], ru = I + ir;
+      float g[MB], u[MB];
 #pragma unroll
-    for (int t = 0; t < MB; ++t) {
-      if (t < mb && lig == t)
-        a.h[(size_t)(it.off + tb + t) * I + i] = f32_to_bf16(silu_f(g[t]) * u[t]);
+      for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
+      const float* sgf = S13f + (size_t)(ir >> 7) * (H / 128);
+      const float* suf = S13f + (size_t)(ru >> 7) * (H / 128);
+      const uint16_t* sgh = S13h + (size_t)ir * (H / 128);
+      const uint16_t* suh = S13h + (size_t)ru * (H / 128);
+      for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
+        dot_row<FMT, MB>(wg[r], n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
+        dot_row<FMT, MB>(wu[r], n_ch, c0, LG, xs, H, mb, suf, suh, u);
+        if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
+        load_row(W13 + (size_t)ir * n_ch, n_ch, c0 + LG * kMaxChunksInFlight, LG, wg[r]);
+        load_row(W13 + (size_t)ru * n_ch, n_ch, c0 + LG * kMaxChunksInFlight, LG, wu[r]);
+      }
+      group_reduce<MB>(g, LG);
+      group_reduce<MB>(u, LG);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        if (t < mb && lig == t)
+          a.h[(size_t)(it.off + tb + t) * I + ir] = f32_to_bf16(silu_f(g[t]) * u[t]);
+      }
     }
   }
 }
@@ -1018,8 +1174,8 @@ __device__ __forceinline__ void copy_blob_rest(const ExpertArgs& a, const uint8_
 template <int FMT, int MB>
 __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom& g, int w, int P, char* lds,
                           int n_miss) {
-  const PlanLds L = carve_plan(lds, p.E, p.K, p.n);
-  const size_t plan_b = plan_lds_bytes(p.E, p.K, p.n);
+  const CopierLds L = carve_copier(lds, p.E, p.K, p.n);
+  const size_t plan_b = copier_lds_bytes(p.E, p.K, p.n);
   int* s_ent = reinterpret_cast<int*>(lds + plan_b);                                    // [n]
   char* s_sc = lds + plan_b + al16(4 * (size_t)p.n);                                    // scales
   uint16_t* xs = reinterpret_cast<uint16_t*>(s_sc + kStreamScaleLds);                   // [MB][H]
@@ -1033,7 +1189,7 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
       for (int q = 0; q < i; ++q) rank += L.ids[q] == e;
       s_ent[rank] = i;
     }
-    const int m = L.cnt[e], off = L.pref[2 * p.E + e];
+    const int m = L.cnt[e], off = L.off[r];
     const uint8_t* src = p.host_rows + (size_t)e * p.stride;
     uint8_t* dst = p.slots + (size_t)L.victim[r] * p.stride;
     for (; gi < g.gx; gi += P) stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, s_ent, m, off, xs, s_sc);
@@ -1085,21 +1241,26 @@ __global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, Gemv
   }
 }
 
-// Device-planned step with no many-token expert, launch A: workgroups [0, P)
-// plan the wave and page in its missing experts with their gate/up projection
-// (stream_in); workgroup P plans it and publishes the plan, the new LRU state,
-// the work lists and the counters; the rest run the gate/up projection of the
-// experts that were already resident (lean discovery, `a.lean` set).  No
-// workgroup waits for another.
+// Device-planned step with no many-token expert (E, K <= 256), launch A:
+// workgroups [0, P) make the copiers' part of the plan (copier_plan) and page in
+// the wave's missing experts with their gate/up projection (stream_in);
+// workgroup P makes the whole plan and publishes it (plan, new LRU state, work
+// lists, counters); the rest run the gate/up projection of the experts that were
+// already resident (lean discovery, `a.lean` set).  Every planning workgroup
+// decides from the same state copy by the same rules, and no workgroup waits
+// for another.
 template <int FMT, int MB>
 __global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs a, GemvGeom g) {
   extern __shared__ __align__(16) char lds[];
-  if ((int)blockIdx.x <= P) {
-    const int n_miss = plan_page_in_block(p, blockIdx.x, P, lds);
-    if ((int)blockIdx.x < P) stream_in<FMT, MB>(p, a, g, blockIdx.x, P, lds, n_miss);
+  if ((int)blockIdx.x < P) {
+    stream_in<FMT, MB>(p, a, g, blockIdx.x, P, lds, copier_plan(p, lds));
+  } else if ((int)blockIdx.x == P) {
+    plan_page_in_block(p, P, P, lds);
   } else {
+    // two row blocks per workgroup, so every workgroup of the launch is resident at once
+    const int gx2 = (g.gx + 1) / 2;
     const int b = blockIdx.x - P - 1;
-    gate_up_block<FMT, MB>(a, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
+    gate_up_block<FMT, MB, 2>(a, b % gx2, b / gx2, g.LG, g.rows_per_block, lds);
   }
 }
 
@@ -1183,11 +1344,11 @@ __device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 d
 // Device-planned step, launch B: the down projection of every expert of the
 // wave and the fixed-order top-k sum, by output rows.  Workgroup b owns the RB
 // rows [b*RB, b*RB + RB) that one wavefront covers in gemv_down_kernel's
-// geometry (two rows per lane group).  Its NW (4..8) wavefronts take the wave's
-// GEMV experts round-robin; each issues the weight loads of its first expert
-// (its descriptor is one load away) before the workgroup stages the step's h
-// rows (if STAGE) and routed ids in LDS, and the loads of its next expert
-// before it computes the current one.  Every entry's w[e] * (W2
+// geometry (two rows per lane group).  Its NW (1..8) wavefronts take the
+// wave's GEMV experts round-robin; each issues the weight loads of its first
+// two experts (their descriptors are one load away) before the workgroup stages
+// the step's h rows (if STAGE) and routed ids in LDS, and a later expert's as
+// soon as a register set is free.  Every entry's w[e] * (W2
 // h)[row] goes to LDS; then each token's k entries are summed in j order
 // (invalid ids skipped) and rounded once to bf16: the arithmetic of down_block +
 // topk_sum_rows.  Workgroup 0 makes the new LRU-state copy current.
@@ -1209,12 +1370,16 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uin
   const int n_items = hdr[hdr_gemv(a.MW, 1)];               // wave 0's GEMV items start at 0
   const int n0 = r0 + 2 * grp;
   const bool act0 = n0 < H, act1 = n0 + 1 < H;
-  // this wavefront's experts it, it + NW, ...: the next one's first round of
-  // weight loads is in flight while the current one is computed
-  int it = wv;
-  int4 d = it < a.E ? desc[it] : make_int4(0, 0, 0, 0);
-  DownRows rA, rB;      // ping-pong buffers (named, so they stay in registers)
-  if (it < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
+  // this wavefront's experts wv, wv + NW, wv + 2 NW, ...: the first two experts'
+  // first rounds of weight loads are issued before the staging, and each later
+  // one's as soon as its buffer is free (ping-pong between two named register
+  // sets)
+  int i0 = wv, i1 = wv + NW;
+  int4 d0 = i0 < a.E ? desc[i0] : make_int4(0, 0, 0, 0);
+  int4 d1 = i1 < a.E ? desc[i1] : make_int4(0, 0, 0, 0);
+  DownRows rA, rB;
+  if (i0 < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d0.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
+  if (i1 < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d1.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
   for (int i = threadIdx.x; i < n; i += blockDim.x) s_id[i] = a.ids[i];
   if constexpr (STAGE) {
     const int n16 = n * I / 8;
@@ -1223,25 +1388,20 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uin
   }
   __syncthreads();
   const uint16_t* hbase = STAGE ? s_h : a.h;
-  while (it < n_items) {
-    int nx = it + NW;
-    int4 dn = make_int4(0, 0, 0, 0);
-    if (nx < n_items) {
-      dn = desc[nx];
-      fetch_down_rows<FMT>(a, a.slots + (size_t)dn.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
+  while (i0 < n_items) {
+    down_rows_item<FMT, MB>(a, d0, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
+    i0 += 2 * NW;
+    if (i0 < n_items) {
+      d0 = desc[i0];
+      fetch_down_rows<FMT>(a, a.slots + (size_t)d0.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
     }
-    down_rows_item<FMT, MB>(a, d, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
-    it = nx;
-    d = dn;
-    if (it >= n_items) break;
-    nx = it + NW;
-    if (nx < n_items) {
-      dn = desc[nx];
-      fetch_down_rows<FMT>(a, a.slots + (size_t)dn.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
+    if (i1 >= n_items) break;
+    down_rows_item<FMT, MB>(a, d1, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
+    i1 += 2 * NW;
+    if (i1 < n_items) {
+      d1 = desc[i1];
+      fetch_down_rows<FMT>(a, a.slots + (size_t)d1.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
     }
-    down_rows_item<FMT, MB>(a, d, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
-    it = nx;
-    d = dn;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < T * RB; idx += blockDim.x) {
@@ -1347,9 +1507,9 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, true);
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t copier = plan_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds + (size_t)mb * a.H * 2;
-  const size_t lds = std::max(copier, lean_head(a) + (size_t)mb * a.H * 2);
-  const int blocks = P + 1 + g.gx * items;
+  const size_t copier = copier_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds + (size_t)mb * a.H * 2;
+  const size_t lds = std::max(std::max(copier, plan_lds_bytes(d.E, d.K, n)), lean_head(a) + (size_t)mb * a.H * 2);
+  const int blocks = P + 1 + (g.gx + 1) / 2 * items;
   PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g)));
 }
 
@@ -1367,11 +1527,15 @@ void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, i
   const int LG = lanes_per_row(a.I / vpc_of(wtype));
   const int RB = 2 * (64 / LG);
   const int n = a.T * a.k;
-  // one wavefront per expert the wave can hold, 4..8
-  const int nw = std::max(4, std::min(8, n));
+  // wavefronts per workgroup: about two experts each, at most 8, and no more
+  // than keep every workgroup of the launch resident at once (about 2048
+  // wavefronts of this kernel's size on 256 CUs)
+  const int grid_x = ceil_div(a.H, RB);
+  const int items = std::min(n, a.E);
+  const int nw = std::max(1, std::min(std::min(8, ceil_div(items, 2)), std::max(1, 2048 / grid_x)));
   const size_t head = al16(4 * (size_t)n * RB) + al16(4 * (size_t)n);
   const size_t staged = head + (size_t)n * a.I * 2;
-  const dim3 grid(ceil_div(a.H, RB)), block(64 * nw);
+  const dim3 grid(grid_x), block(64 * nw);
   if (staged <= 64 * 1024) {
     PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, true><<<grid, block, staged, s>>>(a, LG, out, flip)));
   } else {
