@@ -10,8 +10,9 @@
  * least recently used experts outside the wave and copying in the missing
  * ones, runs the SwiGLU expert FFN over the wave's own entries (each
  * (token, expert) output already multiplied by its router weight, no top-k
- * sum), writes every entry once into a merged buffer, and finally applies
- * one fixed-order top-k sum.  The output equals the unpaged layer's.
+ * sum), keeps every entry once (per block of output rows in LDS on a
+ * device-planned step, in a merged buffer on a host-planned one), and finally
+ * applies one fixed-order top-k sum.  The output equals the unpaged layer's.
  *
  * Conventions for every entry point:
  *   - Return 0 (PE_OK) on success or a negative PE_ERR_* code; no exception
@@ -126,9 +127,10 @@ int pe_load_expert(pe_ctx* ctx, int layer, int expert,
  * If T*k <= K (and PE_FLAG_FORCE_HOST_PLAN is off) the step is one wave
  * planned on the device with no host synchronisation ("Captured decode" on
  * the docs page), so the call may be captured into a hipGraph.  Otherwise
- * the host reads the ids and the layer's LRU state back (one stream
- * synchronisation), plans the waves and enqueues them; under stream capture
- * that path returns PE_ERR_NOT_CAPTURABLE without enqueuing anything.
+ * the host reads the ids back, and the layer's LRU state unless a host-planned
+ * step was the last to change it (one stream synchronisation), plans the
+ * waves and enqueues them; under stream capture that path returns
+ * PE_ERR_NOT_CAPTURABLE without enqueuing anything.
  * Entries whose id is outside [0, E) contribute 0 and are counted in
  * pe_stats.bad_ids. */
 int pe_forward(pe_ctx* ctx, int layer, const void* x, const int32_t* topk_ids,
@@ -201,11 +203,15 @@ int pe_plan_host(int num_experts, int num_resident, int top_k, int T, const int3
                  int32_t* evicted, int32_t* slot_of);
 
 /* ---- measurement ------------------------------------------------------ */
-#define PE_STAGE_PLAN     0   /* device LRU planner                        */
-#define PE_STAGE_PAGE_IN  1   /* page-in (kernel or DMA copies)            */
-#define PE_STAGE_GATE_UP  2   /* gate/up projection + SwiGLU               */
-#define PE_STAGE_DOWN     3   /* down projection x router weight           */
-#define PE_STAGE_TOPK_SUM 4   /* fixed-order top-k sum                     */
+#define PE_STAGE_PLAN     0   /* (unused: planning runs inside PAGE_IN)             */
+#define PE_STAGE_PAGE_IN  1   /* the launch that plans (device-planned) and pages in
+                                 the missing experts with their gate/up projection
+                                 while the resident ones run theirs; or a wave's
+                                 page-in kernel / DMA copies                     */
+#define PE_STAGE_GATE_UP  2   /* separate gate/up launches (MFMA and unpaged paths) */
+#define PE_STAGE_DOWN     3   /* down projection x router weight (with the top-k
+                                 sum on a device-planned step)                   */
+#define PE_STAGE_TOPK_SUM 4   /* separate fixed-order top-k sum launch            */
 #define PE_NUM_STAGES     5
 
 /* While enabled, pe_forward brackets each stage's launches with a pair of
