@@ -32,7 +32,11 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
   uint32_t* last_use = reinterpret_cast<uint32_t*>(st + ll.last_use);
   int32_t* slot_of = blk + ll.slot_of;
 
-  std::vector<int> cnt(E, 0);
+  // scratch kept per thread: a host-planned step runs on the caller's thread
+  thread_local std::vector<int> cnt, order, u_of, in_wave, seen, wave;
+  thread_local std::vector<std::pair<uint32_t, int>> cand;
+  thread_local std::vector<char> hit, was_hit;
+  cnt.assign(E, 0);
   int bad = 0, valid = 0;
   for (int i = 0; i < n_entries; ++i) {
     int e = ids[i];
@@ -40,7 +44,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     ++cnt[e];
     ++valid;
   }
-  std::vector<int> order;
+  order.clear();
   for (int e = 0; e < E; ++e) if (cnt[e] && expert_slot[e] >= 0) order.push_back(e);
   for (int e = 0; e < E; ++e) if (cnt[e] && expert_slot[e] < 0) order.push_back(e);
   const int D = (int)order.size();
@@ -57,8 +61,8 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
   int32_t* tile_row = work + wl.tile_row;
   int32_t* entries = work + wl.entries;
 
-  std::vector<int> u_of(E, -1), in_wave(E, -1);
-  std::vector<std::pair<uint32_t, int>> cand;
+  u_of.assign(E, -1);
+  in_wave.assign(E, -1);
   int u = 0, off = 0, ng = 0, nt = 0, page_ins = 0, max_gemv = 0;
   hdr[0] = n_waves;
   hdr[hdr_wave_u(MW, 0)] = 0;
@@ -78,7 +82,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     int32_t* pe_ = blk + ll.plan_expert + (size_t)w * K;
     int32_t* ps_ = blk + ll.plan_slot + (size_t)w * K;
     int32_t* pv_ = blk + ll.plan_evicted + (size_t)w * K;
-    std::vector<char> hit(n);
+    hit.assign(n, 0);
     for (int i = 0; i < n; ++i) hit[i] = expert_slot[order[b + i]] >= 0;
     for (int i = 0; i < n; ++i) {
       int e = order[b + i];
@@ -97,8 +101,8 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     ++tick;
     // used experts of this wave, ascending id; GEMV items and MFMA tiles list the
     // experts resident before the wave first, then the ones paged in
-    std::vector<int> wave(order.begin() + b, order.begin() + b + n);
-    std::vector<char> was_hit(E, 0);
+    wave.assign(order.begin() + b, order.begin() + b + n);
+    was_hit.assign(E, 0);
     for (int i = 0; i < n; ++i) was_hit[order[b + i]] = hit[i];
     std::sort(wave.begin(), wave.end());
     int g0 = ng, t0 = nt;
@@ -139,7 +143,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
   }
   used_off[u] = off;
   // entries in ascending index at their expert's positions; slot map at wave time
-  std::vector<int> seen(E, 0);
+  seen.assign(E, 0);
   for (int i = 0; i < n_entries; ++i) {
     int e = ids[i];
     if (e < 0 || e >= E) { slot_of[i] = -1; continue; }

@@ -136,6 +136,23 @@ def test_small_formats_paged_vs_oracle_and_unpaged(wtype, batch, K):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("batch", [2, 9])
+def test_many_experts_take_the_general_planner(batch):
+    """E above 256 (the copiers' one-wavefront planner covers E <= 256): the
+    device-planned step (batch*k <= K) runs the general planner + page-in +
+    expert kernels, the host-planned one (batch*k > K) its usual waves."""
+    wl = synth.workload("decode_bf16_k40_b1", layers=2, experts=320, top_k=4, resident=24, hidden=256, inter=256,
+                        batch=batch, steps=6)
+    print("case E=320 batch %d" % batch, flush=True)
+    got, st = _run_decode(wl)
+    if batch * wl.top_k <= wl.resident:
+        assert st["device_planned"] == wl.steps * wl.layers
+    else:
+        assert st["host_planned"] == wl.steps * wl.layers
+    ref, _ = _run_decode(wl, flags=pe.PE_FLAG_UNPAGED, check_oracle=False)
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("wtype", ["bf16", "int4"])
 def test_ragged_shapes(wtype):
     """Row lengths that leave lanes idle and token batches past the GEMV batch."""
