@@ -50,6 +50,11 @@ def parse():
                     help="profiling: run device-planned steps without the hipGraph (per-dispatch counters)")
     ap.add_argument("--layers", type=int, default=None,
                     help="profiling: fewer MoE layers (never used for the reported number)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="concurrency sweep: decode tok/s for every batch in --sweep-batches at every K in "
+                         "--sweep-resident (the workload's format and routing), one JSON line per point")
+    ap.add_argument("--sweep-batches", default="1,2,3,4,5,6,7,8")
+    ap.add_argument("--sweep-resident", default="24,40")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="profiling: first run one plain device-to-device copy of this many MiB, "
                          "a known-size kernel to scale memory counters by")
@@ -61,6 +66,9 @@ def main():
         pmc_summary(*sys.argv[2:6])
         return
     args = parse()
+    if args.sweep and args.gpus == 1:
+        sweep(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this method keeps its slot tables and LRU state on one GPU, "
               "and multi-GPU runs are out of scope; run with --gpus 1", file=sys.stderr)
@@ -312,6 +320,83 @@ def main():
                                                                        M, D, has_prefill, args.cpu_budget)
     m.close()
     print(json.dumps(result), flush=True)
+
+
+def sweep(args):
+    """Decode throughput against batch size at several K (the docs page's
+    "Captured decode": batch x top_k <= K runs one device-planned captured
+    wave, larger batches are host-planned; the blog measures the drop past
+    K // top_k concurrent requests).  One context per K, loaded once; every
+    point is timed from an empty slot table over the same number of steps."""
+    import torch
+
+    import harness
+    import synth
+    import host_paged_expert_amd as pe
+
+    dev = "cuda:0"
+    torch.cuda.init()
+    Bs = [int(v) for v in args.sweep_batches.split(",")]
+    Ks = [int(v) for v in args.sweep_resident.split(",")]
+    steps = args.steps or 128
+    warmup = max(0, min(args.warmup, steps))
+    link = None
+    for K in Ks:
+        wl0 = synth.workload(args.workload, resident=K, batch=max(Bs), steps=steps)
+        m = harness.make_moe(wl0, max_tokens=max(Bs))
+        t0 = time.time()
+        harness.load_store(m, wl0)
+        log("sweep: K=%d context loaded in %.1fs" % (K, time.time() - t0))
+        if link is None:
+            link = max(pe.pe_link_probe(m.ctx, 1 << 30, 0, 5), pe.pe_link_probe(m.ctx, 1 << 30, 1, 5))
+        S_alg, _ = pe.pe_expert_bytes(wl0.wtype, wl0.hidden, wl0.inter)
+        stream = torch.cuda.current_stream()
+        for B in Bs:
+            wl = synth.workload(args.workload, resident=K, batch=B, steps=steps)
+            routing = synth.routing_for(wl)
+            x, ids, w = harness.decode_inputs(wl, routing, dev)
+            out = torch.empty((wl.layers, B, wl.hidden), dtype=torch.bfloat16, device=dev)
+            runner = harness.DecodeRunner(m, wl, x, ids, w, out, stream)
+
+            def cold():
+                torch.cuda.synchronize()
+                m.reset_lru(-1, stream)
+                runner.rewind()
+                torch.cuda.synchronize()
+                m.reset_stats()
+            cold()
+            runner.run(warmup)
+            cold()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            runner.run(steps)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            st = m.stats()
+            D, M = st["distinct"], st["page_ins"]
+            t_roof = D * S_alg / (HBM_PEAK_GBS * 1e9) + M * S_alg / (link * 1e9)
+            value = steps * B / (ms / 1e3)
+            res = {"metric": "paged-MoE decode tok/s, 48-layer 128-expert top-8; HBM & page-in GB/s % peak",
+                   "value": round(value, 3), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+                   "ms_per_step": round(ms / steps, 4), "higher_is_better": True, "scaling": "weak",
+                   "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x",
+                                                  "int4": "int4-w/bf16-x"}[wl.wtype],
+                   "data": "synthetic",
+                   "config": {"workload": "sweep:" + args.workload, "layers": wl.layers, "experts": wl.experts,
+                              "top_k": wl.top_k, "resident": K, "hidden": wl.hidden, "inter": wl.inter,
+                              "wtype": wl.wtype, "batch": B, "max_captured_batch": m.max_captured_batch,
+                              "path": "captured" if runner.captured else "host-planned"},
+                   "window": {"distinct": D, "page_ins": M, "waves": st["waves"],
+                              "miss_rate": round(M / max(st["entries"], 1), 4)},
+                   "roofline_path": {"model": "D*S/HBM + M*S/link", "link_gbs": round(link, 2),
+                                     "roof_tok_s": round(steps * B / t_roof, 2),
+                                     "frac": round(value / (steps * B / t_roof), 4)}}
+            log("sweep: K=%d batch %d (%s): %.1f tok/s, %.3f of roofline, %d waves" % (
+                K, B, res["config"]["path"], value, res["roofline_path"]["frac"], st["waves"]))
+            print(json.dumps(res), flush=True)
+            del runner
+        m.close()
 
 
 def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=False, budget_s=20.0):
