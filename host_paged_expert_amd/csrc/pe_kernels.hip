@@ -1527,12 +1527,12 @@ void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, i
   const int LG = lanes_per_row(a.I / vpc_of(wtype));
   const int RB = 2 * (64 / LG);
   const int n = a.T * a.k;
-  // wavefronts per workgroup: about two experts each, at most 8, and no more
-  // than keep every workgroup of the launch resident at once (about 2048
-  // wavefronts of this kernel's size on 256 CUs)
+  // wavefronts per workgroup: one per expert, at most 8, and no more than keep
+  // every workgroup of the launch resident at once (about 2048 wavefronts of
+  // this kernel's size on 256 CUs)
   const int grid_x = ceil_div(a.H, RB);
   const int items = std::min(n, a.E);
-  const int nw = std::max(1, std::min(std::min(8, ceil_div(items, 2)), std::max(1, 2048 / grid_x)));
+  const int nw = std::max(1, std::min(std::min(8, items), std::max(1, 2048 / grid_x)));
   const size_t head = al16(4 * (size_t)n * RB) + al16(4 * (size_t)n);
   const size_t staged = head + (size_t)n * a.I * 2;
   const dim3 grid(grid_x), block(64 * nw);
