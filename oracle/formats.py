@@ -11,6 +11,9 @@ canonical tensors (as produced by `synth.expert_tensors`) are:
   w = (q - 8) * s[n, c/128] with q a nibble (element 2i in the low nibble of
   byte i of the row) and s an IEEE fp16 scale.  This is the reading that
   reproduces the blog's 2.43 MB per expert.
+- int8: the docs page also names GPTQ int8.  Read as int4's scheme with 8-bit
+  codes: symmetric group-128 along the input dimension, one byte per weight,
+  w = (q - 128) * s[n, c/128] with s an IEEE fp16 scale.
 """
 import numpy as np
 
@@ -68,6 +71,16 @@ def dequant_int4_g128(qp: np.ndarray, s: np.ndarray) -> np.ndarray:
     return ((q - 8).astype(np.float32) * scale).astype(np.float32)
 
 
+def dequant_int8_g128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """w[n, c] = (q[n, c] - 128) * fp16 scale[n, c // 128], q one byte per weight."""
+    qi = np.asarray(q, np.uint8).astype(np.int64)
+    R, C = qi.shape
+    sf = f16_to_f32(s)
+    assert sf.shape == (R, C // 128)
+    scale = np.repeat(sf, 128, axis=1)
+    return ((qi - 128).astype(np.float32) * scale).astype(np.float32)
+
+
 def dequant_expert(wtype: str, t13, t2, s13=None, s2=None):
     """Canonical expert tensors -> (W13 fp32 [2I, H], W2 fp32 [H, I])."""
     if wtype == "bf16":
@@ -76,4 +89,6 @@ def dequant_expert(wtype: str, t13, t2, s13=None, s2=None):
         return dequant_fp8_b128(t13, s13), dequant_fp8_b128(t2, s2)
     if wtype == "int4":
         return dequant_int4_g128(t13, s13), dequant_int4_g128(t2, s2)
+    if wtype == "int8":
+        return dequant_int8_g128(t13, s13), dequant_int8_g128(t2, s2)
     raise ValueError(wtype)

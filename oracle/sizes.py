@@ -21,6 +21,9 @@ def expert_bytes(wtype: str, hidden: int, inter: int) -> int:
     if wtype == "int4":                                  # 4-bit codes + fp16 per 128 inputs per row
         groups = 2 * inter * (hidden // 128) + hidden * (inter // 128)
         return n // 2 + 2 * groups
+    if wtype == "int8":                                  # 8-bit codes + fp16 per 128 inputs per row
+        groups = 2 * inter * (hidden // 128) + hidden * (inter // 128)
+        return n + 2 * groups
     raise ValueError(wtype)
 
 

@@ -176,3 +176,26 @@ void synth_quant_int4_g128(const float* w, int rows, int cols, uint8_t* q, uint1
     }
   }
 }
+
+/* Symmetric group-128 int8 quantiser along the input (column) dimension:
+ * s = fp16(amax(group)/127) (1 if all zero), q = clamp(rne(w/s), -128, 127) + 128
+ * using the fp16-rounded s.  q: [rows, cols] bytes; s: [rows, cols/128] fp16 bits. */
+void synth_quant_int8_g128(const float* w, int rows, int cols, uint8_t* q, uint16_t* s) {
+  int ng = cols / 128;
+  for (int r = 0; r < rows; ++r) {
+    const float* row = w + (size_t)r * cols;
+    uint8_t* qrow = q + (size_t)r * cols;
+    for (int g = 0; g < ng; ++g) {
+      float amax = 0.0f;
+      for (int c = 0; c < 128; ++c) { float a = fabsf(row[g * 128 + c]); if (a > amax) amax = a; }
+      uint16_t sh = amax > 0.0f ? f16_from_f32(amax / 127.0f) : (uint16_t)0x3C00u;
+      s[(size_t)r * ng + g] = sh;
+      uint32_t e = (sh >> 10) & 0x1Fu, m = sh & 0x3FFu;
+      float sf = e ? ldexpf((float)(1024u + m), (int)e - 25) : ldexpf((float)m, -24);
+      for (int c = 0; c < 128; ++c) {
+        float v = nearbyintf(row[g * 128 + c] / sf);
+        qrow[g * 128 + c] = (uint8_t)((int)fminf(fmaxf(v, -128.0f), 127.0f) + 128);
+      }
+    }
+  }
+}

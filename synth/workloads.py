@@ -18,7 +18,7 @@ class Workload:
     resident: int         # K slots per layer
     hidden: int           # H
     inter: int            # I (expert SwiGLU intermediate)
-    wtype: str            # "bf16" | "fp8" | "int4"
+    wtype: str            # "bf16" | "fp8" | "int4" | "int8"
     batch: int            # decode tokens per step (independent chains)
     steps: int            # decode steps
     routing: str          # "persist_uniform" | "persist_zipf" | "prefill_zipf"
@@ -44,6 +44,9 @@ WORKLOADS = {
                                   "persist_zipf", 0.7, 1.0),
     # Same shapes, group-128 int4 experts, K=26, batch 4 (32 entries > K: host-planned).
     "decode_int4_k26_b4": Workload("decode_int4_k26_b4", 48, 128, 8, 26, 2048, 768, "int4", 4, 512,
+                                   "persist_zipf", 0.7, 1.0),
+    # Same shapes, GPTQ-style int8 experts (group-128 fp16 scales), K=40, batch 4 (one captured wave).
+    "decode_int8_k40_b4": Workload("decode_int8_k40_b4", 48, 128, 8, 40, 2048, 768, "int8", 4, 512,
                                    "persist_zipf", 0.7, 1.0),
     # bf16, K=92: a cold 2048-token prefill chunk (Zipf 0.8, 8 distinct ids per token),
     # then 256 decode steps at batch 1 continuing from the last prefill token.

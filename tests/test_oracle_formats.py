@@ -1,4 +1,4 @@
-"""Pins for oracle/formats.py: e4m3fn, int4 and bf16 decoding."""
+"""Pins for oracle/formats.py: e4m3fn, int4, int8 and bf16 decoding."""
 import numpy as np
 import pytest
 import torch
@@ -85,6 +85,35 @@ def test_int4_dequant_error_within_half_step():
         assert formats.unpack_int4(q).min() >= 1        # symmetric: -8 is never used
 
 
+def test_int8_dequant_vs_elementwise():
+    """Each weight decoded on its own: the byte as an integer minus 128, times the
+    fp16 scale of its row and 128-column group read with Python's own half codec."""
+    import struct
+    rng = np.random.default_rng(8)
+    q = rng.integers(0, 256, (3, 256), dtype=np.uint8)
+    s = np.array([[0x3C00, 0x2E66], [0x1400, 0xB800], [0x0001, 0x7BFF]], np.uint16)   # 1, 0.1, tiny, -0.5, subnormal, max
+    w = formats.dequant_int8_g128(q, s)
+    for r in range(3):
+        for c in range(256):
+            sc = struct.unpack("<e", struct.pack("<H", int(s[r, c // 128])))[0]
+            assert w[r, c] == np.float32((int(q[r, c]) - 128) * sc)
+
+
+def test_int8_dequant_error_within_half_step():
+    wl = synth.workload("decode_int8_k40_b4", hidden=256, inter=128)
+    f13, f2 = synth.expert_draws(wl.hidden, wl.inter, 0, 1)
+    q13, q2, s13, s2 = synth.expert_tensors(wl, 0, 1)
+    for f, q, s in ((f13, q13, s13), (f2, q2, s2)):
+        w = formats.dequant_int8_g128(q, s)
+        step = np.repeat(formats.f16_to_f32(s), 128, axis=1)
+        assert np.all(np.abs(w - f) <= step / 2 * (1 + 1e-6))
+        qi = q.astype(np.int64) - 128
+        assert qi.min() >= -127                          # symmetric: -128 is never used
+        # each group's largest magnitude lands on the last code (up to the fp16 rounding of s)
+        gmax = np.abs(qi).reshape(q.shape[0], -1, 128).max(axis=2)
+        assert np.all(gmax >= 126)
+
+
 def test_fp8_dequant_error_within_rounding():
     wl = synth.workload("decode_fp8_k40_b4", hidden=256, inter=128)
     f13, f2 = synth.expert_draws(wl.hidden, wl.inter, 0, 1)
@@ -100,7 +129,7 @@ def test_fp8_dequant_error_within_rounding():
 
 
 def test_dequant_expert_shapes():
-    for name in ("decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4"):
+    for name in ("decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4", "decode_int8_k40_b4"):
         wl = synth.workload(name, hidden=256, inter=128)
         w13, w2 = formats.dequant_expert(wl.wtype, *synth.expert_tensors(wl, 1, 2))
         assert w13.shape == (256, 256) and w2.shape == (256, 128)

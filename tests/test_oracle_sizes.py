@@ -79,3 +79,14 @@ def test_choosing_k_example_fits():
     assert ex["resident"] * slot < budget
     assert sizes.suggest_k(ex["resident"] * slot, slot, E) == ex["resident"]
     assert sizes.suggest_k(1e15, slot, E) == E
+
+
+def test_int8_expert_bytes_equal_the_canonical_tensors():
+    """No page value for int8: the closed form against the bytes of the synthetic
+    canonical tensors (codes one byte per weight, fp16 per 128 inputs per row)."""
+    import synth
+    for H, I in ((2048, 768), (256, 128)):
+        wl = synth.workload("decode_int8_k40_b4", hidden=H, inter=I)
+        total = sum(t.nbytes for t in synth.expert_tensors(wl, 0, 3))
+        assert sizes.expert_bytes("int8", H, I) == total
+    assert sizes.expert_bytes("int8", 2048, 768) == 4_792_320
