@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+DTYPES = {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x", "int4": "int4-w/bf16-x", "int8": "int8-w/bf16-x"}
 PCIE5_X16_GBS = 32.0 * 16 * 128 / 130 / 8   # 63.0 GB/s per direction
 
 
@@ -229,9 +230,9 @@ def main():
         st2 = diff(m.stats(), before)
         if st2["page_ins"] != M or st2["distinct"] != D:
             raise RuntimeError("timing pass planned differently from the timed run")
-        w2b = wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5}[wl.wtype]
+        w2b = wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5, "int8": 1}[wl.wtype]
         s2b = {"bf16": 0, "fp8": (wl.hidden // 128) * (wl.inter // 128) * 4,
-               "int4": wl.hidden * (wl.inter // 128) * 2}[wl.wtype]
+               "int4": wl.hidden * (wl.inter // 128) * 2, "int8": wl.hidden * (wl.inter // 128) * 2}[wl.wtype]
         n_pi, ms_pi = tm["page_in"]
         n_dn, ms_dn = tm["down"]
         # the launches each stage brackets on this path
@@ -264,7 +265,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x", "int4": "int4-w/bf16-x"}[wl.wtype],
+        "dtype": DTYPES[wl.wtype],
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "experts": wl.experts, "top_k": wl.top_k,
                    "resident": wl.resident, "hidden": H, "inter": wl.inter, "wtype": wl.wtype,
@@ -380,8 +381,7 @@ def sweep(args):
             res = {"metric": "paged-MoE decode tok/s, 48-layer 128-expert top-8; HBM & page-in GB/s % peak",
                    "value": round(value, 3), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
                    "ms_per_step": round(ms / steps, 4), "higher_is_better": True, "scaling": "weak",
-                   "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x",
-                                                  "int4": "int4-w/bf16-x"}[wl.wtype],
+                   "vs_baseline": None, "dtype": DTYPES[wl.wtype],
                    "data": "synthetic",
                    "config": {"workload": "sweep:" + args.workload, "layers": wl.layers, "experts": wl.experts,
                               "top_k": wl.top_k, "resident": K, "hidden": wl.hidden, "inter": wl.inter,
@@ -469,7 +469,7 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
     tokens = B * len(done) / L                      # a token passes all L layers
     t_total = t_moe + t_sim * (len(done) / L) / steps
     log("oracle MoE: %d (step, layer) pairs in %.2fs" % (len(done), t_moe))
-    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2}[wl.wtype]
+    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2}[wl.wtype]
     cpu = {"value": round(tokens / t_total, 5) if t_total > 0 else None, "unit": "tok/s", "cores": threads,
            "kind": "oracle",
            "sample": "%d (step, layer) pairs from decode steps %s (batch %d) through the fp32 unpaged oracle, "
@@ -504,10 +504,10 @@ def alg_bytes(kernel, wtype, hidden, inter, D, M, launches):
     expert blobs over the link, write them into slots and read the resident
     experts' gate/up weights; the down launches read every distinct expert's
     down weights.  Activations (< 1%) are left out."""
-    S = {"bf16": 2, "fp8": 1, "int4": 0.5}[wtype]
+    S = {"bf16": 2, "fp8": 1, "int4": 0.5, "int8": 1}[wtype]
     w13, w2 = 2 * inter * hidden * S, inter * hidden * S
-    s13 = {"bf16": 0, "fp8": (2 * inter // 128) * (hidden // 128) * 4, "int4": 2 * inter * (hidden // 128) * 2}[wtype]
-    s2 = {"bf16": 0, "fp8": (hidden // 128) * (inter // 128) * 4, "int4": hidden * (inter // 128) * 2}[wtype]
+    s13 = {"bf16": 0, "fp8": (2 * inter // 128) * (hidden // 128) * 4}.get(wtype, 2 * inter * (hidden // 128) * 2)
+    s2 = {"bf16": 0, "fp8": (hidden // 128) * (inter // 128) * 4}.get(wtype, hidden * (inter // 128) * 2)
     blob = w13 + w2 + s13 + s2
     if kernel in ("step_a_kernel", "wave_a_kernel"):
         tot = 2 * M * blob + (D - M) * (w13 + s13)

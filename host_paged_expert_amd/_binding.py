@@ -22,7 +22,8 @@ PE_ERR_NOT_CAPTURABLE = -6
 PE_W_BF16 = 0
 PE_W_FP8_B128 = 1
 PE_W_INT4_G128 = 2
-WTYPES = {"bf16": PE_W_BF16, "fp8": PE_W_FP8_B128, "int4": PE_W_INT4_G128}
+PE_W_INT8_G128 = 3
+WTYPES = {"bf16": PE_W_BF16, "fp8": PE_W_FP8_B128, "int4": PE_W_INT4_G128, "int8": PE_W_INT8_G128}
 
 PE_FLAG_PAGEIN_DMA = 1
 PE_FLAG_FORCE_HOST_PLAN = 2

@@ -66,6 +66,11 @@ bool blob_layout(int wtype, int H, int I, BlobLayout* b) {
       b->s13 = (size_t)2 * I * (H / 128) * 2;
       b->s2 = (size_t)H * (I / 128) * 2;
       break;
+    case PE_W_INT8_G128:
+      b->w13 = n13; b->w2 = n2;
+      b->s13 = (size_t)2 * I * (H / 128) * 2;
+      b->s2 = (size_t)H * (I / 128) * 2;
+      break;
     default: return false;
   }
   b->off_w13 = 0;
@@ -310,7 +315,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     return fail(PE_ERR_INVALID_ARG, "hidden and inter must be positive multiples of 8");
   if (g.hidden > 4096 || g.inter > 4096)
     return fail(PE_ERR_UNSUPPORTED, "hidden and inter above 4096 are not supported");
-  if (g.wtype != PE_W_BF16 && g.wtype != PE_W_FP8_B128 && g.wtype != PE_W_INT4_G128)
+  if (g.wtype != PE_W_BF16 && g.wtype != PE_W_FP8_B128 && g.wtype != PE_W_INT4_G128 && g.wtype != PE_W_INT8_G128)
     return fail(PE_ERR_INVALID_ARG, "unknown weight type %d", g.wtype);
   if (g.wtype != PE_W_BF16 && (g.hidden % 128 || g.inter % 128))
     return fail(PE_ERR_INVALID_ARG, "quantized formats need hidden and inter multiples of 128");

@@ -647,6 +647,9 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<PE_W_BF16> { static constexpr int VPC = 8; };        // values per 16-B chunk
 template <> struct Fmt<PE_W_FP8_B128> { static constexpr int VPC = 16; };
 template <> struct Fmt<PE_W_INT4_G128> { static constexpr int VPC = 32; };
+template <> struct Fmt<PE_W_INT8_G128> { static constexpr int VPC = 16; };
+// int4 and int8 keep one fp16 scale per row and 128 columns
+template <int FMT> constexpr bool kRowScales = FMT == PE_W_INT4_G128 || FMT == PE_W_INT8_G128;
 }  // namespace
 
 // Loads of one row's chunks for one lane: chunks lig, lig + LG, ... (at most
@@ -667,7 +670,7 @@ template <int FMT>
 __device__ __forceinline__ float chunk_scale(const float* __restrict__ s_fp8_row,
                                              const uint16_t* __restrict__ s_i4_row, int col) {
   if constexpr (FMT == PE_W_FP8_B128) return s_fp8_row[col >> 7];
-  else if constexpr (FMT == PE_W_INT4_G128) return half_bits_to_f32(s_i4_row[col >> 7]);
+  else if constexpr (kRowScales<FMT>) return half_bits_to_f32(s_i4_row[col >> 7]);
   else return 1.0f;
 }
 
@@ -720,6 +723,25 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t
       const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[p], true);
       wb[2 * p] = pack_bf16x2(lo[0], lo[1]);
       wb[2 * p + 1] = pack_bf16x2(hi[0], hi[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t >= m) break;
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+      const uint4 x0 = xp[0], x1 = xp[1];
+      const uint32_t xd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float part = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) part = dot2_bf16(wb[p], xd[p], part);
+      acc[t] = __builtin_fmaf(sc, part, acc[t]);
+    }
+  } else if constexpr (FMT == PE_W_INT8_G128) {
+    // 16 bytes q, value q - 128 (an integer bf16 holds exactly), pairs in order
+    uint32_t wb[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      wb[2 * p] = pack_bf16x2((float)(wd[p] & 0xFFu) - 128.0f, (float)((wd[p] >> 8) & 0xFFu) - 128.0f);
+      wb[2 * p + 1] = pack_bf16x2((float)((wd[p] >> 16) & 0xFFu) - 128.0f, (float)(wd[p] >> 24) - 128.0f);
     }
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
@@ -1095,7 +1117,7 @@ __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, cons
   // the block's scale bytes [og, og + nb) (gate) and [ou, ou + nb) (up) of the S13 region
   size_t og = 0, ou = 0;
   int nb = 0;
-  if constexpr (FMT == PE_W_INT4_G128) {
+  if constexpr (kRowScales<FMT>) {
     og = (size_t)i0 * (H / 128) * 2;
     ou = (size_t)(I + i0) * (H / 128) * 2;
     nb = min(g.rows_per_block, I - i0) * (H / 128) * 2;
@@ -1104,7 +1126,7 @@ __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, cons
     ou = (size_t)((I + i0) >> 7) * (H / 128) * 4;
     nb = (H / 128) * 4;
   }
-  const bool store_sc = FMT == PE_W_INT4_G128 || (i0 & 127) == 0;   // one block per FP8 block row
+  const bool store_sc = kRowScales<FMT> || (i0 & 127) == 0;   // one block per FP8 block row
   const float* sgf = reinterpret_cast<const float*>(s_sc);
   const float* suf = reinterpret_cast<const float*>(s_sc + kStreamScaleLds / 2);
   const uint16_t* sgh = reinterpret_cast<const uint16_t*>(s_sc) + (size_t)(i - i0) * (H / 128);
@@ -1436,8 +1458,10 @@ static int pick_mb(int max_m) {
 }
 
 static int vpc_of(int wtype) {
-  return wtype == PE_W_BF16 ? Fmt<PE_W_BF16>::VPC : wtype == PE_W_FP8_B128 ? Fmt<PE_W_FP8_B128>::VPC
-                                                                          : Fmt<PE_W_INT4_G128>::VPC;
+  return wtype == PE_W_BF16 ? Fmt<PE_W_BF16>::VPC
+         : wtype == PE_W_FP8_B128 ? Fmt<PE_W_FP8_B128>::VPC
+         : wtype == PE_W_INT8_G128 ? Fmt<PE_W_INT8_G128>::VPC
+                                   : Fmt<PE_W_INT4_G128>::VPC;
 }
 
 static GemvGeom gate_up_geom(int wtype, const ExpertArgs& a) {
@@ -1469,6 +1493,12 @@ static size_t lean_head(const ExpertArgs& a) { return a.lean ? lean_lds_bytes(a.
       else { constexpr int M_ = 8; CALL; }                                        \
     } else if ((wtype) == PE_W_FP8_B128) {                                        \
       constexpr int F_ = PE_W_FP8_B128;                                           \
+      if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
+      else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
+      else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
+      else { constexpr int M_ = 8; CALL; }                                        \
+    } else if ((wtype) == PE_W_INT8_G128) {                                       \
+      constexpr int F_ = PE_W_INT8_G128;                                          \
       if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
       else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
       else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
@@ -1582,6 +1612,19 @@ __device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst) {
     }
     reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
     reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else if constexpr (FMT == PE_W_INT8_G128) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // q - 128 is an integer of at most 8 bits: the top half of its fp32 is exact
+      const float v0 = (float)(wd[p] & 0xFFu) - 128.0f, v1 = (float)((wd[p] >> 8) & 0xFFu) - 128.0f;
+      const float v2 = (float)((wd[p] >> 16) & 0xFFu) - 128.0f, v3 = (float)(wd[p] >> 24) - 128.0f;
+      o[2 * p] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
+      o[2 * p + 1] = (__float_as_uint(v2) >> 16) | (__float_as_uint(v3) & 0xFFFF0000u);
+    }
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
   } else {
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     uint32_t o[16];
@@ -1607,7 +1650,7 @@ __device__ __forceinline__ void stage_weights(uint16_t* sB, const uint8_t* __res
                                               int kb) {
   constexpr int VPC = Fmt<FMT>::VPC;
   constexpr int CPR = kKB / VPC;                       // chunks per row per stage
-  const size_t row_bytes = (size_t)C * (FMT == PE_W_BF16 ? 2 : FMT == PE_W_FP8_B128 ? 1 : 0) +
+  const size_t row_bytes = (size_t)C * (FMT == PE_W_BF16 ? 2 : (FMT == PE_W_FP8_B128 || FMT == PE_W_INT8_G128) ? 1 : 0) +
                            (FMT == PE_W_INT4_G128 ? (size_t)C / 2 : 0);
   const uint4* base = reinterpret_cast<const uint4*>(W);
   for (int i = threadIdx.x; i < kNT * CPR; i += kMfmaThreads) {
@@ -1682,7 +1725,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     if constexpr (FMT == PE_W_FP8_B128) {
       sg = S13f[(size_t)(n0 >> 7) * (H / 128) + kb];
       su = S13f[(size_t)((I + n0) >> 7) * (H / 128) + kb];
-    } else if constexpr (FMT == PE_W_INT4_G128) {
+    } else if constexpr (kRowScales<FMT>) {
       sg = half_bits_to_f32(S13h[(size_t)ncol * (H / 128) + kb]);
       su = half_bits_to_f32(S13h[(size_t)(I + ncol) * (H / 128) + kb]);
     }
@@ -1763,7 +1806,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
     }
     float sc = 1.f;
     if constexpr (FMT == PE_W_FP8_B128) sc = S2f[(size_t)(n0 >> 7) * (I / 128) + kb];
-    else if constexpr (FMT == PE_W_INT4_G128) sc = half_bits_to_f32(S2h[(size_t)ncol * (I / 128) + kb]);
+    else if constexpr (kRowScales<FMT>) sc = half_bits_to_f32(S2h[(size_t)ncol * (I / 128) + kb]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1790,6 +1833,7 @@ void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t 
   dim3 grid(a.I / kNT, tiles);
   if (wtype == PE_W_BF16) mfma_gate_up_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_FP8_B128) mfma_gate_up_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
+  else if (wtype == PE_W_INT8_G128) mfma_gate_up_kernel<PE_W_INT8_G128><<<grid, kMfmaThreads, 0, s>>>(a);
   else mfma_gate_up_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
 }
 
@@ -1798,6 +1842,7 @@ void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) 
   dim3 grid(a.H / kNT, tiles);
   if (wtype == PE_W_BF16) mfma_down_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_FP8_B128) mfma_down_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
+  else if (wtype == PE_W_INT8_G128) mfma_down_kernel<PE_W_INT8_G128><<<grid, kMfmaThreads, 0, s>>>(a);
   else mfma_down_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
 }
 

@@ -51,6 +51,7 @@ extern "C" {
 #define PE_W_BF16       0   /* unquantized bf16                                   */
 #define PE_W_FP8_B128   1   /* OCP e4m3fn codes, one fp32 multiplier per 128x128  */
 #define PE_W_INT4_G128  2   /* symmetric int4, one fp16 scale per 128 inputs/row  */
+#define PE_W_INT8_G128  3   /* symmetric int8 (GPTQ int8), fp16 scale per 128     */
 
 /* ---- configuration flags --------------------------------------------- */
 #define PE_FLAG_PAGEIN_DMA      1u  /* host-planned steps copy with hipMemcpyAsync
@@ -110,6 +111,8 @@ void pe_destroy(pe_ctx* ctx);
  *   PE_W_INT4_G128: w13 u8 [2I, H/2], w2 u8 [H, I/2] (element 2c is the low
  *                   nibble of byte c), s13 fp16 [2I, H/128], s2 fp16
  *                   [H, I/128]; weight = (nibble - 8) * s.
+ *   PE_W_INT8_G128: w13 u8 [2I, H], w2 u8 [H, I], s13 fp16 [2I, H/128],
+ *                   s2 fp16 [H, I/128]; weight = (byte - 128) * s.
  * The data is copied; the caller keeps ownership.  With PE_FLAG_UNPAGED the
  * blob goes straight to device slot `expert` (synchronous copy).  An expert
  * that is resident when it is reloaded keeps its old slot contents until it

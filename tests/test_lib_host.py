@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(pe.SIGNATURES)
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8"])
 @pytest.mark.parametrize("H,I", [(2048, 768), (256, 128), (1024, 512)])
 def test_expert_bytes_match_oracle(wtype, H, I):
     alg, copied = pe.pe_expert_bytes(wtype, H, I)
