@@ -14,6 +14,11 @@ canonical tensors (as produced by `synth.expert_tensors`) are:
 - int8: the docs page also names GPTQ int8.  Read as int4's scheme with 8-bit
   codes: symmetric group-128 along the input dimension, one byte per weight,
   w = (q - 128) * s[n, c/128] with s an IEEE fp16 scale.
+- MXFP4 (the blog names it among the added formats and runs gpt-oss-20b with
+  it): OCP microscaling, blocks of 32 weights along the input dimension, each
+  an FP4 E2M1 code, sharing one E8M0 scale: w = e2m1(q[n, c]) * 2^(e[n, c/32]
+  - 127).  Codes are packed two per byte like int4 (element 2i in the low
+  nibble of byte i).
 """
 import numpy as np
 
@@ -81,6 +86,32 @@ def dequant_int8_g128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return ((qi - 128).astype(np.float32) * scale).astype(np.float32)
 
 
+def e2m1_to_f32(codes: np.ndarray) -> np.ndarray:
+    """OCP 4-bit float E2M1: sign bit, 2 exponent bits with bias 1, 1 mantissa
+    bit; exponent 0 is subnormal (m/2); no infinities or NaN; largest 6."""
+    c = np.asarray(codes, np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    val = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.power(2.0, e - 1))
+    return (sign * val).astype(np.float32)
+
+
+def e8m0_to_f32(codes: np.ndarray) -> np.ndarray:
+    """OCP E8M0 scale: 2^(e - 127); e = 255 is NaN."""
+    e = np.asarray(codes, np.int64)
+    return np.where(e == 255, np.nan, np.power(2.0, e - 127)).astype(np.float32)
+
+
+def dequant_mxfp4_b32(qp: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """w[n, c] = e2m1(q[n, c]) * 2^(s[n, c // 32] - 127), q packed two per byte."""
+    q = unpack_int4(qp)
+    R, C = q.shape
+    assert s.shape == (R, C // 32)
+    scale = np.repeat(e8m0_to_f32(s), 32, axis=1)
+    return (e2m1_to_f32(q) * scale).astype(np.float32)
+
+
 def dequant_expert(wtype: str, t13, t2, s13=None, s2=None):
     """Canonical expert tensors -> (W13 fp32 [2I, H], W2 fp32 [H, I])."""
     if wtype == "bf16":
@@ -91,4 +122,6 @@ def dequant_expert(wtype: str, t13, t2, s13=None, s2=None):
         return dequant_int4_g128(t13, s13), dequant_int4_g128(t2, s2)
     if wtype == "int8":
         return dequant_int8_g128(t13, s13), dequant_int8_g128(t2, s2)
+    if wtype == "mxfp4":
+        return dequant_mxfp4_b32(t13, s13), dequant_mxfp4_b32(t2, s2)
     raise ValueError(wtype)

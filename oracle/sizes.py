@@ -24,6 +24,9 @@ def expert_bytes(wtype: str, hidden: int, inter: int) -> int:
     if wtype == "int8":                                  # 8-bit codes + fp16 per 128 inputs per row
         groups = 2 * inter * (hidden // 128) + hidden * (inter // 128)
         return n + 2 * groups
+    if wtype == "mxfp4":                                 # 4-bit codes + one E8M0 byte per 32 inputs per row
+        blocks = 2 * inter * (hidden // 32) + hidden * (inter // 32)
+        return n // 2 + blocks
     raise ValueError(wtype)
 
 

@@ -199,3 +199,49 @@ void synth_quant_int8_g128(const float* w, int rows, int cols, uint8_t* q, uint1
     }
   }
 }
+
+/* OCP FP4 E2M1 code of v: round to nearest, ties to the even code (mantissa bit
+ * 0), saturating at +-6; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static uint8_t e2m1_from_f32(float v) {
+  static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  uint8_t sign = signbit(v) ? 8u : 0u;
+  float a = fabsf(v);
+  if (a >= 6.0f) return (uint8_t)(sign | 7u);
+  int best = 0;
+  for (int i = 1; i < 8; ++i) {
+    float d = fabsf(a - mag[i]), db = fabsf(a - mag[best]);
+    if (d < db || (d == db && (i & 1) == 0)) best = i;
+  }
+  return (uint8_t)(sign | (uint8_t)best);
+}
+
+/* MXFP4 quantiser (OCP microscaling) along the input (column) dimension, blocks
+ * of 32: shared exponent X = floor(log2(amax(block))) - 2 (E2M1's largest
+ * exponent), scale 2^X stored as the E8M0 byte X + 127 (127 for an all-zero
+ * block), q = e2m1(w / 2^X).  q: [rows, cols/2] bytes, element 2i in the low
+ * nibble of byte i; s: [rows, cols/32] E8M0 bytes. */
+void synth_quant_mxfp4_b32(const float* w, int rows, int cols, uint8_t* q, uint8_t* s) {
+  int nb = cols / 32;
+  for (int r = 0; r < rows; ++r) {
+    const float* row = w + (size_t)r * cols;
+    uint8_t* qrow = q + (size_t)r * (cols / 2);
+    for (int b = 0; b < nb; ++b) {
+      float amax = 0.0f;
+      for (int c = 0; c < 32; ++c) { float a = fabsf(row[b * 32 + c]); if (a > amax) amax = a; }
+      int e = 127;
+      if (amax > 0.0f) {
+        int ex;
+        frexpf(amax, &ex);              /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+        e = ex - 1 - 2 + 127;
+        if (e < 0) e = 0;
+        if (e > 254) e = 254;
+      }
+      s[(size_t)r * nb + b] = (uint8_t)e;
+      float sc = ldexpf(1.0f, e - 127);
+      for (int c = 0; c < 32; c += 2) {
+        uint8_t lo = e2m1_from_f32(row[b * 32 + c] / sc), hi = e2m1_from_f32(row[b * 32 + c + 1] / sc);
+        qrow[(b * 32 + c) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}

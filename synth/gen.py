@@ -49,6 +49,7 @@ def _L():
                 lib.synth_quant_fp8_b128.argtypes = [vp, i32, i32, vp, vp]
                 lib.synth_quant_int4_g128.argtypes = [vp, i32, i32, vp, vp]
                 lib.synth_quant_int8_g128.argtypes = [vp, i32, i32, vp, vp]
+                lib.synth_quant_mxfp4_b32.argtypes = [vp, i32, i32, vp, vp]
                 _lib = lib
     return _lib
 
@@ -125,6 +126,8 @@ def expert_tensors(wl: Workload, layer: int, expert: int):
           nibbles q (w = (q-8)*s; element 2i in the low nibble of byte i), fp16 scale bits
     int8: (Q13 u8 [2I,H], Q2 u8 [H,I], S13 u16 [2I,H/128], S2 u16 [H,I/128])
           bytes q (w = (q-128)*s), fp16 scale bits
+    mxfp4: (Q13 u8 [2I,H/2], Q2 u8 [H,I/2], S13 u8 [2I,H/32], S2 u8 [H,I/32])
+          E2M1 codes packed like int4, E8M0 block scales (w = e2m1(q) * 2^(s-127))
     """
     H, I = wl.hidden, wl.inter
     L = _L()
@@ -158,6 +161,14 @@ def expert_tensors(wl: Workload, layer: int, expert: int):
         s2 = np.empty((H, I // 128), np.uint16)
         L.synth_quant_int8_g128(f13.ctypes.data, 2 * I, H, q13.ctypes.data, s13.ctypes.data)
         L.synth_quant_int8_g128(f2.ctypes.data, H, I, q2.ctypes.data, s2.ctypes.data)
+        return q13, q2, s13, s2
+    if wl.wtype == "mxfp4":
+        q13 = np.empty((2 * I, H // 2), np.uint8)
+        q2 = np.empty((H, I // 2), np.uint8)
+        s13 = np.empty((2 * I, H // 32), np.uint8)
+        s2 = np.empty((H, I // 32), np.uint8)
+        L.synth_quant_mxfp4_b32(f13.ctypes.data, 2 * I, H, q13.ctypes.data, s13.ctypes.data)
+        L.synth_quant_mxfp4_b32(f2.ctypes.data, H, I, q2.ctypes.data, s2.ctypes.data)
         return q13, q2, s13, s2
     raise ValueError("unknown weight type %r" % wl.wtype)
 

@@ -1,10 +1,11 @@
-"""The five synthetic workloads of the paged-expert MoE layer.
+"""The synthetic workloads of the paged-expert MoE layer.
 
 Shapes follow the pages' model (48 MoE layers, 128 routed experts, top-8;
 hidden 2048 and expert intermediate 768, which give the 4.72 MB block-FP8
 and 2.43 MB int4 expert sizes the blog quotes).  Routing is synthetic
 (Zipf popularity plus token-to-token persistence) and stands in for the
-ShareGPT-driven router decisions the pages measured with.
+ShareGPT-driven router decisions the pages measured with.  The MXFP4 workload
+takes the gpt-oss-20b expert shape instead (hidden = inter = 2880).
 """
 from dataclasses import dataclass
 
@@ -18,7 +19,7 @@ class Workload:
     resident: int         # K slots per layer
     hidden: int           # H
     inter: int            # I (expert SwiGLU intermediate)
-    wtype: str            # "bf16" | "fp8" | "int4" | "int8"
+    wtype: str            # "bf16" | "fp8" | "int4" | "int8" | "mxfp4"
     batch: int            # decode tokens per step (independent chains)
     steps: int            # decode steps
     routing: str          # "persist_uniform" | "persist_zipf" | "prefill_zipf"
@@ -48,6 +49,11 @@ WORKLOADS = {
     # Same shapes, GPTQ-style int8 experts (group-128 fp16 scales), K=40, batch 4 (one captured wave).
     "decode_int8_k40_b4": Workload("decode_int8_k40_b4", 48, 128, 8, 40, 2048, 768, "int8", 4, 512,
                                    "persist_zipf", 0.7, 1.0),
+    # MXFP4 experts in the shape of the blog's gpt-oss-20b runs: 24 MoE layers, 32
+    # experts, top-4, hidden and expert intermediate 2880 (not a multiple of 128,
+    # so every expert takes the GEMV kernels); K=16, batch 1.
+    "decode_mxfp4_k16_b1": Workload("decode_mxfp4_k16_b1", 24, 32, 4, 16, 2880, 2880, "mxfp4", 1, 512,
+                                    "persist_zipf", 0.7, 1.0),
     # bf16, K=92: a cold 2048-token prefill chunk (Zipf 0.8, 8 distinct ids per token),
     # then 256 decode steps at batch 1 continuing from the last prefill token.
     "prefill_bf16_k92": Workload("prefill_bf16_k92", 48, 128, 8, 92, 2048, 768, "bf16", 1, 256,

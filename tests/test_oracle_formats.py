@@ -1,4 +1,4 @@
-"""Pins for oracle/formats.py: e4m3fn, int4, int8 and bf16 decoding."""
+"""Pins for oracle/formats.py: e4m3fn, int4, int8, MXFP4 and bf16 decoding."""
 import numpy as np
 import pytest
 import torch
@@ -128,8 +128,64 @@ def test_fp8_dequant_error_within_rounding():
         assert np.all(blk == 448.0)
 
 
+# OCP microscaling spec, FP4 E2M1 value table: codes 0..7 are +0, 0.5, 1, 1.5,
+# 2, 3, 4, 6 and codes 8..15 the same magnitudes negated.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_e2m1_all_codes_match_the_spec_table():
+    got = formats.e2m1_to_f32(np.arange(16))
+    assert got.tolist() == E2M1_TABLE
+    assert np.signbit(got[8]) and not np.signbit(got[0])
+
+
+def test_e8m0_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = formats.e8m0_to_f32(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float32).numpy()
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert got[127] == 1.0 and got[128] == 2.0 and got[126] == 0.5 and np.isnan(got[255])
+
+
+def test_mxfp4_dequant_vs_elementwise():
+    """Each weight decoded on its own from the spec's value table: the nibble
+    (low nibble first) times 2 to the power of its 32-column block's byte - 127."""
+    rng = np.random.default_rng(9)
+    qp = rng.integers(0, 256, (3, 32), dtype=np.uint8)        # 3 rows x 64 columns
+    s = np.array([[127, 120], [130, 0], [252, 1]], np.uint8)
+    w = formats.dequant_mxfp4_b32(qp, s)
+    for r in range(3):
+        for c in range(64):
+            nib = (int(qp[r, c // 2]) >> (4 * (c % 2))) & 0xF
+            want = np.float32(E2M1_TABLE[nib] * 2.0 ** (int(s[r, c // 32]) - 127))
+            assert w[r, c] == want, (r, c)
+
+
+def test_mxfp4_quantiser_rounds_to_the_nearest_grid_point():
+    """The synthetic MXFP4 tensors against the spec's scale rule: each block's
+    E8M0 exponent is floor(log2(amax)) - 2, and every weight decodes to the E2M1
+    grid point nearest to w / 2^X (saturating at 6), times 2^X."""
+    wl = synth.workload("decode_mxfp4_k16_b1", hidden=256, inter=128)
+    f13, f2 = synth.expert_draws(wl.hidden, wl.inter, 0, 1)
+    q13, q2, s13, s2 = synth.expert_tensors(wl, 0, 1)
+    grid = np.array(sorted(set(abs(v) for v in E2M1_TABLE)))
+    for f, q, s in ((f13, q13, s13), (f2, q2, s2)):
+        w = formats.dequant_mxfp4_b32(q, s)
+        amax = np.abs(f).reshape(f.shape[0], -1, 32).max(axis=2)
+        assert np.array_equal(s.astype(np.int64), np.floor(np.log2(amax)).astype(np.int64) - 2 + 127)
+        sc = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)
+        a = np.minimum(np.abs(f) / sc, 6.0)
+        dist = np.abs(a[..., None] - grid)
+        best = dist.min(axis=-1)
+        got = np.abs(w) / sc
+        # the decoded magnitude is a nearest grid point (ties may go either way here)
+        assert np.all(np.abs(a - got) <= best + 1e-12)
+        assert np.all((np.sign(w) == np.sign(f)) | (w == 0))
+
+
 def test_dequant_expert_shapes():
-    for name in ("decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4", "decode_int8_k40_b4"):
+    for name in ("decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4", "decode_int8_k40_b4",
+                 "decode_mxfp4_k16_b1"):
         wl = synth.workload(name, hidden=256, inter=128)
         w13, w2 = formats.dequant_expert(wl.wtype, *synth.expert_tensors(wl, 1, 2))
         assert w13.shape == (256, 256) and w2.shape == (256, 128)

@@ -31,7 +31,7 @@ def test_tiny_workload_paged_equals_unpaged_for_every_k():
             assert np.array_equal(out, ref[s]), (K, s)
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8", "mxfp4"])
 def test_multi_wave_prefill_like_paged_equals_unpaged(wtype):
     wl = synth.workload("prefill_bf16_k92", layers=1, experts=12, top_k=3, hidden=128, inter=128,
                         wtype=wtype, prefill_tokens=24, steps=4)

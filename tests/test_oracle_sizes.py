@@ -90,3 +90,16 @@ def test_int8_expert_bytes_equal_the_canonical_tensors():
         total = sum(t.nbytes for t in synth.expert_tensors(wl, 0, 3))
         assert sizes.expert_bytes("int8", H, I) == total
     assert sizes.expert_bytes("int8", 2048, 768) == 4_792_320
+
+
+def test_mxfp4_expert_bytes_equal_the_canonical_tensors():
+    """MXFP4 (OCP): 4-bit codes plus one E8M0 byte per 32 inputs per row.  At
+    the gpt-oss-20b expert shape (hidden = inter = 2880) that is 3 x 2880 x 2880
+    / 2 code bytes and 3 x 2880 x 90 scale bytes, with no padding: the slot
+    holds exactly the host layout."""
+    import synth
+    for H, I in ((2880, 2880), (256, 128)):
+        wl = synth.workload("decode_mxfp4_k16_b1", hidden=H, inter=I)
+        total = sum(t.nbytes for t in synth.expert_tensors(wl, 0, 3))
+        assert sizes.expert_bytes("mxfp4", H, I) == total
+    assert sizes.expert_bytes("mxfp4", 2880, 2880) == 12_441_600 + 777_600
