@@ -27,7 +27,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-DTYPES = {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x", "int4": "int4-w/bf16-x", "int8": "int8-w/bf16-x"}
+DTYPES = {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16-x", "int4": "int4-w/bf16-x", "int8": "int8-w/bf16-x",
+          "mxfp4": "mxfp4-w/bf16-x"}
+
+
+def part_bytes(wtype, hidden, inter):
+    """Bytes of an expert's four parts (w13, w2, s13, s2) in the library's
+    formats: bf16; e4m3 + fp32 per 128x128 block; int4 / int8 codes + fp16 per
+    row and 128 inputs; MXFP4 codes + one E8M0 byte per row and 32 inputs."""
+    H, I = hidden, inter
+    if wtype == "bf16":
+        return 4 * I * H, 2 * I * H, 0, 0
+    if wtype == "fp8":
+        return 2 * I * H, I * H, (2 * I // 128) * (H // 128) * 4, (H // 128) * (I // 128) * 4
+    if wtype == "int4":
+        return I * H, I * H // 2, 2 * I * (H // 128) * 2, H * (I // 128) * 2
+    if wtype == "int8":
+        return 2 * I * H, I * H, 2 * I * (H // 128) * 2, H * (I // 128) * 2
+    if wtype == "mxfp4":
+        return I * H, I * H // 2, 2 * I * (H // 32), H * (I // 32)
+    raise ValueError(wtype)
 PCIE5_X16_GBS = 32.0 * 16 * 128 / 130 / 8   # 63.0 GB/s per direction
 
 
@@ -230,9 +249,7 @@ def main():
         st2 = diff(m.stats(), before)
         if st2["page_ins"] != M or st2["distinct"] != D:
             raise RuntimeError("timing pass planned differently from the timed run")
-        w2b = wl.inter * wl.hidden * {"bf16": 2, "fp8": 1, "int4": 0.5, "int8": 1}[wl.wtype]
-        s2b = {"bf16": 0, "fp8": (wl.hidden // 128) * (wl.inter // 128) * 4,
-               "int4": wl.hidden * (wl.inter // 128) * 2, "int8": wl.hidden * (wl.inter // 128) * 2}[wl.wtype]
+        _, w2b, _, s2b = part_bytes(wl.wtype, wl.hidden, wl.inter)
         n_pi, ms_pi = tm["page_in"]
         n_dn, ms_dn = tm["down"]
         # the launches each stage brackets on this path
@@ -469,7 +486,7 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
     tokens = B * len(done) / L                      # a token passes all L layers
     t_total = t_moe + t_sim * (len(done) / L) / steps
     log("oracle MoE: %d (step, layer) pairs in %.2fs" % (len(done), t_moe))
-    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2}[wl.wtype]
+    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 2e-2}[wl.wtype]
     cpu = {"value": round(tokens / t_total, 5) if t_total > 0 else None, "unit": "tok/s", "cores": threads,
            "kind": "oracle",
            "sample": "%d (step, layer) pairs from decode steps %s (batch %d) through the fp32 unpaged oracle, "
@@ -504,10 +521,7 @@ def alg_bytes(kernel, wtype, hidden, inter, D, M, launches):
     expert blobs over the link, write them into slots and read the resident
     experts' gate/up weights; the down launches read every distinct expert's
     down weights.  Activations (< 1%) are left out."""
-    S = {"bf16": 2, "fp8": 1, "int4": 0.5, "int8": 1}[wtype]
-    w13, w2 = 2 * inter * hidden * S, inter * hidden * S
-    s13 = {"bf16": 0, "fp8": (2 * inter // 128) * (hidden // 128) * 4}.get(wtype, 2 * inter * (hidden // 128) * 2)
-    s2 = {"bf16": 0, "fp8": (hidden // 128) * (inter // 128) * 4}.get(wtype, hidden * (inter // 128) * 2)
+    w13, w2, s13, s2 = part_bytes(wtype, hidden, inter)
     blob = w13 + w2 + s13 + s2
     if kernel in ("step_a_kernel", "wave_a_kernel"):
         tot = 2 * M * blob + (D - M) * (w13 + s13)

@@ -8,7 +8,8 @@ streams.
 from ._binding import (  # noqa: F401
     LIB_PATH, PEError, lib,
     PE_OK, PE_ERR_INVALID_ARG, PE_ERR_UNSUPPORTED, PE_ERR_OOM_HOST_PIN, PE_ERR_OOM_DEVICE, PE_ERR_HIP,
-    PE_ERR_NOT_CAPTURABLE, PE_W_BF16, PE_W_FP8_B128, PE_W_INT4_G128, PE_W_INT8_G128, WTYPES,
+    PE_ERR_NOT_CAPTURABLE, PE_W_BF16, PE_W_FP8_B128, PE_W_INT4_G128, PE_W_INT8_G128, PE_W_MXFP4_B32,
+    WTYPES,
     PE_FLAG_PAGEIN_DMA, PE_FLAG_FORCE_HOST_PLAN, PE_FLAG_UNPAGED, SIGNATURES,
     pe_create, pe_destroy, pe_load_expert, pe_forward, pe_forward_rc, pe_reset_lru, pe_expert_bytes,
     pe_suggest_k, pe_max_captured_batch, pe_max_waves, pe_get_lru_state, pe_get_plan, pe_get_slot_map, pe_get_stats,

@@ -23,7 +23,9 @@ PE_W_BF16 = 0
 PE_W_FP8_B128 = 1
 PE_W_INT4_G128 = 2
 PE_W_INT8_G128 = 3
-WTYPES = {"bf16": PE_W_BF16, "fp8": PE_W_FP8_B128, "int4": PE_W_INT4_G128, "int8": PE_W_INT8_G128}
+PE_W_MXFP4_B32 = 4
+WTYPES = {"bf16": PE_W_BF16, "fp8": PE_W_FP8_B128, "int4": PE_W_INT4_G128, "int8": PE_W_INT8_G128,
+          "mxfp4": PE_W_MXFP4_B32}
 
 PE_FLAG_PAGEIN_DMA = 1
 PE_FLAG_FORCE_HOST_PLAN = 2

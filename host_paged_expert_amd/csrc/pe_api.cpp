@@ -71,6 +71,11 @@ bool blob_layout(int wtype, int H, int I, BlobLayout* b) {
       b->s13 = (size_t)2 * I * (H / 128) * 2;
       b->s2 = (size_t)H * (I / 128) * 2;
       break;
+    case PE_W_MXFP4_B32:
+      b->w13 = n13 / 2; b->w2 = n2 / 2;
+      b->s13 = (size_t)2 * I * (H / 32);
+      b->s2 = (size_t)H * (I / 32);
+      break;
     default: return false;
   }
   b->off_w13 = 0;
@@ -271,10 +276,23 @@ const char* pe_strerror(int status) {
 
 const char* pe_last_error(void) { return g_err.c_str(); }
 
+namespace {
+// The format's divisibility rule for hidden and inter: whole 16-byte chunks
+// per row (bf16: 8), whole scale groups (FP8 / int4 / int8: 128), and whole
+// 32-column MXFP4 blocks with 2-byte aligned row scales (64).
+int check_multiples(int wtype, int hidden, int inter) {
+  if (wtype == PE_W_MXFP4_B32) {
+    if (hidden % 64 || inter % 64) return fail(PE_ERR_INVALID_ARG, "MXFP4 needs hidden and inter multiples of 64");
+  } else if (wtype != PE_W_BF16 && (hidden % 128 || inter % 128)) {
+    return fail(PE_ERR_INVALID_ARG, "quantized formats need hidden and inter multiples of 128");
+  }
+  return PE_OK;
+}
+}  // namespace
+
 int pe_expert_bytes(int wtype, int hidden, int inter, size_t* algorithmic, size_t* copied) {
   if (hidden <= 0 || inter <= 0) return fail(PE_ERR_INVALID_ARG, "hidden and inter must be positive");
-  if (wtype != PE_W_BF16 && (hidden % 128 || inter % 128))
-    return fail(PE_ERR_INVALID_ARG, "quantized formats need hidden and inter multiples of 128");
+  if (int rc = check_multiples(wtype, hidden, inter)) return rc;
   BlobLayout b;
   if (!blob_layout(wtype, hidden, inter, &b)) return fail(PE_ERR_INVALID_ARG, "unknown weight type %d", wtype);
   if (algorithmic) *algorithmic = b.algorithmic;
@@ -315,10 +333,9 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     return fail(PE_ERR_INVALID_ARG, "hidden and inter must be positive multiples of 8");
   if (g.hidden > 4096 || g.inter > 4096)
     return fail(PE_ERR_UNSUPPORTED, "hidden and inter above 4096 are not supported");
-  if (g.wtype != PE_W_BF16 && g.wtype != PE_W_FP8_B128 && g.wtype != PE_W_INT4_G128 && g.wtype != PE_W_INT8_G128)
+  if (g.wtype < PE_W_BF16 || g.wtype > PE_W_MXFP4_B32)
     return fail(PE_ERR_INVALID_ARG, "unknown weight type %d", g.wtype);
-  if (g.wtype != PE_W_BF16 && (g.hidden % 128 || g.inter % 128))
-    return fail(PE_ERR_INVALID_ARG, "quantized formats need hidden and inter multiples of 128");
+  if (int rc = check_multiples(g.wtype, g.hidden, g.inter)) return rc;
   if (g.flags & ~(PE_FLAG_PAGEIN_DMA | PE_FLAG_FORCE_HOST_PLAN | PE_FLAG_UNPAGED))
     return fail(PE_ERR_INVALID_ARG, "unknown flags 0x%x", g.flags);
   if ((long long)g.max_tokens * g.top_k > (1 << 24))

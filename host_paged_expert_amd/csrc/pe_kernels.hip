@@ -648,9 +648,25 @@ template <> struct Fmt<PE_W_BF16> { static constexpr int VPC = 8; };        // v
 template <> struct Fmt<PE_W_FP8_B128> { static constexpr int VPC = 16; };
 template <> struct Fmt<PE_W_INT4_G128> { static constexpr int VPC = 32; };
 template <> struct Fmt<PE_W_INT8_G128> { static constexpr int VPC = 16; };
-// int4 and int8 keep one fp16 scale per row and 128 columns
-template <int FMT> constexpr bool kRowScales = FMT == PE_W_INT4_G128 || FMT == PE_W_INT8_G128;
+template <> struct Fmt<PE_W_MXFP4_B32> { static constexpr int VPC = 32; };
+// Per-row scales: int4 and int8 keep one fp16 scale per row and 128 columns,
+// MXFP4 one E8M0 byte per row and 32 columns (one 16-byte chunk).
+template <int FMT> constexpr bool kGroupScales = FMT == PE_W_INT4_G128 || FMT == PE_W_INT8_G128;
+template <int FMT> constexpr bool kRowScales = kGroupScales<FMT> || FMT == PE_W_MXFP4_B32;
+template <int FMT> constexpr int kScaleCols = FMT == PE_W_MXFP4_B32 ? 32 : 128;
+template <int FMT> constexpr int kScaleBytes = FMT == PE_W_MXFP4_B32 ? 1 : 2;
 }  // namespace
+
+// Byte offset of row `row`'s scales in the row-scale region of a matrix with C columns.
+template <int FMT>
+__host__ __device__ __forceinline__ size_t row_scale_off(size_t row, int C) {
+  return row * (size_t)(C / kScaleCols<FMT>) * kScaleBytes<FMT>;
+}
+
+// OCP E8M0 scale byte: 2^(e - 127) (e = 0 gives the fp32 subnormal 2^-127; 255 is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u) : e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23);
+}
 
 // Loads of one row's chunks for one lane: chunks lig, lig + LG, ... (at most
 // kMaxChunksInFlight per call, starting at chunk c0).
@@ -664,13 +680,15 @@ __device__ __forceinline__ void load_row(const uint4* __restrict__ row, int n_ch
 }
 
 // The scale of the 16-byte chunk starting at column `col` of a row: the FP8
-// block scale (one per 128 x 128 block) or the int4 group scale (one per row
-// and 128 columns); 1 for bf16 (unused).
+// block scale (one per 128 x 128 block), the int4 / int8 group scale (fp16,
+// one per row and 128 columns) or the MXFP4 block scale (E8M0, one per row and
+// 32 columns); 1 for bf16 (unused).  `s_row` points at the row's scales.
 template <int FMT>
 __device__ __forceinline__ float chunk_scale(const float* __restrict__ s_fp8_row,
-                                             const uint16_t* __restrict__ s_i4_row, int col) {
+                                             const uint8_t* __restrict__ s_row, int col) {
   if constexpr (FMT == PE_W_FP8_B128) return s_fp8_row[col >> 7];
-  else if constexpr (kRowScales<FMT>) return half_bits_to_f32(s_i4_row[col >> 7]);
+  else if constexpr (kGroupScales<FMT>) return half_bits_to_f32(reinterpret_cast<const uint16_t*>(s_row)[col >> 7]);
+  else if constexpr (FMT == PE_W_MXFP4_B32) return e8m0_to_f32(s_row[col >> 5]);
   else return 1.0f;
 }
 
@@ -691,11 +709,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Dot product of one 16-byte weight chunk (columns col .. col + VPC - 1) with m
 // <= MB token vectors [MB][C] (bf16; in LDS or global memory), accumulated into
 // acc in fp32 in a fixed order.  The chunk is decoded once into bf16 pairs
-// (exact for all three formats) and each token takes one v_dot2 per pair, pair
-// by pair; for FP8 and int4 the chunk's partial sum is then multiplied by its
-// scale `sc` and added.  int4 nibbles are decoded as (q - 8) / 16 (exact), so
+// (exact for every format) and each token takes one v_dot2 per pair, pair by
+// pair; for the quantized formats the chunk's partial sum is then multiplied by
+// its scale `sc` and added.  int4 nibbles are decoded as (q - 8) / 16 (exact), so
 // their partial sum is 1/16 of the true one and the scale is taken times 16:
-// the product is the same number.  Every GEMV path runs a row as these chunk
+// the product is the same number.  MXFP4 codes are decoded to their E2M1 values
+// (at most two significant bits: exact in bf16) and the chunk's one E8M0 scale
+// multiplies the partial sum.  Every GEMV path runs a row as these chunk
 // steps in ascending chunk order per lane, so a (token, row) dot product never
 // depends on the launch it ran in.
 template <int FMT, int MB>
@@ -754,6 +774,32 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, int col, const uint16_t
       for (int p = 0; p < 8; ++p) part = dot2_bf16(wb[p], xd[p], part);
       acc[t] = __builtin_fmaf(sc, part, acc[t]);
     }
+  } else if constexpr (FMT == PE_W_MXFP4_B32) {
+    // 32 E2M1 codes, element 2i the low nibble of byte i; v_cvt_scalef32_pk_bf16_fp4
+    // with scale 1 turns the two codes of one byte into a bf16 pair (low first)
+    uint32_t wb[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      wb[4 * v] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], 1.0f, 0));
+      wb[4 * v + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], 1.0f, 1));
+      wb[4 * v + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], 1.0f, 2));
+      wb[4 * v + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], 1.0f, 3));
+    }
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (t >= m) break;
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + t * C + col);
+      float part = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 xv = xp[v];
+        part = dot2_bf16(wb[4 * v], xv.x, part);
+        part = dot2_bf16(wb[4 * v + 1], xv.y, part);
+        part = dot2_bf16(wb[4 * v + 2], xv.z, part);
+        part = dot2_bf16(wb[4 * v + 3], xv.w, part);
+      }
+      acc[t] = __builtin_fmaf(sc, part, acc[t]);
+    }
   } else {
     // 32 nibbles, element 2i the low nibble of byte i; q ^ 8 read as a signed
     // 4-bit value is q - 8, which v_cvt_off_f32_i4 turns into (q - 8) / 16
@@ -791,7 +837,7 @@ template <int FMT, int MB>
 __device__ __forceinline__ void dot_row(const uint4 (&w)[kMaxChunksInFlight], int n_ch, int c0, int LG,
                                         const uint16_t* __restrict__ xs, int C, int m,
                                         const float* __restrict__ s_fp8_row,   // fp8: scales of this row's 128-row block
-                                        const uint16_t* __restrict__ s_i4_row, // int4: scales of this row
+                                        const uint8_t* __restrict__ s_row,     // per-row formats: this row's scales
                                         float (&acc)[MB]) {
   constexpr int VPC = Fmt<FMT>::VPC;
 #pragma unroll
@@ -799,7 +845,7 @@ __device__ __forceinline__ void dot_row(const uint4 (&w)[kMaxChunksInFlight], in
     const int c = c0 + q * LG;
     if (c >= n_ch) break;
     const int col = c * VPC;
-    dot_chunk<FMT, MB>(w[q], col, xs, C, m, chunk_scale<FMT>(s_fp8_row, s_i4_row, col), acc);
+    dot_chunk<FMT, MB>(w[q], col, xs, C, m, chunk_scale<FMT>(s_fp8_row, s_row, col), acc);
   }
 }
 
@@ -946,7 +992,7 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
   const uint8_t* blob = a.slots + (size_t)it.slot * a.slot_stride;
   const uint4* W13 = reinterpret_cast<const uint4*>(blob + a.off_w13);
   const float* S13f = reinterpret_cast<const float*>(blob + a.off_s13);
-  const uint16_t* S13h = reinterpret_cast<const uint16_t*>(blob + a.off_s13);
+  const uint8_t* S13b = blob + a.off_s13;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
   int i[NR];
@@ -978,8 +1024,8 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
       for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
       const float* sgf = S13f + (size_t)(ir >> 7) * (H / 128);
       const float* suf = S13f + (size_t)(ru >> 7) * (H / 128);
-      const uint16_t* sgh = S13h + (size_t)ir * (H / 128);
-      const uint16_t* suh = S13h + (size_t)ru * (H / 128);
+      const uint8_t* sgh = S13b + row_scale_off<FMT>(ir, H);
+      const uint8_t* suh = S13b + row_scale_off<FMT>(ru, H);
       for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
         dot_row<FMT, MB>(wg[r], n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
         dot_row<FMT, MB>(wu[r], n_ch, c0, LG, xs, H, mb, suf, suh, u);
@@ -1018,7 +1064,7 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
   const uint8_t* blob = a.slots + (size_t)it.slot * a.slot_stride;
   const uint4* W2 = reinterpret_cast<const uint4*>(blob + a.off_w2);
   const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
-  const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
+  const uint8_t* S2b = blob + a.off_s2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
   const int n0 = bx * rows_per_block + 2 * (wv * groups + grp);   // rows n0, n0 + 1
@@ -1040,10 +1086,10 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
     for (int t = 0; t < MB; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
     for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
       dot_row<FMT, MB>(w0, n_ch, c0, LG, hs, I, mb, S2f + (size_t)(n0 >> 7) * (I / 128),
-                       S2h + (size_t)n0 * (I / 128), y0);
+                       S2b + row_scale_off<FMT>(n0, I), y0);
       if (act1)
         dot_row<FMT, MB>(w1, n_ch, c0, LG, hs, I, mb, S2f + (size_t)((n0 + 1) >> 7) * (I / 128),
-                         S2h + (size_t)(n0 + 1) * (I / 128), y1);
+                         S2b + row_scale_off<FMT>(n0 + 1, I), y1);
       if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
       load_row(r0, n_ch, c0 + LG * kMaxChunksInFlight, LG, w0);
       if (act1) load_row(r1, n_ch, c0 + LG * kMaxChunksInFlight, LG, w1);
@@ -1086,17 +1132,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, G
 }
 
 // LDS for the gate/up scales one stream_gate_up_rows block stages (gate rows in
-// the first half, up rows in the second): at most 512 bytes each for hidden <=
-// 4096 (int4: rows_per_block * hidden / 128 fp16; FP8: one 128-row block row).
-constexpr size_t kStreamScaleLds = 1024;
+// the first half, up rows in the second): at most 1024 bytes each for hidden <=
+// 4096 (int4 / int8: rows_per_block * hidden / 128 fp16, at most 512; MXFP4:
+// rows_per_block * hidden / 32 bytes, at most 1024; FP8: one 128-row block row).
+constexpr size_t kStreamScaleLds = 2048;
 
 // Gate/up row block gi of a missing expert, paged in and projected in one pass:
 // rows i of the block (gemv_gate_up_kernel's geometry) are read from the mapped
 // host row `src`, stored into the slot `dst` and, as each 16-byte chunk arrives,
 // dotted with the expert's m token vectors (entries `ent`, staged in LDS `xs`),
-// one chunk per row in flight ahead of the arithmetic.  The block's FP8 / int4
-// scales are staged once through LDS `s_sc` (one contiguous read per side) and
-// stored into the slot as well.  The lane's chunk order and the reduction are
+// one chunk per row in flight ahead of the arithmetic.  The block's scales are
+// staged once through LDS `s_sc` (one contiguous read per side, in 2-byte units)
+// and stored into the slot as well.  The lane's chunk order and the reduction are
 // those of gate_up_block, so h is bit-identical to a gate/up projection read
 // back from the slot.
 template <int FMT, int MB>
@@ -1118,9 +1165,9 @@ __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, cons
   size_t og = 0, ou = 0;
   int nb = 0;
   if constexpr (kRowScales<FMT>) {
-    og = (size_t)i0 * (H / 128) * 2;
-    ou = (size_t)(I + i0) * (H / 128) * 2;
-    nb = min(g.rows_per_block, I - i0) * (H / 128) * 2;
+    og = row_scale_off<FMT>(i0, H);
+    ou = row_scale_off<FMT>(I + i0, H);
+    nb = (int)row_scale_off<FMT>(min(g.rows_per_block, I - i0), H);
   } else if constexpr (FMT == PE_W_FP8_B128) {
     og = (size_t)(i0 >> 7) * (H / 128) * 4;
     ou = (size_t)((I + i0) >> 7) * (H / 128) * 4;
@@ -1129,8 +1176,8 @@ __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, cons
   const bool store_sc = kRowScales<FMT> || (i0 & 127) == 0;   // one block per FP8 block row
   const float* sgf = reinterpret_cast<const float*>(s_sc);
   const float* suf = reinterpret_cast<const float*>(s_sc + kStreamScaleLds / 2);
-  const uint16_t* sgh = reinterpret_cast<const uint16_t*>(s_sc) + (size_t)(i - i0) * (H / 128);
-  const uint16_t* suh = reinterpret_cast<const uint16_t*>(s_sc + kStreamScaleLds / 2) + (size_t)(i - i0) * (H / 128);
+  const uint8_t* sgh = reinterpret_cast<const uint8_t*>(s_sc) + row_scale_off<FMT>(i - i0, H);
+  const uint8_t* suh = reinterpret_cast<const uint8_t*>(s_sc + kStreamScaleLds / 2) + row_scale_off<FMT>(i - i0, H);
   // the first token batch also stores the rows (tb == 0 runs even for m == 0)
   for (int tb = 0; tb == 0 || tb < m; tb += MB) {
     const int mb = max(0, min(MB, m - tb));
@@ -1301,7 +1348,7 @@ __device__ __forceinline__ void fetch_down_rows(const ExpertArgs& a, const uint8
   const int I = a.I;
   const uint4* W2 = reinterpret_cast<const uint4*>(blob + a.off_w2);
   const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
-  const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
+  const uint8_t* S2b = blob + a.off_s2;
   if (act0) load_row(W2 + (size_t)n0 * n_ch, n_ch, c0, LG, r.w0);
   if (act1) load_row(W2 + (size_t)(n0 + 1) * n_ch, n_ch, c0, LG, r.w1);
 #pragma unroll
@@ -1309,9 +1356,9 @@ __device__ __forceinline__ void fetch_down_rows(const ExpertArgs& a, const uint8
     const int c = c0 + q * LG;
     r.s0[q] = r.s1[q] = 1.0f;
     if (c >= n_ch) continue;
-    if (act0) r.s0[q] = chunk_scale<FMT>(S2f + (size_t)(n0 >> 7) * (I / 128), S2h + (size_t)n0 * (I / 128), c * VPC);
+    if (act0) r.s0[q] = chunk_scale<FMT>(S2f + (size_t)(n0 >> 7) * (I / 128), S2b + row_scale_off<FMT>(n0, I), c * VPC);
     if (act1)
-      r.s1[q] = chunk_scale<FMT>(S2f + (size_t)((n0 + 1) >> 7) * (I / 128), S2h + (size_t)(n0 + 1) * (I / 128),
+      r.s1[q] = chunk_scale<FMT>(S2f + (size_t)((n0 + 1) >> 7) * (I / 128), S2b + row_scale_off<FMT>(n0 + 1, I),
                                  c * VPC);
   }
 }
@@ -1461,6 +1508,7 @@ static int vpc_of(int wtype) {
   return wtype == PE_W_BF16 ? Fmt<PE_W_BF16>::VPC
          : wtype == PE_W_FP8_B128 ? Fmt<PE_W_FP8_B128>::VPC
          : wtype == PE_W_INT8_G128 ? Fmt<PE_W_INT8_G128>::VPC
+         : wtype == PE_W_MXFP4_B32 ? Fmt<PE_W_MXFP4_B32>::VPC
                                    : Fmt<PE_W_INT4_G128>::VPC;
 }
 
@@ -1499,6 +1547,12 @@ static size_t lean_head(const ExpertArgs& a) { return a.lean ? lean_lds_bytes(a.
       else { constexpr int M_ = 8; CALL; }                                        \
     } else if ((wtype) == PE_W_INT8_G128) {                                       \
       constexpr int F_ = PE_W_INT8_G128;                                          \
+      if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
+      else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
+      else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
+      else { constexpr int M_ = 8; CALL; }                                        \
+    } else if ((wtype) == PE_W_MXFP4_B32) {                                       \
+      constexpr int F_ = PE_W_MXFP4_B32;                                          \
       if (mb == 1) { constexpr int M_ = 1; CALL; }                                \
       else if (mb == 2) { constexpr int M_ = 2; CALL; }                           \
       else if (mb == 4) { constexpr int M_ = 4; CALL; }                           \
@@ -1581,8 +1635,11 @@ void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, i
 // LDS (rows padded by 8 bf16 against bank conflicts).  FP8 and int4 weights are
 // decoded into LDS as exact bf16 (every e4m3 value and every nibble - 8 is a
 // bf16 number); their block / group scale multiplies the fp32 partial product
-// of each 128-wide K block.  Every output element's arithmetic depends only on
-// its own token row and weight row, never on the other rows of the tile.
+// of each 128-wide K block.  MXFP4 codes are decoded with their 32-column E8M0
+// scale applied (an E2M1 value times a power of two: exact in bf16 within
+// bf16's range), so its K blocks take no scale.  Every output element's
+// arithmetic depends only on its own token row and weight row, never on the
+// other rows of the tile.
 
 namespace {
 constexpr int kMfmaThreads = 256;
@@ -1594,9 +1651,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 }  // namespace
 
 // Decode one 16-byte chunk of weights of format FMT into bf16 in LDS at `dst`
-// (VPC values); returns nothing, writes VPC/8 16-byte LDS words.
+// (VPC values); returns nothing, writes VPC/8 16-byte LDS words.  `sc` (MXFP4
+// only) is the chunk's block scale, applied here.
 template <int FMT>
-__device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst) {
+__device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst, float sc) {
   if constexpr (FMT == PE_W_BF16) {
     *reinterpret_cast<uint4*>(dst) = w;
   } else if constexpr (FMT == PE_W_FP8_B128) {
@@ -1625,6 +1683,21 @@ __device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst) {
     }
     reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
     reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else if constexpr (FMT == PE_W_MXFP4_B32) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[16];
+    // e2m1 * 2^k has at most two significant bits: the top half of the fp32 is exact
+    auto top = [sc](auto v) { return (__float_as_uint(v[0] * sc) >> 16) | (__float_as_uint(v[1] * sc) & 0xFFFF0000u); };
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      o[4 * p] = top(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[p], 1.0f, 0));
+      o[4 * p + 1] = top(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[p], 1.0f, 1));
+      o[4 * p + 2] = top(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[p], 1.0f, 2));
+      o[4 * p + 3] = top(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[p], 1.0f, 3));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<uint4*>(dst)[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
   } else {
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     uint32_t o[16];
@@ -1644,19 +1717,21 @@ __device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst) {
 }
 
 // Stage kNT weight rows [row0, row0 + kNT) x K block kb of a row-major matrix with
-// C columns into LDS (bf16, padded rows).
+// C columns into LDS (bf16, padded rows); S is the matrix's row-scale region
+// (read for MXFP4 only).
 template <int FMT>
-__device__ __forceinline__ void stage_weights(uint16_t* sB, const uint8_t* __restrict__ W, int C, int row0,
-                                              int kb) {
+__device__ __forceinline__ void stage_weights(uint16_t* sB, const uint8_t* __restrict__ W,
+                                              const uint8_t* __restrict__ S, int C, int row0, int kb) {
   constexpr int VPC = Fmt<FMT>::VPC;
   constexpr int CPR = kKB / VPC;                       // chunks per row per stage
-  const size_t row_bytes = (size_t)C * (FMT == PE_W_BF16 ? 2 : (FMT == PE_W_FP8_B128 || FMT == PE_W_INT8_G128) ? 1 : 0) +
-                           (FMT == PE_W_INT4_G128 ? (size_t)C / 2 : 0);
+  const size_t row_bytes = (size_t)(C / VPC) * 16;   // 16 bytes per VPC columns
   const uint4* base = reinterpret_cast<const uint4*>(W);
   for (int i = threadIdx.x; i < kNT * CPR; i += kMfmaThreads) {
     const int r = i / CPR, c = i - r * CPR;
     const size_t chunk = ((size_t)(row0 + r) * row_bytes) / 16 + (size_t)kb * CPR + c;
-    decode_chunk_to_lds<FMT>(base[chunk], sB + r * kLdsRow + c * VPC);
+    float sc = 1.0f;
+    if constexpr (FMT == PE_W_MXFP4_B32) sc = chunk_scale<FMT>(nullptr, S + row_scale_off<FMT>(row0 + r, C), (kb * CPR + c) * VPC);
+    decode_chunk_to_lds<FMT>(base[chunk], sB + r * kLdsRow + c * VPC, sc);
   }
 }
 
@@ -1701,8 +1776,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
       if (tok >= 0) v = reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + kb * kKB)[c];
       *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = v;
     }
-    stage_weights<FMT>(sG, W13, H, n0, kb);
-    stage_weights<FMT>(sU, W13, H, I + n0, kb);
+    stage_weights<FMT>(sG, W13, blob + a.off_s13, H, n0, kb);
+    stage_weights<FMT>(sU, W13, blob + a.off_s13, H, I + n0, kb);
     __syncthreads();
     f32x4_t pg[2], pu[2];
 #pragma unroll
@@ -1725,7 +1800,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     if constexpr (FMT == PE_W_FP8_B128) {
       sg = S13f[(size_t)(n0 >> 7) * (H / 128) + kb];
       su = S13f[(size_t)((I + n0) >> 7) * (H / 128) + kb];
-    } else if constexpr (kRowScales<FMT>) {
+    } else if constexpr (kGroupScales<FMT>) {
       sg = half_bits_to_f32(S13h[(size_t)ncol * (H / 128) + kb]);
       su = half_bits_to_f32(S13h[(size_t)(I + ncol) * (H / 128) + kb]);
     }
@@ -1733,7 +1808,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (FMT == PE_W_BF16) {
+        if constexpr (FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32) {
           accg[h][i] += pg[h][i];
           accu[h][i] += pu[h][i];
         } else {
@@ -1787,7 +1862,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
       if (r < rows) v = reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB)[c];
       *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = v;
     }
-    stage_weights<FMT>(sB, W2, I, n0, kb);
+    stage_weights<FMT>(sB, W2, blob + a.off_s2, I, n0, kb);
     __syncthreads();
     f32x4_t p[2];
 #pragma unroll
@@ -1806,12 +1881,12 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
     }
     float sc = 1.f;
     if constexpr (FMT == PE_W_FP8_B128) sc = S2f[(size_t)(n0 >> 7) * (I / 128) + kb];
-    else if constexpr (kRowScales<FMT>) sc = half_bits_to_f32(S2h[(size_t)ncol * (I / 128) + kb]);
+    else if constexpr (kGroupScales<FMT>) sc = half_bits_to_f32(S2h[(size_t)ncol * (I / 128) + kb]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (FMT == PE_W_BF16) acc[h][i] += p[h][i];
+        if constexpr (FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32) acc[h][i] += p[h][i];
         else acc[h][i] = __builtin_fmaf(sc, p[h][i], acc[h][i]);
       }
   }
@@ -1834,6 +1909,7 @@ void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t 
   if (wtype == PE_W_BF16) mfma_gate_up_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_FP8_B128) mfma_gate_up_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_INT8_G128) mfma_gate_up_kernel<PE_W_INT8_G128><<<grid, kMfmaThreads, 0, s>>>(a);
+  else if (wtype == PE_W_MXFP4_B32) mfma_gate_up_kernel<PE_W_MXFP4_B32><<<grid, kMfmaThreads, 0, s>>>(a);
   else mfma_gate_up_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
 }
 
@@ -1843,6 +1919,7 @@ void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) 
   if (wtype == PE_W_BF16) mfma_down_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_FP8_B128) mfma_down_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_INT8_G128) mfma_down_kernel<PE_W_INT8_G128><<<grid, kMfmaThreads, 0, s>>>(a);
+  else if (wtype == PE_W_MXFP4_B32) mfma_down_kernel<PE_W_MXFP4_B32><<<grid, kMfmaThreads, 0, s>>>(a);
   else mfma_down_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
 }
 

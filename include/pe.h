@@ -52,6 +52,8 @@ extern "C" {
 #define PE_W_FP8_B128   1   /* OCP e4m3fn codes, one fp32 multiplier per 128x128  */
 #define PE_W_INT4_G128  2   /* symmetric int4, one fp16 scale per 128 inputs/row  */
 #define PE_W_INT8_G128  3   /* symmetric int8 (GPTQ int8), fp16 scale per 128     */
+#define PE_W_MXFP4_B32  4   /* OCP MXFP4: E2M1 codes, one E8M0 scale per 32 inputs
+                               of a row (the blog's added formats, gpt-oss-20b)   */
 
 /* ---- configuration flags --------------------------------------------- */
 #define PE_FLAG_PAGEIN_DMA      1u  /* host-planned steps copy with hipMemcpyAsync
@@ -68,8 +70,9 @@ typedef struct {
   int top_k;          /* routed experts per token k (1..E)                   */
   int num_resident;   /* slots per layer K, top_k <= K <= E (ignored, = E,
                          with PE_FLAG_UNPAGED)                               */
-  int hidden;         /* H, multiple of 128 (of 8 for bf16)                  */
-  int inter;          /* expert SwiGLU intermediate I, multiple of 128 (8)   */
+  int hidden;         /* H <= 4096, multiple of 128 (of 8 for bf16, of 64
+                         for MXFP4)                                          */
+  int inter;          /* expert SwiGLU intermediate I, same rule as H        */
   int max_tokens;     /* largest T passed to pe_forward                      */
   int device;         /* HIP device ordinal                                  */
   int wtype;          /* PE_W_*                                              */

@@ -89,12 +89,12 @@ def dequant_int8_g128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
 def e2m1_to_f32(codes: np.ndarray) -> np.ndarray:
     """OCP 4-bit float E2M1: sign bit, 2 exponent bits with bias 1, 1 mantissa
     bit; exponent 0 is subnormal (m/2); no infinities or NaN; largest 6."""
-    c = np.asarray(codes, np.int64) & 0xF
+    c = np.arange(16)                      # the value of each of the 16 codes, then a lookup
     sign = np.where(c & 0x8, -1.0, 1.0)
     e = (c >> 1) & 0x3
     m = c & 0x1
     val = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.power(2.0, e - 1))
-    return (sign * val).astype(np.float32)
+    return (sign * val).astype(np.float32)[np.asarray(codes, np.int64) & 0xF]
 
 
 def e8m0_to_f32(codes: np.ndarray) -> np.ndarray:

@@ -1,5 +1,6 @@
 """GPU parity at the workloads' full sizes (48 layers, E=128, top-8, H=2048,
-I=768, every decode step of the window), launched as bench.py times them:
+I=768; MXFP4 at the gpt-oss-20b expert shape, 24 layers, E=32, top-4,
+H=I=2880; every decode step of the window), launched as bench.py times them:
 device-planned workloads as one replayed hipGraph per step, host-planned ones
 eagerly (harness.DecodeRunner).
 
@@ -28,8 +29,11 @@ from oracle.lru import LayerLRU
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2}
-SAMPLE_LAYERS = (0, 23, 47)
+TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 2e-2}
+
+
+def _sample_layers(L):
+    return (0, L // 2, L - 1)
 
 
 def _say(msg):
@@ -102,7 +106,8 @@ def _first_diff(a, b):
     return ne[0].tolist() if len(ne) else None
 
 
-@pytest.mark.parametrize("name", ["decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4"])
+@pytest.mark.parametrize("name", ["decode_bf16_k40_b1", "decode_fp8_k40_b4", "decode_int4_k26_b4",
+                                  "decode_mxfp4_k16_b1"])
 def test_fullsize_decode(name):
     wl = synth.WORKLOADS[name]
     _say("case %s: %d steps x %d layers, batch %d" % (name, wl.steps, wl.layers, wl.batch))
@@ -132,11 +137,11 @@ def test_fullsize_decode(name):
     got = harness.bf16_bits(out_p[sorted(check_steps)])
     for i, s in enumerate(sorted(check_steps)):
         xr = formats.bf16_to_f32(harness.bf16_bits(x[s]))
-        for l in SAMPLE_LAYERS:
+        for l in _sample_layers(wl.layers):
             ref = moe.moe_layer(xr, r["decode_ids"][s, l], r["decode_w"][s, l], _expert_fn(wl, l))
             _close(got[i, l], ref, wl.wtype, "%s step %d layer %d" % (name, s, l))
     _say("%s: %d sampled (step, layer) outputs within %g of the oracle" %
-         (name, len(check_steps) * len(SAMPLE_LAYERS), TOL[wl.wtype]))
+         (name, len(check_steps) * 3, TOL[wl.wtype]))
     paged.close()
     unpaged.close()
 
@@ -183,7 +188,7 @@ def test_fullsize_prefill_then_decode():
         _close(harness.bf16_bits(pp[l])[rows], ref, wl.wtype, "prefill layer %d" % l)
     for s in (0, wl.steps - 1):
         xd = formats.bf16_to_f32(harness.bf16_bits(x[s]))
-        for l in SAMPLE_LAYERS:
+        for l in _sample_layers(L):
             ref = moe.moe_layer(xd, r["decode_ids"][s, l], r["decode_w"][s, l], _expert_fn(wl, l))
             _close(harness.bf16_bits(pd[s, l]), ref, wl.wtype, "continuation step %d layer %d" % (s, l))
     _say("sampled prefill tokens and continuation outputs within %g of the oracle" % TOL[wl.wtype])

@@ -2,7 +2,7 @@
 
 - Plans, LRU state and slot maps are bit-exact against the oracle's simulator.
 - Outputs are within max|gpu - ref| <= 1e-2 * max|ref| (bf16, FP8, int8) or
-  2e-2 (int4) of the oracle's fp32 unpaged layer.
+  2e-2 (int4, MXFP4) of the oracle's fp32 unpaged layer.
 - Paged output is bit-identical to an unpaged run of the same kernels
   (PE_FLAG_UNPAGED: K = E, every expert resident), for every K.
 """
@@ -19,7 +19,7 @@ from oracle.lru import LayerLRU
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2}
+TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 2e-2}
 
 
 def _expert_fn(wl, layer):
@@ -120,7 +120,7 @@ def test_tiny_paged_bit_identical_to_unpaged_for_every_k():
 SMALL = dict(layers=2, experts=16, top_k=4, hidden=256, inter=256, steps=10)
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8", "mxfp4"])
 @pytest.mark.parametrize("batch,K", [(1, 6), (3, 6), (2, 8)])
 def test_small_formats_paged_vs_oracle_and_unpaged(wtype, batch, K):
     """Device-planned (batch*k <= K) and host-planned multi-wave (batch*k > K)
@@ -153,10 +153,11 @@ def test_many_experts_take_the_general_planner(batch):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "int4"])
+@pytest.mark.parametrize("wtype", ["bf16", "int4", "mxfp4"])
 def test_ragged_shapes(wtype):
-    """Row lengths that leave lanes idle and token batches past the GEMV batch."""
-    H, I = (384, 640) if wtype == "int4" else (200, 72)
+    """Row lengths that leave lanes idle and token batches past the GEMV batch
+    (MXFP4: multiples of 64 but not of 128, GEMV only)."""
+    H, I = {"int4": (384, 640), "mxfp4": (320, 448), "bf16": (200, 72)}[wtype]
     wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=12, top_k=3, resident=12, hidden=H, inter=I,
                         wtype=wtype, batch=5, steps=3)
     print("case ragged %s H=%d I=%d" % (wtype, H, I), flush=True)

@@ -15,7 +15,7 @@ from oracle.lru import LayerLRU
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2}
+TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 2e-2}
 
 
 def _expert_fn(wl, layer):
@@ -82,7 +82,7 @@ def _prefill_run(wl, flags=0, check=True):
     return res, st
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8", "mxfp4"])
 def test_prefill_multi_wave_mfma_vs_oracle_and_unpaged(wtype):
     wl = synth.workload("prefill_bf16_k92", layers=2, experts=16, top_k=4, resident=6, hidden=256, inter=384,
                         wtype=wtype, prefill_tokens=100, steps=4)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(pe.SIGNATURES)
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8", "mxfp4"])
 @pytest.mark.parametrize("H,I", [(2048, 768), (256, 128), (1024, 512)])
 def test_expert_bytes_match_oracle(wtype, H, I):
     alg, copied = pe.pe_expert_bytes(wtype, H, I)
@@ -45,6 +45,11 @@ def test_expert_bytes_pages_sizes():
 def test_expert_bytes_rejects_bad_shapes():
     with pytest.raises(pe.PEError):
         pe.pe_expert_bytes("fp8", 2048, 700)
+    with pytest.raises(pe.PEError):
+        pe.pe_expert_bytes("int4", 2880, 2880)          # group-128 formats need multiples of 128
+    with pytest.raises(pe.PEError):
+        pe.pe_expert_bytes("mxfp4", 2880 + 32, 2880)    # MXFP4 needs multiples of 64
+    assert pe.pe_expert_bytes("mxfp4", 2880, 2880)[0] == sizes.expert_bytes("mxfp4", 2880, 2880)
     with pytest.raises(pe.PEError):
         pe.pe_expert_bytes(7, 2048, 768)
 
