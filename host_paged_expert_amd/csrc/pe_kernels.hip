@@ -17,6 +17,8 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "../../include/pe.h"
 #include "pe_kernels.h"
@@ -975,14 +977,16 @@ __device__ __forceinline__ size_t gemv_lds_head(const ExpertArgs& a) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Gate/up projection + SwiGLU of one workgroup: used expert `by`, NR blocks of
-// intermediate rows from bx * NR * rows_per_block; every lane group takes one
+// Gate/up projection + SwiGLU of one workgroup: used expert `by`, `nr` blocks of
+// intermediate rows from bx * nr * rows_per_block; every lane group takes one
 // row i of each block and computes h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).
-// The weight loads of all the group's rows are issued before the token vectors
-// are staged in LDS.  NR only changes how many rows a workgroup covers, not a
-// row's arithmetic.
-template <int FMT, int MB, int NR = 1>
-__device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds) {
+// The first block's weight loads are issued before the token vectors are
+// staged in LDS; the blocks then run one after another on one set of weight
+// registers, so `nr` changes neither a row's arithmetic nor the registers a
+// lane needs (a launch picks it so that all its workgroups are resident).
+template <int FMT, int MB>
+__device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds,
+                              int nr = 1) {
   GemvItem it;
   if (!gemv_item(a, by, it, lds)) return;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + gemv_lds_head(a));   // [MB][H]
@@ -995,30 +999,26 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
   const uint8_t* S13b = blob + a.off_s13;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  int i[NR];
-  bool active[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    i[r] = (bx * NR + r) * rows_per_block + wv * groups + grp;    // this group's rows
-    active[r] = i[r] < I;
-  }
+  const int i0 = bx * nr * rows_per_block + wv * groups + grp;     // this group's row in the first block
   const int32_t* ent = it.ent;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
-    uint4 wg[NR][kMaxChunksInFlight], wu[NR][kMaxChunksInFlight];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-      if (active[r]) {
-        load_row(W13 + (size_t)i[r] * n_ch, n_ch, lig, LG, wg[r]);
-        load_row(W13 + (size_t)(I + i[r]) * n_ch, n_ch, lig, LG, wu[r]);
-      }
+    uint4 wg[kMaxChunksInFlight], wu[kMaxChunksInFlight];
+    if (i0 < I) {
+      load_row(W13 + (size_t)i0 * n_ch, n_ch, lig, LG, wg);
+      load_row(W13 + (size_t)(I + i0) * n_ch, n_ch, lig, LG, wu);
+    }
     __syncthreads();
     stage_rows(xs, a.x, H, ent + tb, mb, a.k);
     __syncthreads();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (!active[r]) continue;
-      const int ir = i[r], ru = I + ir;
+#pragma unroll 1
+    for (int r = 0; r < nr; ++r) {
+      const int ir = i0 + r * rows_per_block, ru = I + ir;
+      if (ir >= I) break;
+      if (r > 0) {
+        load_row(W13 + (size_t)ir * n_ch, n_ch, lig, LG, wg);
+        load_row(W13 + (size_t)ru * n_ch, n_ch, lig, LG, wu);
+      }
       float g[MB], u[MB];
 #pragma unroll
       for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
@@ -1027,11 +1027,11 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
       const uint8_t* sgh = S13b + row_scale_off<FMT>(ir, H);
       const uint8_t* suh = S13b + row_scale_off<FMT>(ru, H);
       for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
-        dot_row<FMT, MB>(wg[r], n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
-        dot_row<FMT, MB>(wu[r], n_ch, c0, LG, xs, H, mb, suf, suh, u);
+        dot_row<FMT, MB>(wg, n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
+        dot_row<FMT, MB>(wu, n_ch, c0, LG, xs, H, mb, suf, suh, u);
         if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
-        load_row(W13 + (size_t)ir * n_ch, n_ch, c0 + LG * kMaxChunksInFlight, LG, wg[r]);
-        load_row(W13 + (size_t)ru * n_ch, n_ch, c0 + LG * kMaxChunksInFlight, LG, wu[r]);
+        load_row(W13 + (size_t)ir * n_ch, n_ch, c0 + LG * kMaxChunksInFlight, LG, wg);
+        load_row(W13 + (size_t)ru * n_ch, n_ch, c0 + LG * kMaxChunksInFlight, LG, wu);
       }
       group_reduce<MB>(g, LG);
       group_reduce<MB>(u, LG);
@@ -1319,17 +1319,18 @@ __global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, Gemv
 // decides from the same state copy by the same rules, and no workgroup waits
 // for another.
 template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs a, GemvGeom g) {
+__global__ __launch_bounds__(kGemvThreads) void step_a_kernel(PlanArgs p, int P, ExpertArgs a, GemvGeom g,
+                                                              int nr) {
   extern __shared__ __align__(16) char lds[];
   if ((int)blockIdx.x < P) {
     stream_in<FMT, MB>(p, a, g, blockIdx.x, P, lds, copier_plan(p, lds));
   } else if ((int)blockIdx.x == P) {
     plan_page_in_block(p, P, P, lds);
   } else {
-    // two row blocks per workgroup, so every workgroup of the launch is resident at once
-    const int gx2 = (g.gx + 1) / 2;
+    // nr row blocks per workgroup, so every workgroup of the launch is resident at once
+    const int gxn = (g.gx + nr - 1) / nr;
     const int b = blockIdx.x - P - 1;
-    gate_up_block<FMT, MB, 2>(a, b % gx2, b / gx2, g.LG, g.rows_per_block, lds);
+    gate_up_block<FMT, MB>(a, b % gxn, b / gxn, g.LG, g.rows_per_block, lds, nr);
   }
 }
 
@@ -1530,6 +1531,26 @@ static GemvGeom down_geom(int wtype, const ExpertArgs& a) {
 
 static size_t lean_head(const ExpertArgs& a) { return a.lean ? lean_lds_bytes(a.T * a.k) : 0; }
 
+// Workgroups of kGemvThreads threads with `lds` bytes of LDS each that the
+// device holds at once (per-CU occupancy times CUs), cached per kernel and LDS
+// size; 0 if the runtime cannot tell.
+static int resident_blocks(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, lds);
+  auto hit = cache.find(key);
+  if (hit != cache.end()) return hit->second;
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kGemvThreads, lds) != hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    per_cu = cus = 0;
+  }
+  return cache[key] = per_cu * cus;
+}
+
 // Instantiate a kernel template over the weight format and token batch.
 #define PE_DISPATCH(wtype, mb, CALL)                                              \
   do {                                                                            \
@@ -1593,8 +1614,15 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const GemvGeom g = gate_up_geom(wtype, a);
   const size_t copier = copier_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds + (size_t)mb * a.H * 2;
   const size_t lds = std::max(std::max(copier, plan_lds_bytes(d.E, d.K, n)), lean_head(a) + (size_t)mb * a.H * 2);
-  const int blocks = P + 1 + (g.gx + 1) / 2 * items;
-  PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g)));
+  // Row blocks per gate/up workgroup: the fewest that leave every workgroup of
+  // the launch resident at once (a second dispatch round would start its
+  // workgroups only after the first ones end).
+  int resident = 0;
+  PE_DISPATCH(wtype, mb, (resident = resident_blocks(reinterpret_cast<const void*>(&step_a_kernel<F_, M_>), lds)));
+  int nr = resident > 0 ? 1 : 2;
+  while (resident > 0 && nr < g.gx && P + 1 + ceil_div(g.gx, nr) * items > resident) ++nr;
+  const int blocks = P + 1 + ceil_div(g.gx, nr) * items;
+  PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g, nr)));
 }
 
 void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int P, const uint8_t* host_rows,
