@@ -154,6 +154,35 @@ def test_many_experts_take_the_general_planner(batch):
 
 
 @pytest.mark.parametrize("wtype", ["bf16", "int4", "mxfp4"])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_largest_hidden_and_inter(wtype, batch):
+    """H = I = 4096, the largest the library takes (a bf16 expert is 100 MB):
+    device-planned steps (batch 1) and host-planned ones (batch 3: 6 entries >
+    K = 3, mostly two waves), against the oracle and an unpaged run."""
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=8, top_k=2, resident=3, hidden=4096, inter=4096,
+                        wtype=wtype, batch=batch, steps=4)
+    print("case H=I=4096 %s batch %d" % (wtype, batch), flush=True)
+    got, st = _run_decode(wl)
+    assert st["host_planned" if batch * wl.top_k > wl.resident else "device_planned"] == wl.steps
+    ref, _ = _run_decode(wl, flags=pe.PE_FLAG_UNPAGED, check_oracle=False)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("batch", [4, 9])
+def test_most_experts(batch):
+    """E = 1024, the largest expert count: 32 entries fill K = 32 exactly (one
+    device-planned wave); 72 entries over ~55 distinct experts take two
+    host-planned waves."""
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=1024, top_k=8, resident=32, hidden=128, inter=128,
+                        batch=batch, steps=6)
+    print("case E=1024 batch %d" % batch, flush=True)
+    got, st = _run_decode(wl)
+    assert st["device_planned" if batch * wl.top_k <= wl.resident else "host_planned"] == wl.steps
+    ref, _ = _run_decode(wl, flags=pe.PE_FLAG_UNPAGED, check_oracle=False)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int4", "mxfp4"])
 def test_ragged_shapes(wtype):
     """Row lengths that leave lanes idle and token batches past the GEMV batch
     (MXFP4: multiples of 64 but not of 128, GEMV only)."""
