@@ -193,9 +193,10 @@ def test_ragged_shapes(wtype):
     _run_decode(wl)
 
 
-def test_force_host_plan_and_dma_match_device_plan_bitwise():
-    wl = synth.workload("decode_bf16_k40_b1", wtype="fp8", batch=1, resident=6, **SMALL)
-    print("case host-plan/dma equivalence", flush=True)
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4", "int8", "mxfp4"])
+def test_force_host_plan_and_dma_match_device_plan_bitwise(wtype):
+    wl = synth.workload("decode_bf16_k40_b1", wtype=wtype, batch=1, resident=6, **SMALL)
+    print("case host-plan/dma equivalence %s" % wtype, flush=True)
     a, sa = _run_decode(wl, check_oracle=False)
     b, sb = _run_decode(wl, flags=pe.PE_FLAG_FORCE_HOST_PLAN, check_oracle=False)
     c, sc = _run_decode(wl, flags=pe.PE_FLAG_FORCE_HOST_PLAN | pe.PE_FLAG_PAGEIN_DMA, check_oracle=False)
