@@ -1658,9 +1658,11 @@ void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, i
 // ------------------------------------------------------------------ MFMA grouped GEMM
 //
 // Experts with at least kMfmaMinTokens entries in a step (prefill waves) run on
-// v_mfma_f32_16x16x32_bf16.  A block computes a tile of kTileM = 32 token rows
+// v_mfma_f32_16x16x32_bf16.  A block computes a tile of kTileM = 128 token rows
 // of one used expert against 64 weight rows, staging K in blocks of 128 through
-// LDS (rows padded by 8 bf16 against bank conflicts).  FP8 and int4 weights are
+// LDS (rows padded by 8 bf16 against bank conflicts); each wavefront takes 16 of
+// the weight rows against all 128 token rows, so a weight tile staged once
+// serves eight 16-row MFMA blocks.  FP8 and int4 weights are
 // decoded into LDS as exact bf16 (every e4m3 value and every nibble - 8 is a
 // bf16 number); their block / group scale multiplies the fp32 partial product
 // of each 128-wide K block.  MXFP4 codes are decoded with their 32-column E8M0
@@ -1674,9 +1676,27 @@ constexpr int kMfmaThreads = 256;
 constexpr int kNT = 64;          // weight rows per block (16 per wavefront)
 constexpr int kKB = 128;         // K per LDS stage = one FP8 block / int4 group
 constexpr int kLdsRow = kKB + 8; // padded LDS row, bf16 elements
+constexpr int kMH = kTileM / 16; // 16-row MFMA blocks per tile (every wavefront covers all of them)
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 }  // namespace
+
+// The (tile, column block) item of this workgroup.  Workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2) in linear block order; the
+// items are given out so that every XCD takes a contiguous run of them, tile by
+// tile, so the column blocks of one token tile (which share its rows of x or h)
+// and the tiles of one expert (which share its weights) meet in one L2.  Only
+// the order changes: every item is computed the same way wherever it runs.
+__device__ __forceinline__ void mfma_item(int& tile_idx, int& nblk) {
+  constexpr int kXcds = 8;
+  const int nb = gridDim.x, total = gridDim.x * gridDim.y;
+  const int b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int xcd = b % kXcds, k = b / kXcds;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int q = xcd * per + min(xcd, rem) + k;
+  tile_idx = q / nb;
+  nblk = q - tile_idx * nb;
+}
 
 // Decode one 16-byte chunk of weights of format FMT into bf16 in LDS at `dst`
 // (VPC values); returns nothing, writes VPC/8 16-byte LDS words.  `sc` (MXFP4
@@ -1744,27 +1764,50 @@ __device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst, floa
   }
 }
 
-// Stage kNT weight rows [row0, row0 + kNT) x K block kb of a row-major matrix with
-// C columns into LDS (bf16, padded rows); S is the matrix's row-scale region
-// (read for MXFP4 only).
+// One K block's staging per thread: kAPer 16-byte chunks of token rows and
+// kWPer<FMT> chunks of each weight matrix.  All of a thread's loads of a block
+// are issued before any of them is stored to LDS, so they are in flight
+// together.
+constexpr int kAPer = kTileM * (kKB / 8) / kMfmaThreads;
+template <int FMT> constexpr int kWPer = kNT * (kKB / Fmt<FMT>::VPC) / kMfmaThreads;
+
+// Loads of kNT weight rows [row0, row0 + kNT) x K block kb of a row-major matrix
+// with C columns (and, for MXFP4, each chunk's scale from the row-scale region S).
 template <int FMT>
-__device__ __forceinline__ void stage_weights(uint16_t* sB, const uint8_t* __restrict__ W,
-                                              const uint8_t* __restrict__ S, int C, int row0, int kb) {
+__device__ __forceinline__ void load_weights(uint4 (&v)[kWPer<FMT>], float (&sc)[kWPer<FMT>],
+                                             const uint8_t* __restrict__ W, const uint8_t* __restrict__ S,
+                                             int C, int row0, int kb) {
   constexpr int VPC = Fmt<FMT>::VPC;
   constexpr int CPR = kKB / VPC;                       // chunks per row per stage
-  const size_t row_bytes = (size_t)(C / VPC) * 16;   // 16 bytes per VPC columns
+  const size_t row_chunks = (size_t)(C / VPC);         // 16 bytes per VPC columns
   const uint4* base = reinterpret_cast<const uint4*>(W);
-  for (int i = threadIdx.x; i < kNT * CPR; i += kMfmaThreads) {
+#pragma unroll
+  for (int q = 0; q < kWPer<FMT>; ++q) {
+    const int i = threadIdx.x + q * kMfmaThreads;
     const int r = i / CPR, c = i - r * CPR;
-    const size_t chunk = ((size_t)(row0 + r) * row_bytes) / 16 + (size_t)kb * CPR + c;
-    float sc = 1.0f;
-    if constexpr (FMT == PE_W_MXFP4_B32) sc = chunk_scale<FMT>(nullptr, S + row_scale_off<FMT>(row0 + r, C), (kb * CPR + c) * VPC);
-    decode_chunk_to_lds<FMT>(base[chunk], sB + r * kLdsRow + c * VPC, sc);
+    v[q] = base[(size_t)(row0 + r) * row_chunks + (size_t)kb * CPR + c];
+    sc[q] = 1.0f;
+    if constexpr (FMT == PE_W_MXFP4_B32)
+      sc[q] = chunk_scale<FMT>(nullptr, S + row_scale_off<FMT>(row0 + r, C), (kb * CPR + c) * VPC);
   }
 }
 
-// Gate/up + SwiGLU on MFMA: tile (blockIdx.y within the wave's tiles) x 64
-// intermediate rows (blockIdx.x).
+// Decode the loaded chunks into LDS rows (bf16, padded).
+template <int FMT>
+__device__ __forceinline__ void store_weights(const uint4 (&v)[kWPer<FMT>], const float (&sc)[kWPer<FMT>],
+                                              uint16_t* sB) {
+  constexpr int VPC = Fmt<FMT>::VPC;
+  constexpr int CPR = kKB / VPC;
+#pragma unroll
+  for (int q = 0; q < kWPer<FMT>; ++q) {
+    const int i = threadIdx.x + q * kMfmaThreads;
+    const int r = i / CPR, c = i - r * CPR;
+    decode_chunk_to_lds<FMT>(v[q], sB + r * kLdsRow + c * VPC, sc[q]);
+  }
+}
+
+// Gate/up + SwiGLU on MFMA: one token tile of the wave x 64 intermediate rows
+// (the item mfma_item gives this workgroup).
 template <int FMT>
 __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a) {
   __shared__ __align__(16) uint16_t sA[kTileM * kLdsRow];
@@ -1774,13 +1817,15 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
   const int32_t* hdr = a.work + a.o.hdr;
   int t0, t1;
   part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
-  const int tile = t0 + blockIdx.y;
+  int tile_idx, nblk;
+  mfma_item(tile_idx, nblk);
+  const int tile = t0 + tile_idx;
   if (tile >= t1) return;
   const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
   const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
   const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
   const int H = a.H, I = a.I;
-  const int n0 = blockIdx.x * kNT;
+  const int n0 = nblk * kNT;
   const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
   const uint8_t* W13 = blob + a.off_w13;
   const float* S13f = reinterpret_cast<const float*>(blob + a.off_s13);
@@ -1789,27 +1834,37 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
   const int ln = lane & 15, lk = lane >> 4;
   if (threadIdx.x < kTileM)
     sTok[threadIdx.x] = threadIdx.x < rows ? a.work[a.o.entries + off + row0 + threadIdx.x] / a.k : -1;
-  f32x4_t accg[2], accu[2];
+  f32x4_t accg[kMH], accu[kMH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < kMH; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) { accg[h][i] = 0.f; accu[h][i] = 0.f; }
   const int ncol = n0 + 16 * wv + ln;     // this lane's output column (intermediate row)
   for (int kb = 0; kb < H / kKB; ++kb) {
     __syncthreads();
-    for (int i = threadIdx.x; i < kTileM * (kKB / 8); i += kMfmaThreads) {
+    uint4 va[kAPer], vg[kWPer<FMT>], vu[kWPer<FMT>];
+    float sg_[kWPer<FMT>], su_[kWPer<FMT>];
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
       const int r = i / (kKB / 8), c = i - r * (kKB / 8);
       const int tok = sTok[r];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tok >= 0) v = reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + kb * kKB)[c];
-      *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = v;
+      va[q] = tok >= 0 ? reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + kb * kKB)[c] : make_uint4(0, 0, 0, 0);
     }
-    stage_weights<FMT>(sG, W13, blob + a.off_s13, H, n0, kb);
-    stage_weights<FMT>(sU, W13, blob + a.off_s13, H, I + n0, kb);
-    __syncthreads();
-    f32x4_t pg[2], pu[2];
+    load_weights<FMT>(vg, sg_, W13, blob + a.off_s13, H, n0, kb);
+    load_weights<FMT>(vu, su_, W13, blob + a.off_s13, H, I + n0, kb);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int q = 0; q < kAPer; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB / 8), c = i - r * (kKB / 8);
+      *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = va[q];
+    }
+    store_weights<FMT>(vg, sg_, sG);
+    store_weights<FMT>(vu, su_, sU);
+    __syncthreads();
+    f32x4_t pg[kMH], pu[kMH];
+#pragma unroll
+    for (int h = 0; h < kMH; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) { pg[h][i] = 0.f; pu[h][i] = 0.f; }
 #pragma unroll
@@ -1818,7 +1873,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
       const bf16x8_t bg = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sG + (16 * wv + ln) * kLdsRow + kc));
       const bf16x8_t bu = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sU + (16 * wv + ln) * kLdsRow + kc));
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < kMH; ++h) {
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (16 * h + ln) * kLdsRow + kc));
         pg[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, pg[h], 0, 0, 0);
         pu[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, pu[h], 0, 0, 0);
@@ -1833,7 +1888,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
       su = half_bits_to_f32(S13h[(size_t)(I + ncol) * (H / 128) + kb]);
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < kMH; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32) {
@@ -1846,7 +1901,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
       }
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < kMH; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * h + 4 * lk + i;
@@ -1855,7 +1910,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     }
 }
 
-// Down projection x router weight on MFMA: tile x 64 output columns.
+// Down projection x router weight on MFMA: one token tile x 64 output columns
+// (the item mfma_item gives this workgroup).
 template <int FMT>
 __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
   __shared__ __align__(16) uint16_t sA[kTileM * kLdsRow];
@@ -1863,38 +1919,50 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
   const int32_t* hdr = a.work + a.o.hdr;
   int t0, t1;
   part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
-  const int tile = t0 + blockIdx.y;
+  int tile_idx, nblk;
+  mfma_item(tile_idx, nblk);
+  const int tile = t0 + tile_idx;
   if (tile >= t1) return;
   const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
   const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
   const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
   const int H = a.H, I = a.I;
-  const int n0 = blockIdx.x * kNT;
+  const int n0 = nblk * kNT;
   const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
   const uint8_t* W2 = blob + a.off_w2;
   const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
   const uint16_t* S2h = reinterpret_cast<const uint16_t*>(blob + a.off_s2);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ln = lane & 15, lk = lane >> 4;
-  f32x4_t acc[2];
+  f32x4_t acc[kMH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < kMH; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
   const int ncol = n0 + 16 * wv + ln;
   for (int kb = 0; kb < I / kKB; ++kb) {
     __syncthreads();
-    for (int i = threadIdx.x; i < kTileM * (kKB / 8); i += kMfmaThreads) {
-      const int r = i / (kKB / 8), c = i - r * (kKB / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < rows) v = reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB)[c];
-      *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = v;
-    }
-    stage_weights<FMT>(sB, W2, blob + a.off_s2, I, n0, kb);
-    __syncthreads();
-    f32x4_t p[2];
+    uint4 va[kAPer], vb[kWPer<FMT>];
+    float sb_[kWPer<FMT>];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int q = 0; q < kAPer; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB / 8), c = i - r * (kKB / 8);
+      va[q] = r < rows ? reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB)[c]
+                       : make_uint4(0, 0, 0, 0);
+    }
+    load_weights<FMT>(vb, sb_, W2, blob + a.off_s2, I, n0, kb);
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB / 8), c = i - r * (kKB / 8);
+      *reinterpret_cast<uint4*>(sA + r * kLdsRow + c * 8) = va[q];
+    }
+    store_weights<FMT>(vb, sb_, sB);
+    __syncthreads();
+    f32x4_t p[kMH];
+#pragma unroll
+    for (int h = 0; h < kMH; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[h][i] = 0.f;
 #pragma unroll
@@ -1902,7 +1970,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
       const int kc = ks * 32 + 8 * lk;
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sB + (16 * wv + ln) * kLdsRow + kc));
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < kMH; ++h) {
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (16 * h + ln) * kLdsRow + kc));
         p[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, p[h], 0, 0, 0);
       }
@@ -1911,7 +1979,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
     if constexpr (FMT == PE_W_FP8_B128) sc = S2f[(size_t)(n0 >> 7) * (I / 128) + kb];
     else if constexpr (kGroupScales<FMT>) sc = half_bits_to_f32(S2h[(size_t)ncol * (I / 128) + kb]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < kMH; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32) acc[h][i] += p[h][i];
@@ -1920,7 +1988,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
   }
   const int32_t* ent = a.work + a.o.entries + off + row0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < kMH; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * h + 4 * lk + i;

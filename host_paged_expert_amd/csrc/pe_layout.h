@@ -15,7 +15,7 @@ constexpr int kMaxExperts = 1024;
 // unpaged step run every expert through the same arithmetic.
 constexpr int kMfmaMinTokens = 16;
 constexpr int kNoMfma = 1 << 30;   // threshold that sends every expert to the GEMV kernels
-constexpr int kTileM = 32;   // token rows per MFMA tile
+constexpr int kTileM = 128;  // token rows per MFMA tile
 
 // Device statistic counters (uint64 each).
 enum StatIdx {
