@@ -860,25 +860,39 @@ __device__ __forceinline__ void group_reduce(float (&acc)[MB], int LG) {
   }
 }
 
+// Copy n 16-byte words into LDS, word i from src_of(i) to dst[i], every thread
+// of the block taking words threadIdx.x, + blockDim.x, ...  Each thread issues
+// four loads before it stores them, so a copy of more words than threads costs
+// one load latency per four words instead of one per word.
+template <class SrcOf>
+__device__ __forceinline__ void copy_words_to_lds(uint4* dst, int n, SrcOf src_of) {
+  const int st = blockDim.x;
+  int i = threadIdx.x;
+  for (; i + 3 * st < n; i += 4 * st) {
+    const uint4 v0 = *src_of(i), v1 = *src_of(i + st), v2 = *src_of(i + 2 * st), v3 = *src_of(i + 3 * st);
+    dst[i] = v0;
+    dst[i + st] = v1;
+    dst[i + 2 * st] = v2;
+    dst[i + 3 * st] = v3;
+  }
+  for (; i < n; i += st) dst[i] = *src_of(i);
+}
+
 // Stage rows `entries[pos0 + t] / k` (t < mb) of a bf16 [*, C] matrix into LDS.
 __device__ __forceinline__ void stage_rows(uint16_t* xs, const uint16_t* __restrict__ src, int C,
                                            const int32_t* __restrict__ row_idx, int mb, int divisor) {
   const int n16 = C / 8;
-  for (int i = threadIdx.x; i < mb * n16; i += blockDim.x) {
-    int t = i / n16, c = i - t * n16;
-    int r = row_idx[t] / divisor;
-    reinterpret_cast<uint4*>(xs + t * C)[c] = reinterpret_cast<const uint4*>(src + (size_t)r * C)[c];
-  }
+  copy_words_to_lds(reinterpret_cast<uint4*>(xs), mb * n16, [=](int i) {
+    const int t = i / n16, c = i - t * n16;
+    return reinterpret_cast<const uint4*>(src + (size_t)(row_idx[t] / divisor) * C) + c;
+  });
 }
 
 // Stage consecutive rows [pos0, pos0 + mb) of a bf16 [*, C] matrix into LDS.
 __device__ __forceinline__ void stage_consecutive(uint16_t* xs, const uint16_t* __restrict__ src, int C,
                                                   int pos0, int mb) {
-  const int n16 = C / 8;
-  for (int i = threadIdx.x; i < mb * n16; i += blockDim.x) {
-    int t = i / n16, c = i - t * n16;
-    reinterpret_cast<uint4*>(xs + t * C)[c] = reinterpret_cast<const uint4*>(src + (size_t)(pos0 + t) * C)[c];
-  }
+  const uint4* base = reinterpret_cast<const uint4*>(src + (size_t)pos0 * C);
+  copy_words_to_lds(reinterpret_cast<uint4*>(xs), mb * (C / 8), [=](int i) { return base + i; });
 }
 
 struct GemvItem {
@@ -1452,9 +1466,8 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uin
   if (i1 < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d1.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
   for (int i = threadIdx.x; i < n; i += blockDim.x) s_id[i] = a.ids[i];
   if constexpr (STAGE) {
-    const int n16 = n * I / 8;
-    for (int i = threadIdx.x; i < n16; i += blockDim.x)
-      reinterpret_cast<uint4*>(s_h)[i] = reinterpret_cast<const uint4*>(a.h)[i];
+    const uint4* hw = reinterpret_cast<const uint4*>(a.h);
+    copy_words_to_lds(reinterpret_cast<uint4*>(s_h), n * I / 8, [=](int i) { return hw + i; });
   }
   __syncthreads();
   const uint16_t* hbase = STAGE ? s_h : a.h;
