@@ -1680,7 +1680,8 @@ void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, i
 // bf16 number); their block / group scale multiplies the fp32 partial product
 // of each 128-wide K block.  MXFP4 codes are decoded with their 32-column E8M0
 // scale applied (an E2M1 value times a power of two: exact in bf16 within
-// bf16's range), so its K blocks take no scale.  Every output element's
+// bf16's range), so its K blocks take no scale, and bf16 and MXFP4 MFMAs
+// accumulate straight into the output accumulators.  Every output element's
 // arithmetic depends only on its own token row and weight row, never on the
 // other rows of the tile.
 
@@ -1782,6 +1783,8 @@ __device__ __forceinline__ void decode_chunk_to_lds(uint4 w, uint16_t* dst, floa
 // are issued before any of them is stored to LDS, so they are in flight
 // together.
 constexpr int kAPer = kTileM * (kKB / 8) / kMfmaThreads;
+// FP8, int4 and int8 multiply each 128-wide K block's partial product by its scale.
+template <int FMT> constexpr bool kBlockScaled = FMT == PE_W_FP8_B128 || kGroupScales<FMT>;
 template <int FMT> constexpr int kWPer = kNT * (kKB / Fmt<FMT>::VPC) / kMfmaThreads;
 
 // Loads of kNT weight rows [row0, row0 + kNT) x K block kb of a row-major matrix
@@ -1853,10 +1856,15 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
 #pragma unroll
     for (int i = 0; i < 4; ++i) { accg[h][i] = 0.f; accu[h][i] = 0.f; }
   const int ncol = n0 + 16 * wv + ln;     // this lane's output column (intermediate row)
-  for (int kb = 0; kb < H / kKB; ++kb) {
-    __syncthreads();
-    uint4 va[kAPer], vg[kWPer<FMT>], vu[kWPer<FMT>];
-    float sg_[kWPer<FMT>], su_[kWPer<FMT>];
+  // Formats without a per-block scale accumulate straight into accg / accu, and
+  // with the registers that saves they load K block kb + 1 while block kb's
+  // MFMAs run; the scaled formats keep a per-block partial and load each block
+  // at its start.
+  constexpr bool kPipe = !kBlockScaled<FMT>;
+  uint4 va[kAPer], vg[kWPer<FMT>], vu[kWPer<FMT>];
+  float sg_[kWPer<FMT>], su_[kWPer<FMT>];
+  __syncthreads();     // sTok
+  auto load_block = [&](int kb) {
 #pragma unroll
     for (int q = 0; q < kAPer; ++q) {
       const int i = threadIdx.x + q * kMfmaThreads;
@@ -1866,6 +1874,12 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     }
     load_weights<FMT>(vg, sg_, W13, blob + a.off_s13, H, n0, kb);
     load_weights<FMT>(vu, su_, W13, blob + a.off_s13, H, I + n0, kb);
+  };
+  const int nK = H / kKB;
+  if constexpr (kPipe) load_block(0);
+  for (int kb = 0; kb < nK; ++kb) {
+    __syncthreads();
+    if constexpr (!kPipe) load_block(kb);
 #pragma unroll
     for (int q = 0; q < kAPer; ++q) {
       const int i = threadIdx.x + q * kMfmaThreads;
@@ -1875,6 +1889,22 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     store_weights<FMT>(vg, sg_, sG);
     store_weights<FMT>(vu, su_, sU);
     __syncthreads();
+    if constexpr (kPipe) {
+      if (kb + 1 < nK) load_block(kb + 1);
+#pragma unroll
+      for (int ks = 0; ks < kKB / 32; ++ks) {
+        const int kc = ks * 32 + 8 * lk;
+        const bf16x8_t bg = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sG + (16 * wv + ln) * kLdsRow + kc));
+        const bf16x8_t bu = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sU + (16 * wv + ln) * kLdsRow + kc));
+#pragma unroll
+        for (int h = 0; h < kMH; ++h) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (16 * h + ln) * kLdsRow + kc));
+          accg[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[h], 0, 0, 0);
+          accu[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[h], 0, 0, 0);
+        }
+      }
+      continue;
+    }
     f32x4_t pg[kMH], pu[kMH];
 #pragma unroll
     for (int h = 0; h < kMH; ++h)
@@ -1904,13 +1934,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     for (int h = 0; h < kMH; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32) {
-          accg[h][i] += pg[h][i];
-          accu[h][i] += pu[h][i];
-        } else {
-          accg[h][i] = __builtin_fmaf(sg, pg[h][i], accg[h][i]);
-          accu[h][i] = __builtin_fmaf(su, pu[h][i], accu[h][i]);
-        }
+        accg[h][i] = __builtin_fmaf(sg, pg[h][i], accg[h][i]);
+        accu[h][i] = __builtin_fmaf(su, pu[h][i], accu[h][i]);
       }
   }
 #pragma unroll
@@ -1953,10 +1978,11 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
   const int ncol = n0 + 16 * wv + ln;
-  for (int kb = 0; kb < I / kKB; ++kb) {
-    __syncthreads();
-    uint4 va[kAPer], vb[kWPer<FMT>];
-    float sb_[kWPer<FMT>];
+  // K block kb + 1 is loaded while block kb's MFMAs run; formats without a
+  // per-block scale accumulate straight into acc.
+  uint4 va[kAPer], vb[kWPer<FMT>];
+  float sb_[kWPer<FMT>];
+  auto load_block = [&](int kb) {
 #pragma unroll
     for (int q = 0; q < kAPer; ++q) {
       const int i = threadIdx.x + q * kMfmaThreads;
@@ -1965,6 +1991,11 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
                        : make_uint4(0, 0, 0, 0);
     }
     load_weights<FMT>(vb, sb_, W2, blob + a.off_s2, I, n0, kb);
+  };
+  const int nK = I / kKB;
+  load_block(0);
+  for (int kb = 0; kb < nK; ++kb) {
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < kAPer; ++q) {
       const int i = threadIdx.x + q * kMfmaThreads;
@@ -1973,6 +2004,20 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
     }
     store_weights<FMT>(vb, sb_, sB);
     __syncthreads();
+    if (kb + 1 < nK) load_block(kb + 1);
+    if constexpr (!kBlockScaled<FMT>) {
+#pragma unroll
+      for (int ks = 0; ks < kKB / 32; ++ks) {
+        const int kc = ks * 32 + 8 * lk;
+        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sB + (16 * wv + ln) * kLdsRow + kc));
+#pragma unroll
+        for (int h = 0; h < kMH; ++h) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (16 * h + ln) * kLdsRow + kc));
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[h], 0, 0, 0);
+        }
+      }
+      continue;
+    }
     f32x4_t p[kMH];
 #pragma unroll
     for (int h = 0; h < kMH; ++h)
@@ -1994,10 +2039,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
 #pragma unroll
     for (int h = 0; h < kMH; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32) acc[h][i] += p[h][i];
-        else acc[h][i] = __builtin_fmaf(sc, p[h][i], acc[h][i]);
-      }
+      for (int i = 0; i < 4; ++i) acc[h][i] = __builtin_fmaf(sc, p[h][i], acc[h][i]);
   }
   const int32_t* ent = a.work + a.o.entries + off + row0;
 #pragma unroll
