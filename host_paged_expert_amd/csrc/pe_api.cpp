@@ -112,15 +112,15 @@ struct pe_ctx {
   uint8_t* host_store = nullptr;       // page-locked, mapped: [L][E][stride]
   uint8_t* host_store_dev = nullptr;   // its device-visible address
   uint8_t* slots = nullptr;            // device: [L][K][stride]
-  int32_t* blocks = nullptr;           // device: [L][ll.total]
-  int32_t* work = nullptr;             // device: [wl.total]
+  size_t layer_words = 0;              // ll.total + wl.total, rounded: a layer's block, then its work lists
+  int32_t* blocks = nullptr;           // device: [L][layer_words]
   uint16_t* h = nullptr;               // device: [max_entries][I] bf16
   float* merged = nullptr;             // device: [max_entries][H] fp32
   unsigned long long* stats = nullptr; // device: [ST_COUNT]
   int32_t* st_ids = nullptr;           // pinned staging: [max_entries]
-  int32_t* st_blk = nullptr;           // pinned: per layer [L][ll.total], the host mirror of its block
+  int32_t* st_blk = nullptr;           // pinned: [L][layer_words], the host mirror of each layer's block and
+                                       // work lists (a host-planned step uploads both in one copy)
   std::vector<char> mirror_ok;         // per layer: st_blk holds the device block's LRU state
-  int32_t* st_work = nullptr;          // pinned staging: [wl.total]
   pe::HostPlanSummary* sum = nullptr;
   unsigned long long host_counts[pe::ST_COUNT] = {};
   // Second stream (default priority): runs the experts that were already
@@ -145,8 +145,7 @@ void free_ctx(pe_ctx* c) {
   if (c->host_store) (void)hipHostFree(c->host_store);
   if (c->st_ids) (void)hipHostFree(c->st_ids);
   if (c->st_blk) (void)hipHostFree(c->st_blk);
-  if (c->st_work) (void)hipHostFree(c->st_work);
-  for (void* p : {(void*)c->slots, (void*)c->blocks, (void*)c->work, (void*)c->h, (void*)c->merged,
+  for (void* p : {(void*)c->slots, (void*)c->blocks, (void*)c->h, (void*)c->merged,
                   (void*)c->stats})
     if (p) (void)hipFree(p);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
@@ -169,7 +168,7 @@ pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const 
   a.slots = c->slots + (size_t)layer * c->d.K * c->b.stride;
   a.slot_stride = c->b.stride;
   a.off_w13 = c->b.off_w13; a.off_w2 = c->b.off_w2; a.off_s13 = c->b.off_s13; a.off_s2 = c->b.off_s2;
-  a.work = c->work;
+  a.work = c->blocks + (size_t)layer * c->layer_words + c->ll.total;
   a.o = c->o;
   a.MW = c->d.max_waves;
   a.wave = wave;
@@ -351,6 +350,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   c->d = pe::make_dims(g.num_layers, g.num_experts, K, g.top_k, g.hidden, g.inter, g.max_tokens);
   c->ll = pe::make_layer_layout(c->d);
   c->wl = pe::make_work_layout(c->d);
+  c->layer_words = c->ll.total + c->wl.total;     // both multiples of 64 words
   c->o = pe::make_offsets(c->ll, c->wl);
   blob_layout(g.wtype, g.hidden, g.inter, &c->b);
   // The MFMA kernels stage K in blocks of 128 and tile weight rows by 64.
@@ -379,8 +379,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   }
   struct { void** p; size_t bytes; } dev[] = {
       {reinterpret_cast<void**>(&c->slots), (size_t)d.L * d.K * c->b.stride},
-      {reinterpret_cast<void**>(&c->blocks), (size_t)d.L * c->ll.total * 4},
-      {reinterpret_cast<void**>(&c->work), c->wl.total * 4},
+      {reinterpret_cast<void**>(&c->blocks), (size_t)d.L * c->layer_words * 4},
       {reinterpret_cast<void**>(&c->h), (size_t)d.max_entries * d.I * 2},
       {reinterpret_cast<void**>(&c->merged), (size_t)d.max_entries * d.H * 4},
       {reinterpret_cast<void**>(&c->stats), pe::ST_COUNT * 8},
@@ -394,7 +393,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     }
   }
   struct { int32_t** p; size_t words; } pin[] = {
-      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, (size_t)d.L * c->ll.total}, {&c->st_work, c->wl.total}};
+      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, (size_t)d.L * c->layer_words}};
   for (auto& a : pin) {
     if (hipHostMalloc(reinterpret_cast<void**>(a.p), a.words * 4, hipHostMallocDefault) != hipSuccess) {
       *a.p = nullptr;
@@ -404,8 +403,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     }
   }
   if (hipMemset(c->stats, 0, pe::ST_COUNT * 8) != hipSuccess ||
-      hipMemset(c->blocks, 0, (size_t)d.L * c->ll.total * 4) != hipSuccess ||
-      hipMemset(c->work, 0, c->wl.total * 4) != hipSuccess) {
+      hipMemset(c->blocks, 0, (size_t)d.L * c->layer_words * 4) != hipSuccess) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "initialising device buffers failed");
   }
@@ -416,7 +414,7 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     return fail(PE_ERR_HIP, "creating the side stream and its events failed");
   }
   c->mirror_ok.assign(d.L, 0);
-  pe::launch_reset_lru(c->blocks, c->ll.total, 0, d.L, c->o, d.E, d.K, unpaged, nullptr);
+  pe::launch_reset_lru(c->blocks, c->layer_words, 0, d.L, c->o, d.E, d.K, unpaged, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "resetting the LRU state failed: %s", hipGetErrorString(hipGetLastError()));
@@ -470,7 +468,7 @@ int pe_reset_lru(pe_ctx* c, int layer, void* stream) {
   if (rc) return rc;
   const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->d.L : layer + 1;
   for (int l = l0; l < l1; ++l) c->mirror_ok[l] = 0;
-  pe::launch_reset_lru(c->blocks, c->ll.total, l0, l1, c->o, c->d.E, c->d.K, c->unpaged,
+  pe::launch_reset_lru(c->blocks, c->layer_words, l0, l1, c->o, c->d.E, c->d.K, c->unpaged,
                        static_cast<hipStream_t>(stream));
   PE_HIP(hipGetLastError());
   return PE_OK;
@@ -488,7 +486,8 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   const pe::Dims& d = c->d;
   const int n = T * d.k;
-  int32_t* blk = c->blocks + (size_t)layer * c->ll.total;
+  int32_t* blk = c->blocks + (size_t)layer * c->layer_words;
+  int32_t* work_l = blk + c->ll.total;
   uint8_t* slots_l = c->slots + (size_t)layer * d.K * c->b.stride;
   const uint8_t* host_l = c->unpaged ? nullptr : c->host_store_dev + (size_t)layer * d.E * c->b.stride;
   const bool device_plan = n <= d.K && !(c->cfg.flags & PE_FLAG_FORCE_HOST_PLAN);
@@ -522,7 +521,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       a.mfma_min = mfma_min;
       {
         StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-        pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, mfma_min, c->work, c->stats, host_l,
+        pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, mfma_min, work_l, c->stats, host_l,
                           slots_l, c->b.stride, c->b.copied, c->stream_wgs, a, items, T, s);
       }
       pe::ExpertArgs all = expert_args(c, layer, 0, x, topk_w, 0);
@@ -542,7 +541,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
     const int tiles = mfma_min != pe::kNoMfma ? pe::ceil_div(n, pe::kTileM) + items : 0;
     {
       StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-      pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, mfma_min, c->work, c->stats, host_l, slots_l,
+      pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, mfma_min, work_l, c->stats, host_l, slots_l,
                               c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
     }
     run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
@@ -565,7 +564,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   // it); that is the one synchronisation.  Plan every wave on the host, upload
   // the block (state, plans, slot map) and the work lists, then run the waves in
   // order.
-  int32_t* mirror = c->st_blk + (size_t)layer * c->ll.total;
+  int32_t* mirror = c->st_blk + (size_t)layer * c->layer_words;
   PE_HIP(hipMemcpyAsync(c->st_ids, topk_ids, (size_t)n * 4, hipMemcpyDeviceToHost, s));
   if (!c->mirror_ok[layer])
     PE_HIP(hipMemcpyAsync(mirror, blk, c->ll.state_prefix * 4, hipMemcpyDeviceToHost, s));
@@ -574,10 +573,10 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   pe::HostPlanSummary& sm = *c->sum;
   pe::Dims dp = d;
   dp.mfma_min = mfma_min;
-  if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, mirror, c->st_work, &sm) != 0)
+  if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, mirror, mirror + c->ll.total, &sm) != 0)
     return fail(PE_ERR_INVALID_ARG, "step needs more waves than the context holds");
-  PE_HIP(hipMemcpyAsync(blk, mirror, (c->ll.slot_of + n) * 4, hipMemcpyHostToDevice, s));
-  PE_HIP(hipMemcpyAsync(c->work, c->st_work, (c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));
+  // the block (state, plans, slot map) and the work lists that follow it, in one copy
+  PE_HIP(hipMemcpyAsync(blk, mirror, (c->ll.total + c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));
   c->mirror_ok[layer] = 1;
   const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
   for (int w = 0; w < sm.n_waves; ++w) {
@@ -659,7 +658,7 @@ int pe_get_lru_state(pe_ctx* c, int layer, int32_t* slot_expert, uint32_t* last_
   if (rc) return rc;
   PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   std::vector<int32_t> blk(c->ll.state_prefix);
-  PE_HIP(hipMemcpy(blk.data(), c->blocks + (size_t)layer * c->ll.total, blk.size() * 4, hipMemcpyDeviceToHost));
+  PE_HIP(hipMemcpy(blk.data(), c->blocks + (size_t)layer * c->layer_words, blk.size() * 4, hipMemcpyDeviceToHost));
   const int32_t* st = blk.data() + c->ll.state(blk[c->ll.cur] & 1);
   if (slot_expert) memcpy(slot_expert, st + c->ll.slot_expert, (size_t)c->d.K * 4);
   if (last_use) memcpy(last_use, st + c->ll.last_use, (size_t)c->d.K * 4);
@@ -676,7 +675,7 @@ int pe_get_plan(pe_ctx* c, int layer, int wave, int32_t* count, int32_t* experts
   if (rc) return rc;
   PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   std::vector<int32_t> blk(c->ll.slot_of);
-  PE_HIP(hipMemcpy(blk.data(), c->blocks + (size_t)layer * c->ll.total, blk.size() * 4, hipMemcpyDeviceToHost));
+  PE_HIP(hipMemcpy(blk.data(), c->blocks + (size_t)layer * c->layer_words, blk.size() * 4, hipMemcpyDeviceToHost));
   const int K = c->d.K;
   if (count) *count = blk[c->ll.plan_count + wave];
   if (experts) memcpy(experts, blk.data() + c->ll.plan_expert + (size_t)wave * K, (size_t)K * 4);
@@ -693,7 +692,7 @@ int pe_get_slot_map(pe_ctx* c, int layer, int32_t* slot_of, int T, void* stream)
   int rc = use_device(c);
   if (rc) return rc;
   PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  PE_HIP(hipMemcpy(slot_of, c->blocks + (size_t)layer * c->ll.total + c->ll.slot_of, (size_t)T * c->d.k * 4,
+  PE_HIP(hipMemcpy(slot_of, c->blocks + (size_t)layer * c->layer_words + c->ll.slot_of, (size_t)T * c->d.k * 4,
                    hipMemcpyDeviceToHost));
   return PE_OK;
 }
