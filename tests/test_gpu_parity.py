@@ -242,6 +242,42 @@ def test_invalid_ids_are_counted_and_contribute_nothing():
     m.close()
 
 
+@pytest.mark.parametrize("wtype", ["bf16", "int4"])
+def test_repeated_ids_within_a_token(wtype):
+    """A token may name one expert at several of its k positions: each position
+    is its own entry (own router weight), summed in position order.  One
+    device-planned step (6 entries <= K = 6) and one host-planned step (9
+    entries > K, one of them invalid), against the oracle and an unpaged run."""
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=12, top_k=3, resident=6, hidden=256, inter=256,
+                        wtype=wtype, batch=3, steps=1)
+    print("case repeated ids %s" % wtype, flush=True)
+    x = torch.from_numpy(synth.hidden_states(wl, 0, 3).view(np.int16)).view(torch.bfloat16).to(DEV)
+    cases = [(np.array([[4, 4, 7], [7, 1, 7]], np.int32), 2),
+             (np.array([[2, 2, 2], [0, 5, 0], [9, 11, -1]], np.int32), 3)]
+    rng = np.random.default_rng(3)
+    outs = {}
+    for flags in (0, pe.PE_FLAG_UNPAGED):
+        m = harness.make_moe(wl, flags=flags)
+        harness.load_store(m, wl)
+        for ci, (ids_np, T) in enumerate(cases):
+            w_np = rng.random(ids_np.shape).astype(np.float32) if flags == 0 else outs[("w", ci)]
+            outs[("w", ci)] = w_np
+            out = torch.empty((T, wl.hidden), dtype=torch.bfloat16, device=DEV)
+            m.forward(0, x[:T], torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), out, T=T)
+            torch.cuda.synchronize()
+            outs[(flags, ci)] = harness.bf16_bits(out)
+            if flags == 0:
+                ref = moe.moe_layer(formats.bf16_to_f32(harness.bf16_bits(x[:T])), ids_np, w_np, _expert_fn(wl, 0),
+                                    num_experts=wl.experts)
+                _check_close(outs[(flags, ci)], ref, wtype, "case %d" % ci)
+        st = m.stats()
+        if flags == 0:
+            assert st["device_planned"] == 1 and st["host_planned"] == 1 and st["bad_ids"] == 1
+        m.close()
+    for ci in range(len(cases)):
+        assert np.array_equal(outs[(0, ci)], outs[(pe.PE_FLAG_UNPAGED, ci)]), ci
+
+
 def test_zero_tokens_is_a_noop():
     wl = synth.workload("tiny_bf16")
     m = harness.make_moe(wl)
