@@ -15,7 +15,7 @@ import host_paged_expert_amd as pe
 
 
 def host_threads() -> int:
-    """Worker threads for loading: the machine's CPU share (at most 16)."""
+    """Worker threads for loading: the CPUs this process may use, at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
