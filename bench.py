@@ -258,7 +258,7 @@ def main():
         elif args.dma:
             pi_name, dn_name = "hipMemcpyAsync page-in", "gemv_down_kernel"
         else:
-            pi_name, dn_name = "wave_a_kernel", "gemv_down_kernel"
+            pi_name, dn_name = "wave_a_kernel", HOST_DOWN
         kernel = {
             "page_in": {"name": pi_name, "launches": n_pi, "avg_us": 1e3 * ms_pi / max(n_pi, 1),
                         "bytes_per_launch": M * S_alg / max(n_pi, 1),
@@ -502,6 +502,9 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
 
 
 PMC_KERNELS = ("step_a_kernel", "down_sum_kernel", "wave_a_kernel", "gemv_down_kernel", "page_in_kernel")
+# The down launches of a host-planned step: the fused down projection + top-k
+# sum when the step is one wave, the plain down kernel per wave otherwise.
+HOST_DOWN = "down_sum_kernel+gemv_down_kernel"
 
 
 def source_hash():
@@ -555,8 +558,12 @@ def pmc_summary(fetch_csv, write_csv, bench_json, out_json):
     out = {"source_sha256_16": source_hash(), "workload": cfg["workload"], "fetch_scale": round(fs, 4),
            "write_scale": round(ws, 4), "window": {"distinct": win["distinct"], "page_ins": win["page_ins"]},
            "kernels": {}}
-    for name in PMC_KERNELS:
-        keys = [k for k in f if name in k]
+    if cfg.get("path") == "host-planned" and cfg.get("pagein") == "kernel":
+        groups = [("wave_a_kernel", ("wave_a_kernel",)), (HOST_DOWN, ("down_sum_kernel", "gemv_down_kernel"))]
+    else:
+        groups = [(name, (name,)) for name in PMC_KERNELS]
+    for name, members in groups:
+        keys = [k for k in f if any(m in k for m in members)]
         if not keys:
             continue
         fv = [v for k in keys for v in f[k]]

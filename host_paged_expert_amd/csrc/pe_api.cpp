@@ -579,6 +579,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   PE_HIP(hipMemcpyAsync(blk, mirror, (c->ll.total + c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));
   c->mirror_ok[layer] = 1;
   const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
+  bool summed = false;     // the top-k sum already ran with the last down projection
   for (int w = 0; w < sm.n_waves; ++w) {
     const int cnt = mirror[c->ll.plan_count + w];
     const int g_all = sm.gemv_items[w], g_hit = sm.gemv_hits[w];
@@ -595,7 +596,18 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       }
       a.part = 0;
       StageTimer tm(c, PE_STAGE_DOWN, s);
-      pe::launch_gemv_down(c->cfg.wtype, a, g_all, sm.max_gemv_tokens, s);
+      if (sm.n_waves == 1 && mfma_min == pe::kNoMfma) {
+        // one wave of few tokens: its down projection and the top-k sum in one
+        // launch, as in a device-planned step (the same arithmetic as the
+        // down kernel followed by the sum over the merged buffer)
+        a.ids = topk_ids;
+        a.T = T;
+        a.E = d.E;
+        pe::launch_down_sum(c->cfg.wtype, a, sm.max_gemv_tokens, static_cast<uint16_t*>(out), nullptr, s);
+        summed = true;
+      } else {
+        pe::launch_gemv_down(c->cfg.wtype, a, g_all, sm.max_gemv_tokens, s);
+      }
       continue;
     }
     const bool fork = !c->unpaged && cnt > 0 && (g_hit > 0 || t_hit > 0);
@@ -625,7 +637,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       run_experts(c, layer, w, 0, x, topk_w, g_all, sm.max_gemv_tokens, t_all, s);
     }
   }
-  {
+  if (!summed) {
     StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
     pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), nullptr, s);
   }

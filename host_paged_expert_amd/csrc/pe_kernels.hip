@@ -694,6 +694,48 @@ __device__ __forceinline__ float chunk_scale(const float* __restrict__ s_fp8_row
   else return 1.0f;
 }
 
+// The GEMV blocks stage the scales of their rows in LDS with the token vectors,
+// so that a chunk's scale is an LDS read rather than a global load issued
+// behind the previous chunk's arithmetic.  A row range's scales are one
+// contiguous byte range of the scale region (FP8: the scale rows of the 128-row
+// blocks it touches), staged in 16-byte words from `begin`, a multiple of 16.
+// The rounding never leaves the blob: each scale region ends within 15 bytes of
+// a 256-byte boundary that is the next region's start or the end of the copied
+// blob.
+struct ScaleSpan {
+  size_t begin;
+  int words;
+};
+
+// Scale bytes before row `row` of a C-column matrix (FP8: before its 128-row block).
+template <int FMT>
+__host__ __device__ __forceinline__ size_t scale_row_off(int row, int C) {
+  if constexpr (FMT == PE_W_FP8_B128) return (size_t)(row >> 7) * (C / 128) * 4;
+  else return row_scale_off<FMT>(row, C);
+}
+
+// Words of the staged scales of rows [r0, r1) (r0 < r1).
+template <int FMT>
+__device__ __forceinline__ ScaleSpan scale_span(int r0, int r1, int C) {
+  size_t e;
+  if constexpr (FMT == PE_W_FP8_B128) e = scale_row_off<FMT>(r1 - 1, C) + (C / 128) * 4;
+  else e = scale_row_off<FMT>(r1, C);
+  const size_t b = scale_row_off<FMT>(r0, C) & ~(size_t)15;
+  return {b, (int)(((e + 15) & ~(size_t)15) - b) / 16};
+}
+
+// Most words scale_span can give for `rows` consecutive rows (0 for bf16).
+template <int FMT>
+__host__ __device__ __forceinline__ int scale_stage_words(int rows, int C) {
+  if constexpr (FMT == PE_W_BF16) {
+    return 0;
+  } else {
+    const size_t bytes = FMT == PE_W_FP8_B128 ? (size_t)((rows + 126) / 128 + 1) * (C / 128) * 4
+                                              : row_scale_off<FMT>(rows, C);
+    return (int)((bytes + 15) / 16 + 2);
+  }
+}
+
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 // a.lo * b.lo + a.hi * b.hi + c, a and b packed bf16 pairs (v_dot2c_f32_bf16).
@@ -864,18 +906,23 @@ __device__ __forceinline__ void group_reduce(float (&acc)[MB], int LG) {
 // of the block taking words threadIdx.x, + blockDim.x, ...  Each thread issues
 // four loads before it stores them, so a copy of more words than threads costs
 // one load latency per four words instead of one per word.
-template <class SrcOf>
-__device__ __forceinline__ void copy_words_to_lds(uint4* dst, int n, SrcOf src_of) {
+template <class SrcOf, class DstOf>
+__device__ __forceinline__ void copy_words_to_lds(int n, SrcOf src_of, DstOf dst_of) {
   const int st = blockDim.x;
   int i = threadIdx.x;
   for (; i + 3 * st < n; i += 4 * st) {
     const uint4 v0 = *src_of(i), v1 = *src_of(i + st), v2 = *src_of(i + 2 * st), v3 = *src_of(i + 3 * st);
-    dst[i] = v0;
-    dst[i + st] = v1;
-    dst[i + 2 * st] = v2;
-    dst[i + 3 * st] = v3;
+    *dst_of(i) = v0;
+    *dst_of(i + st) = v1;
+    *dst_of(i + 2 * st) = v2;
+    *dst_of(i + 3 * st) = v3;
   }
-  for (; i < n; i += st) dst[i] = *src_of(i);
+  for (; i < n; i += st) *dst_of(i) = *src_of(i);
+}
+
+template <class SrcOf>
+__device__ __forceinline__ void copy_words_to_lds(uint4* dst, int n, SrcOf src_of) {
+  copy_words_to_lds(n, src_of, [=](int i) { return dst + i; });
 }
 
 // Stage rows `entries[pos0 + t] / k` (t < mb) of a bf16 [*, C] matrix into LDS.
@@ -886,13 +933,6 @@ __device__ __forceinline__ void stage_rows(uint16_t* xs, const uint16_t* __restr
     const int t = i / n16, c = i - t * n16;
     return reinterpret_cast<const uint4*>(src + (size_t)(row_idx[t] / divisor) * C) + c;
   });
-}
-
-// Stage consecutive rows [pos0, pos0 + mb) of a bf16 [*, C] matrix into LDS.
-__device__ __forceinline__ void stage_consecutive(uint16_t* xs, const uint16_t* __restrict__ src, int C,
-                                                  int pos0, int mb) {
-  const uint4* base = reinterpret_cast<const uint4*>(src + (size_t)pos0 * C);
-  copy_words_to_lds(reinterpret_cast<uint4*>(xs), mb * (C / 8), [=](int i) { return base + i; });
 }
 
 struct GemvItem {
@@ -991,13 +1031,21 @@ __device__ __forceinline__ size_t gemv_lds_head(const ExpertArgs& a) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
+// LDS the GEMV blocks stage beyond the lean discovery's: MB token vectors of C
+// values, then `sides` scale areas of scale_stage_words(rows, C) words each.
+template <int FMT>
+__host__ __device__ __forceinline__ size_t gemv_stage_bytes(int MB, int C, int rows, int sides) {
+  return al16((size_t)MB * C * 2) + (size_t)sides * 16 * scale_stage_words<FMT>(rows, C);
+}
+
 // Gate/up projection + SwiGLU of one workgroup: used expert `by`, `nr` blocks of
 // intermediate rows from bx * nr * rows_per_block; every lane group takes one
 // row i of each block and computes h[pos, i] = bf16(silu(W1[i].x) * (W3[i].x)).
-// The first block's weight loads are issued before the token vectors are
-// staged in LDS; the blocks then run one after another on one set of weight
-// registers, so `nr` changes neither a row's arithmetic nor the registers a
-// lane needs (a launch picks it so that all its workgroups are resident).
+// The first block's weight loads are issued before the token vectors and the
+// scales of all the workgroup's rows are staged in LDS; the blocks then run
+// one after another on one set of weight registers, so `nr` changes neither a
+// row's arithmetic nor the registers a lane needs (a launch picks it so that
+// all its workgroups are resident).
 template <int FMT, int MB>
 __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds,
                               int nr = 1) {
@@ -1009,12 +1057,23 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
   const int n_ch = H / VPC;
   const uint8_t* blob = a.slots + (size_t)it.slot * a.slot_stride;
   const uint4* W13 = reinterpret_cast<const uint4*>(blob + a.off_w13);
-  const float* S13f = reinterpret_cast<const float*>(blob + a.off_s13);
   const uint8_t* S13b = blob + a.off_s13;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
   const int i0 = bx * nr * rows_per_block + wv * groups + grp;     // this group's row in the first block
+  // the workgroup's gate rows [R0, R1) and up rows I + [R0, R1): their scales
+  // are staged at s_sc (gate) and s_sc + 16 SW (up)
+  const int R0 = bx * nr * rows_per_block, R1 = min(I, R0 + nr * rows_per_block);
+  const int SW = scale_stage_words<FMT>(nr * rows_per_block, H);
+  char* s_sc = lds + gemv_lds_head(a) + al16((size_t)MB * H * 2);
+  ScaleSpan gs{0, 0}, us{0, 0};
+  if constexpr (FMT != PE_W_BF16) {
+    gs = scale_span<FMT>(R0, R1, H);
+    us = scale_span<FMT>(I + R0, I + R1, H);
+  }
+  const uint16_t* x = a.x;
   const int32_t* ent = it.ent;
+  const int k = a.k;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
     uint4 wg[kMaxChunksInFlight], wu[kMaxChunksInFlight];
@@ -1022,8 +1081,25 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
       load_row(W13 + (size_t)i0 * n_ch, n_ch, lig, LG, wg);
       load_row(W13 + (size_t)(I + i0) * n_ch, n_ch, lig, LG, wu);
     }
-    __syncthreads();
-    stage_rows(xs, a.x, H, ent + tb, mb, a.k);
+    if (tb > 0) __syncthreads();     // the previous batch's token vectors are consumed
+    // the batch's token vectors, and with the first batch the scales
+    const int n16 = H / 8, xw = mb * n16, sw = tb == 0 ? gs.words + us.words : 0;
+    copy_words_to_lds(
+        xw + sw,
+        [=](int i) -> const uint4* {
+          if (i < xw) {
+            const int t = i / n16;
+            return reinterpret_cast<const uint4*>(x + (size_t)(ent[tb + t] / k) * H) + (i - t * n16);
+          }
+          const int j = i - xw;
+          return j < gs.words ? reinterpret_cast<const uint4*>(S13b + gs.begin) + j
+                              : reinterpret_cast<const uint4*>(S13b + us.begin) + (j - gs.words);
+        },
+        [=](int i) -> uint4* {
+          if (i < xw) return reinterpret_cast<uint4*>(xs) + i;
+          const int j = i - xw;
+          return reinterpret_cast<uint4*>(s_sc) + (j < gs.words ? j : SW + j - gs.words);
+        });
     __syncthreads();
 #pragma unroll 1
     for (int r = 0; r < nr; ++r) {
@@ -1036,10 +1112,16 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
       float g[MB], u[MB];
 #pragma unroll
       for (int t = 0; t < MB; ++t) { g[t] = 0.0f; u[t] = 0.0f; }
-      const float* sgf = S13f + (size_t)(ir >> 7) * (H / 128);
-      const float* suf = S13f + (size_t)(ru >> 7) * (H / 128);
-      const uint8_t* sgh = S13b + row_scale_off<FMT>(ir, H);
-      const uint8_t* suh = S13b + row_scale_off<FMT>(ru, H);
+      const char* sg = s_sc;
+      const char* su = s_sc + 16 * (size_t)SW;
+      if constexpr (FMT != PE_W_BF16) {
+        sg += scale_row_off<FMT>(ir, H) - gs.begin;
+        su += scale_row_off<FMT>(ru, H) - us.begin;
+      }
+      const float* sgf = reinterpret_cast<const float*>(sg);
+      const float* suf = reinterpret_cast<const float*>(su);
+      const uint8_t* sgh = reinterpret_cast<const uint8_t*>(sg);
+      const uint8_t* suh = reinterpret_cast<const uint8_t*>(su);
       for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
         dot_row<FMT, MB>(wg, n_ch, c0, LG, xs, H, mb, sgf, sgh, g);
         dot_row<FMT, MB>(wu, n_ch, c0, LG, xs, H, mb, suf, suh, u);
@@ -1060,24 +1142,18 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
 
 // Down projection of one workgroup: used expert `by`, rows from bx *
 // rows_per_block; every lane group takes two rows n, n+1 and writes
-// merged[entry, n] = w[entry] * (W2[n] . h[pos]).
-// With y_lds set, the workgroup also keeps its results in LDS, y_lds[entry *
-// rows_per_block + row - bx * rows_per_block], and marks the entries in
-// mark[entry] (for the fused down + top-k launch).
+// merged[entry, n] = w[entry] * (W2[n] . h[pos]).  The scales of the
+// workgroup's rows are staged in LDS with the first batch of h rows.
 template <int FMT, int MB>
-__device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds,
-                           float* y_lds = nullptr, unsigned char* mark = nullptr) {
+__device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows_per_block, char* lds) {
   GemvItem it;
   if (!gemv_item(a, by, it, lds)) return;
-  if (mark)
-    for (int t = threadIdx.x; t < it.m; t += blockDim.x) mark[it.ent[t]] = 1;
   uint16_t* hs = reinterpret_cast<uint16_t*>(lds + gemv_lds_head(a));   // [MB][I]
   constexpr int VPC = Fmt<FMT>::VPC;
   const int H = a.H, I = a.I;
   const int n_ch = I / VPC;
   const uint8_t* blob = a.slots + (size_t)it.slot * a.slot_stride;
   const uint4* W2 = reinterpret_cast<const uint4*>(blob + a.off_w2);
-  const float* S2f = reinterpret_cast<const float*>(blob + a.off_s2);
   const uint8_t* S2b = blob + a.off_s2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
@@ -1085,25 +1161,43 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
   const bool act0 = n0 < H, act1 = n0 + 1 < H;
   const uint4* r0 = W2 + (size_t)n0 * n_ch;
   const uint4* r1 = W2 + (size_t)(n0 + 1) * n_ch;
+  // the workgroup's rows [R0, R1): their scales are staged at s_sc
+  const int R0 = bx * rows_per_block, R1 = min(H, R0 + rows_per_block);
+  char* s_sc = lds + gemv_lds_head(a) + al16((size_t)MB * I * 2);
+  ScaleSpan ss{0, 0};
+  if constexpr (FMT != PE_W_BF16) ss = scale_span<FMT>(R0, R1, I);
+  const char* sc0 = s_sc;
+  const char* sc1 = s_sc;
+  if constexpr (FMT != PE_W_BF16) {
+    sc0 += scale_row_off<FMT>(n0, I) - ss.begin;
+    sc1 += scale_row_off<FMT>(act1 ? n0 + 1 : n0, I) - ss.begin;
+  }
+  const uint16_t* h = a.h;
   const int32_t* ent = it.ent;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
     uint4 w0[kMaxChunksInFlight], w1[kMaxChunksInFlight];
     if (act0) load_row(r0, n_ch, lig, LG, w0);
     if (act1) load_row(r1, n_ch, lig, LG, w1);
-    __syncthreads();
-    stage_consecutive(hs, a.h, I, it.off + tb, mb);
+    if (tb > 0) __syncthreads();     // the previous batch's h rows are consumed
+    // the batch's h rows (consecutive sorted positions), and with the first batch the scales
+    const int hw = mb * (I / 8), sw = tb == 0 ? ss.words : 0;
+    const uint4* hsrc = reinterpret_cast<const uint4*>(h + (size_t)(it.off + tb) * I);
+    copy_words_to_lds(
+        hw + sw,
+        [=](int i) { return i < hw ? hsrc + i : reinterpret_cast<const uint4*>(S2b + ss.begin) + (i - hw); },
+        [=](int i) { return i < hw ? reinterpret_cast<uint4*>(hs) + i : reinterpret_cast<uint4*>(s_sc) + (i - hw); });
     __syncthreads();
     if (!act0) continue;
     float y0[MB], y1[MB];
 #pragma unroll
     for (int t = 0; t < MB; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
     for (int c0 = lig;; c0 += LG * kMaxChunksInFlight) {
-      dot_row<FMT, MB>(w0, n_ch, c0, LG, hs, I, mb, S2f + (size_t)(n0 >> 7) * (I / 128),
-                       S2b + row_scale_off<FMT>(n0, I), y0);
+      dot_row<FMT, MB>(w0, n_ch, c0, LG, hs, I, mb, reinterpret_cast<const float*>(sc0),
+                       reinterpret_cast<const uint8_t*>(sc0), y0);
       if (act1)
-        dot_row<FMT, MB>(w1, n_ch, c0, LG, hs, I, mb, S2f + (size_t)((n0 + 1) >> 7) * (I / 128),
-                         S2b + row_scale_off<FMT>(n0 + 1, I), y1);
+        dot_row<FMT, MB>(w1, n_ch, c0, LG, hs, I, mb, reinterpret_cast<const float*>(sc1),
+                         reinterpret_cast<const uint8_t*>(sc1), y1);
       if (c0 + LG * kMaxChunksInFlight >= n_ch) break;
       load_row(r0, n_ch, c0 + LG * kMaxChunksInFlight, LG, w0);
       if (act1) load_row(r1, n_ch, c0 + LG * kMaxChunksInFlight, LG, w1);
@@ -1114,14 +1208,8 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
     for (int t = 0; t < MB; ++t) {
       if (t < mb && lig == t) {
         const int e = ent[tb + t];
-        const float v0 = a.topk_w[e] * y0[t];
-        a.merged[(size_t)e * H + n0] = v0;
-        if (y_lds) y_lds[(size_t)e * rows_per_block + (n0 - bx * rows_per_block)] = v0;
-        if (act1) {
-          const float v1 = a.topk_w[e] * y1[t];
-          a.merged[(size_t)e * H + n0 + 1] = v1;
-          if (y_lds) y_lds[(size_t)e * rows_per_block + (n0 + 1 - bx * rows_per_block)] = v1;
-        }
+        a.merged[(size_t)e * H + n0] = a.topk_w[e] * y0[t];
+        if (act1) a.merged[(size_t)e * H + n0 + 1] = a.topk_w[e] * y1[t];
       }
     }
   }
@@ -1425,19 +1513,23 @@ __device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 d
   }
 }
 
-// Device-planned step, launch B: the down projection of every expert of the
-// wave and the fixed-order top-k sum, by output rows.  Workgroup b owns the RB
-// rows [b*RB, b*RB + RB) that one wavefront covers in gemv_down_kernel's
-// geometry (two rows per lane group).  Its NW (1..8) wavefronts take the
-// wave's GEMV experts round-robin; each issues the weight loads of its first
-// two experts (their descriptors are one load away) before the workgroup stages
-// the step's h rows (if STAGE) and routed ids in LDS, and a later expert's as
-// soon as a register set is free.  Every entry's w[e] * (W2
+// One wave's down projection (every GEMV expert of wave 0) and the fixed-order
+// top-k sum, by output rows (launch B of a device-planned step, and the last
+// launch of a one-wave host-planned step).  Workgroup b owns the RB = 2 GR rows
+// [b*RB, b*RB + RB).  A wavefront's 64 / LG lane groups (LG lanes per row, as in
+// gemv_down_kernel) are GR row pairs times GE = 64 / (LG GR) experts: group g
+// takes rows r0 + 2 (g % GR) and + 1 of expert slot g / GR, so fewer rows per
+// workgroup spread short rows over more workgroups without changing a row's
+// lanes, chunk order or reduction.  The NW (1..8) wavefronts take the wave's
+// GEMV experts round-robin, GE at a time; each lane group issues the weight
+// loads of its first two experts (their descriptors are one load away) before
+// the workgroup stages the step's h rows (if STAGE) and routed ids in LDS, and
+// a later expert's as soon as a register set is free.  Every entry's w[e] * (W2
 // h)[row] goes to LDS; then each token's k entries are summed in j order
 // (invalid ids skipped) and rounded once to bf16: the arithmetic of down_block +
-// topk_sum_rows.  Workgroup 0 makes the new LRU-state copy current.
+// topk_sum_rows.  Workgroup 0 makes the new LRU-state copy current, if `flip`.
 template <int FMT, int MB, bool STAGE>
-__global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uint16_t* __restrict__ out,
+__global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, int GR, uint16_t* __restrict__ out,
                                                         int32_t* flip) {
   extern __shared__ __align__(16) char lds[];
   constexpr int VPC = Fmt<FMT>::VPC;
@@ -1445,20 +1537,22 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uin
   const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int groups = 64 / LG, lig = lane % LG, grp = lane / LG;
-  const int RB = 2 * groups, r0 = blockIdx.x * RB;
+  const int GE = groups / GR, gr = grp % GR, ge = grp / GR;
+  const int RB = 2 * GR, r0 = blockIdx.x * RB;
   float* s_y = reinterpret_cast<float*>(lds);                                          // [n][RB]
   int* s_id = reinterpret_cast<int*>(lds + al16(4 * (size_t)n * RB));                  // [n]
   uint16_t* s_h = reinterpret_cast<uint16_t*>(lds + al16(4 * (size_t)n * RB) + al16(4 * (size_t)n));  // [n][I]
   const int32_t* hdr = a.work + a.o.hdr;
   const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
   const int n_items = hdr[hdr_gemv(a.MW, 1)];               // wave 0's GEMV items start at 0
-  const int n0 = r0 + 2 * grp;
+  const int n0 = r0 + 2 * gr;
   const bool act0 = n0 < H, act1 = n0 + 1 < H;
-  // this wavefront's experts wv, wv + NW, wv + 2 NW, ...: the first two experts'
-  // first rounds of weight loads are issued before the staging, and each later
-  // one's as soon as its buffer is free (ping-pong between two named register
-  // sets)
-  int i0 = wv, i1 = wv + NW;
+  // this lane group's experts i, i + NW GE, i + 2 NW GE, ... (i = wv GE + ge):
+  // the first two experts' first rounds of weight loads are issued before the
+  // staging, and each later one's as soon as its buffer is free (ping-pong
+  // between two named register sets)
+  const int step = NW * GE;
+  int i0 = wv * GE + ge, i1 = i0 + step;
   int4 d0 = i0 < a.E ? desc[i0] : make_int4(0, 0, 0, 0);
   int4 d1 = i1 < a.E ? desc[i1] : make_int4(0, 0, 0, 0);
   DownRows rA, rB;
@@ -1473,14 +1567,14 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, uin
   const uint16_t* hbase = STAGE ? s_h : a.h;
   while (i0 < n_items) {
     down_rows_item<FMT, MB>(a, d0, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
-    i0 += 2 * NW;
+    i0 += 2 * step;
     if (i0 < n_items) {
       d0 = desc[i0];
       fetch_down_rows<FMT>(a, a.slots + (size_t)d0.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
     }
     if (i1 >= n_items) break;
     down_rows_item<FMT, MB>(a, d1, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
-    i1 += 2 * NW;
+    i1 += 2 * step;
     if (i1 < n_items) {
       d1 = desc[i1];
       fetch_down_rows<FMT>(a, a.slots + (size_t)d1.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
@@ -1544,6 +1638,17 @@ static GemvGeom down_geom(int wtype, const ExpertArgs& a) {
 
 static size_t lean_head(const ExpertArgs& a) { return a.lean ? lean_lds_bytes(a.T * a.k) : 0; }
 
+// gemv_stage_bytes for a format given at run time.
+static size_t gemv_stage(int wtype, int mb, int C, int rows, int sides) {
+  switch (wtype) {
+    case PE_W_BF16: return gemv_stage_bytes<PE_W_BF16>(mb, C, rows, sides);
+    case PE_W_FP8_B128: return gemv_stage_bytes<PE_W_FP8_B128>(mb, C, rows, sides);
+    case PE_W_INT8_G128: return gemv_stage_bytes<PE_W_INT8_G128>(mb, C, rows, sides);
+    case PE_W_MXFP4_B32: return gemv_stage_bytes<PE_W_MXFP4_B32>(mb, C, rows, sides);
+    default: return gemv_stage_bytes<PE_W_INT4_G128>(mb, C, rows, sides);
+  }
+}
+
 // Workgroups of kGemvThreads threads with `lds` bytes of LDS each that the
 // device holds at once (per-CU occupancy times CUs), cached per kernel and LDS
 // size; 0 if the runtime cannot tell.
@@ -1604,7 +1709,7 @@ void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, h
   if (items <= 0) return;
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t lds = lean_head(a) + (size_t)mb * a.H * 2;
+  const size_t lds = lean_head(a) + gemv_stage(wtype, mb, a.H, g.rows_per_block, 2);
   const dim3 grid(g.gx, items);
   PE_DISPATCH(wtype, mb, (gemv_gate_up_kernel<F_, M_><<<grid, kGemvThreads, lds, s>>>(a, g)));
 }
@@ -1613,7 +1718,7 @@ void launch_gemv_down(int wtype, const ExpertArgs& a, int items, int max_m, hipS
   if (items <= 0) return;
   const int mb = pick_mb(max_m);
   const GemvGeom g = down_geom(wtype, a);
-  const size_t lds = lean_head(a) + (size_t)mb * a.I * 2;
+  const size_t lds = lean_head(a) + gemv_stage(wtype, mb, a.I, g.rows_per_block, 1);
   const dim3 grid(g.gx, items);
   PE_DISPATCH(wtype, mb, (gemv_down_kernel<F_, M_><<<grid, kGemvThreads, lds, s>>>(a, g)));
 }
@@ -1626,14 +1731,26 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
   const size_t copier = copier_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds + (size_t)mb * a.H * 2;
-  const size_t lds = std::max(std::max(copier, plan_lds_bytes(d.E, d.K, n)), lean_head(a) + (size_t)mb * a.H * 2);
+  const size_t fixed = std::max(copier, plan_lds_bytes(d.E, d.K, n));
+  // LDS for nr row blocks per gate/up workgroup (their scales grow with nr)
+  auto lds_for = [&](int nr) {
+    return std::max(fixed, lean_head(a) + gemv_stage(wtype, mb, a.H, nr * g.rows_per_block, 2));
+  };
   // Row blocks per gate/up workgroup: the fewest that leave every workgroup of
   // the launch resident at once (a second dispatch round would start its
   // workgroups only after the first ones end).
-  int resident = 0;
-  PE_DISPATCH(wtype, mb, (resident = resident_blocks(reinterpret_cast<const void*>(&step_a_kernel<F_, M_>), lds)));
-  int nr = resident > 0 ? 1 : 2;
-  while (resident > 0 && nr < g.gx && P + 1 + ceil_div(g.gx, nr) * items > resident) ++nr;
+  auto resident_at = [&](int nr) {
+    int r = 0;
+    PE_DISPATCH(wtype, mb, (r = resident_blocks(reinterpret_cast<const void*>(&step_a_kernel<F_, M_>), lds_for(nr))));
+    return r;
+  };
+  int nr = 1;
+  if (resident_at(1) <= 0) {
+    nr = 2;
+  } else {
+    while (nr < g.gx && P + 1 + ceil_div(g.gx, nr) * items > resident_at(nr)) ++nr;
+  }
+  const size_t lds = lds_for(nr);
   const int blocks = P + 1 + ceil_div(g.gx, nr) * items;
   PE_DISPATCH(wtype, mb, (step_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(p, P, a, g, nr)));
 }
@@ -1642,7 +1759,7 @@ void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int
                    size_t stride, size_t copy_bytes, hipStream_t s) {
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t lds = kStreamScaleLds + (size_t)mb * a.H * 2;
+  const size_t lds = std::max(kStreamScaleLds + (size_t)mb * a.H * 2, gemv_stage(wtype, mb, a.H, g.rows_per_block, 2));
   const int blocks = P + g.gx * hit_items;
   PE_DISPATCH(wtype, mb, (wave_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(a, g, P, host_rows, stride, copy_bytes)));
 }
@@ -1650,21 +1767,26 @@ void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int
 void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s) {
   const int mb = pick_mb(max_m);
   const int LG = lanes_per_row(a.I / vpc_of(wtype));
-  const int RB = 2 * (64 / LG);
+  const int groups = 64 / LG;
+  // row pairs per workgroup: a power of two, at most one per lane group, and few
+  // enough for a workgroup on every CU (256) when the rows allow it
+  int GR = groups;
+  while (GR > 1 && ceil_div(a.H, 2 * GR) < 256) GR >>= 1;
+  const int RB = 2 * GR, GE = groups / GR;
   const int n = a.T * a.k;
-  // wavefronts per workgroup: one per expert, at most 8, and no more than keep
-  // every workgroup of the launch resident at once (about 2048 wavefronts of
-  // this kernel's size on 256 CUs)
+  // wavefronts per workgroup: enough for the wave's experts GE at a time, at
+  // most 8, and no more than keep every workgroup of the launch resident at
+  // once (about 2048 wavefronts of this kernel's size on 256 CUs)
   const int grid_x = ceil_div(a.H, RB);
   const int items = std::min(n, a.E);
-  const int nw = std::max(1, std::min(std::min(8, items), std::max(1, 2048 / grid_x)));
+  const int nw = std::max(1, std::min(std::min(8, ceil_div(items, GE)), std::max(1, 2048 / grid_x)));
   const size_t head = al16(4 * (size_t)n * RB) + al16(4 * (size_t)n);
   const size_t staged = head + (size_t)n * a.I * 2;
   const dim3 grid(grid_x), block(64 * nw);
   if (staged <= 64 * 1024) {
-    PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, true><<<grid, block, staged, s>>>(a, LG, out, flip)));
+    PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, true><<<grid, block, staged, s>>>(a, LG, GR, out, flip)));
   } else {
-    PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, false><<<grid, block, head, s>>>(a, LG, out, flip)));
+    PE_DISPATCH(wtype, mb, (down_sum_kernel<F_, M_, false><<<grid, block, head, s>>>(a, LG, GR, out, flip)));
   }
 }
 
