@@ -902,10 +902,11 @@ __device__ __forceinline__ void group_reduce(float (&acc)[MB], int LG) {
   }
 }
 
-// Copy n 16-byte words into LDS, word i from src_of(i) to dst[i], every thread
-// of the block taking words threadIdx.x, + blockDim.x, ...  Each thread issues
-// four loads before it stores them, so a copy of more words than threads costs
-// one load latency per four words instead of one per word.
+// Copy n 16-byte words into LDS, word i from src_of(i) to dst_of(i), every
+// thread of the block taking words threadIdx.x, + blockDim.x, ...  Each thread
+// issues up to four loads before it stores them (the last round too), so a copy
+// of more words than threads costs one load latency per four words instead of
+// one per word.
 template <class SrcOf, class DstOf>
 __device__ __forceinline__ void copy_words_to_lds(int n, SrcOf src_of, DstOf dst_of) {
   const int st = blockDim.x;
@@ -917,7 +918,16 @@ __device__ __forceinline__ void copy_words_to_lds(int n, SrcOf src_of, DstOf dst
     *dst_of(i + 2 * st) = v2;
     *dst_of(i + 3 * st) = v3;
   }
-  for (; i < n; i += st) *dst_of(i) = *src_of(i);
+  if (i < n) {
+    const bool h1 = i + st < n, h2 = i + 2 * st < n;
+    const uint4 v0 = *src_of(i);
+    uint4 v1 = v0, v2 = v0;
+    if (h1) v1 = *src_of(i + st);
+    if (h2) v2 = *src_of(i + 2 * st);
+    *dst_of(i) = v0;
+    if (h1) *dst_of(i + st) = v1;
+    if (h2) *dst_of(i + 2 * st) = v2;
+  }
 }
 
 template <class SrcOf>

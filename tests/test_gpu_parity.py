@@ -168,6 +168,23 @@ def test_largest_hidden_and_inter(wtype, batch):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("wtype", ["fp8", "int4", "mxfp4"])
+def test_widest_token_batch_at_largest_hidden(wtype):
+    """Batch 8, the widest GEMV token batch, at H = 4096: a gate/up workgroup
+    stages 64 KB of token vectors and its rows' scales (more LDS than one
+    workgroup may take on parts before gfx950).  16 entries fill K = 16: a
+    device-planned step, then the same steps host-planned (one wave each),
+    bitwise equal, and both against the oracle."""
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=16, top_k=2, resident=16, hidden=4096, inter=256,
+                        wtype=wtype, batch=8, steps=3)
+    print("case batch 8 H=4096 %s" % wtype, flush=True)
+    got, st = _run_decode(wl)
+    assert st["device_planned"] == wl.steps
+    hp, st = _run_decode(wl, flags=pe.PE_FLAG_FORCE_HOST_PLAN)
+    assert st["host_planned"] == wl.steps
+    assert np.array_equal(got, hp)
+
+
 @pytest.mark.parametrize("batch", [4, 9])
 def test_most_experts(batch):
     """E = 1024, the largest expert count: 32 entries fill K = 32 exactly (one
@@ -273,6 +290,44 @@ def test_repeated_ids_within_a_token(wtype):
         st = m.stats()
         if flags == 0:
             assert st["device_planned"] == 1 and st["host_planned"] == 1 and st["bad_ids"] == 1
+        m.close()
+    for ci in range(len(cases)):
+        assert np.array_equal(outs[(0, ci)], outs[(pe.PE_FLAG_UNPAGED, ci)]), ci
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4"])
+def test_expert_with_more_entries_than_a_token_batch(wtype):
+    """An expert routed by 10 or 11 of a step's tokens runs its GEMV rows in two
+    token batches (8, then the rest), re-staging the token vectors but keeping
+    the scales staged with the first.  Three steps: device-planned with the
+    expert paged in (streamed), device-planned with it resident, host-planned
+    (13 entries > K = 12, one wave); against the oracle and an unpaged run."""
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=16, top_k=1, resident=12, hidden=512, inter=256,
+                        wtype=wtype, batch=13, steps=1)
+    print("case long expert %s" % wtype, flush=True)
+    x = torch.from_numpy(synth.hidden_states(wl, 0, 13).view(np.int16)).view(torch.bfloat16).to(DEV)
+    a_ids = np.array([3] * 10 + [5, 7], np.int32).reshape(12, 1)
+    b_ids = np.array([3] * 6 + [9] + [3] * 5 + [5], np.int32).reshape(13, 1)
+    cases = [a_ids, a_ids, b_ids]
+    rng = np.random.default_rng(5)
+    ws = [rng.random(c.shape).astype(np.float32) for c in cases]
+    outs = {}
+    for flags in (0, pe.PE_FLAG_UNPAGED):
+        m = harness.make_moe(wl, flags=flags)
+        harness.load_store(m, wl)
+        for ci, ids_np in enumerate(cases):
+            T = ids_np.shape[0]
+            out = torch.empty((T, wl.hidden), dtype=torch.bfloat16, device=DEV)
+            m.forward(0, x[:T], torch.from_numpy(ids_np).to(DEV), torch.from_numpy(ws[ci]).to(DEV), out, T=T)
+            torch.cuda.synchronize()
+            outs[(flags, ci)] = harness.bf16_bits(out)
+            if flags == 0:
+                ref = moe.moe_layer(formats.bf16_to_f32(harness.bf16_bits(x[:T])), ids_np, ws[ci],
+                                    _expert_fn(wl, 0), num_experts=wl.experts)
+                _check_close(outs[(flags, ci)], ref, wtype, "case %d" % ci)
+        st = m.stats()
+        if flags == 0:
+            assert st["device_planned"] == 2 and st["host_planned"] == 1 and st["page_ins"] == 4
         m.close()
     for ci in range(len(cases)):
         assert np.array_equal(outs[(0, ci)], outs[(pe.PE_FLAG_UNPAGED, ci)]), ci
