@@ -47,6 +47,8 @@ def part_bytes(wtype, hidden, inter):
     if wtype == "mxfp4":
         return I * H, I * H // 2, 2 * I * (H // 32), H * (I // 32)
     raise ValueError(wtype)
+
+
 PCIE5_X16_GBS = 32.0 * 16 * 128 / 130 / 8   # 63.0 GB/s per direction
 
 
