@@ -9,8 +9,8 @@
  * (already-resident experts first), makes each wave resident by evicting the
  * least recently used experts outside the wave and copying in the missing
  * ones, runs the SwiGLU expert FFN over the wave's own entries (each
- * (token, expert) output already multiplied by its router weight, no top-k
- * sum), keeps every entry once (per block of output rows in LDS on a
+ * (token, expert) output scaled by the entry's router weight, no top-k sum
+ * yet), keeps every entry once (per block of output rows in LDS on a
  * device-planned step, in a merged buffer on a host-planned one), and finally
  * applies one fixed-order top-k sum.  The output equals the unpaged layer's.
  *

@@ -10,8 +10,8 @@ Contents (citations are to the SGLang "Paged Experts" documentation page,
 docs.sglang.io/docs/advanced_features/paged_experts, and the DonWeb blog post
 "SGLang Paged Experts: corré MoE más grandes que tu VRAM"):
 
-- formats: decoding of bf16, OCP e4m3fn block-FP8 and group-128 int4 expert
-  weights into fp32.
+- formats: decoding of bf16, OCP e4m3fn block-FP8, group-128 int4 and int8,
+  and OCP MXFP4 expert weights into fp32.
 - moe: the unpaged MoE layer — the docs page ("Why Paged Experts?", and step 4
   of "A step: waves, page-in, merge") says the paged layer returns exactly
   this.

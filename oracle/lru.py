@@ -8,7 +8,7 @@ and copies only the missing ones.  Each MoE layer has its own K-slot table
 ("The K-slot table and the host store"); captured and uncaptured steps share
 one LRU state ("Captured decode").
 
-Readings where the page is silent (each also listed in the design notes):
+Readings where the page is silent:
 - distinct experts are ordered resident-first, each part by ascending id;
 - waves are consecutive chunks of K of that order;
 - one wave is one use: every expert of the wave gets last_use = tick, and

@@ -1,9 +1,9 @@
 """The unpaged MoE layer.  TEST INFRASTRUCTURE (oracle).
 
-The docs page says the paged layer "produces the same output as the unpaged
-one" ("Why Paged Experts?") and that the merged entries go through "the same
-top-k sum the kernel would have performed" (step 4 of "A step: waves,
-page-in, merge").  So the reference result is the ordinary routed MoE layer
+The docs page states that paging leaves the layer's output unchanged ("Why
+Paged Experts?") and that the merged entries are summed over top-k as the
+unpaged kernel sums them (step 4 of "A step: waves, page-in, merge").  So the
+reference result is the ordinary routed MoE layer
 
     out[t] = sum_{j=0}^{k-1}  w[t,j] * W2_e ( silu(W1_e x_t) * (W3_e x_t) ),  e = ids[t,j]
 

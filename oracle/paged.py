@@ -1,11 +1,11 @@
 """A CPU paged MoE layer built on the LRU simulator.  TEST INFRASTRUCTURE (oracle).
 
 Steps 3-4 of "A step: waves, page-in, merge" (SGLang Paged Experts docs):
-each wave runs the experts it holds over its own routed entries, writing every
-(token, expert) output, already multiplied by its router weight, into one
-merged buffer; after all waves the merged entries go through the same top-k
-sum.  Because each entry is written once, by the wave that holds its expert,
-the output cannot depend on how experts were split into waves.  Slot
+a wave computes, for each routed entry whose expert it holds, the expert's
+output scaled by the entry's router weight and stores it in its row of one
+merged buffer; once every wave has run, one top-k sum over the merged rows
+gives the layer output.  Every entry is stored exactly once, by the wave of
+its expert, so the wave split has no way to change the result.  Slot
 contents are modelled explicitly (a slot holds whatever expert was last
 copied into it), so a wrong plan shows up as wrong output.
 """
