@@ -1477,18 +1477,20 @@ __device__ __forceinline__ void fetch_down_rows(const ExpertArgs& a, const uint8
 }
 
 // One GEMV expert's down projection for rows n0, n0 + 1 of one lane group:
-// s_y[e * RB + row - r0] = w[e] * (W2[row] . h[pos]) for each of its entries e.
-// `r` holds the first round of loads of token batch 0.  Per lane the chunks run
-// in ascending order and the group reduces by the xor butterfly, as in
-// down_block.
+// s_y[e * RB + row - r0] = w[e] * (W2[row] . h[pos]) for each of its entries e
+// (s_ent: the entry at each sorted position, s_w: router weights by entry,
+// both staged in LDS).  `r` holds the first round of loads of token batch 0.
+// Per lane the chunks run in ascending order and the group reduces by the xor
+// butterfly, as in down_block.
 template <int FMT, int MB>
 __device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 dsc, DownRows& r, int n0,
                                                bool act0, bool act1, int lig, int LG, int n_ch,
-                                               const uint16_t* hbase, float* s_y, int RB, int r0) {
+                                               const uint16_t* hbase, float* s_y, int RB, int r0,
+                                               const int* s_ent, const float* s_w) {
   constexpr int VPC = Fmt<FMT>::VPC;
   const int I = a.I, off = dsc.y, m = dsc.z;
   const uint8_t* blob = a.slots + (size_t)dsc.x * a.slot_stride;
-  const int32_t* ent = a.work + a.o.entries + off;
+  const int* ent = s_ent + off;
   for (int tb = 0; tb < m; tb += MB) {
     const int mb = min(MB, m - tb);
     if (tb > 0) fetch_down_rows<FMT>(a, blob, n0, act0, act1, lig, LG, n_ch, r);
@@ -1515,7 +1517,7 @@ __device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 d
     for (int t = 0; t < MB; ++t) {
       if (t < mb && lig == t && act0) {
         const int e = ent[tb + t];
-        const float we = a.topk_w[e];
+        const float we = s_w[e];
         s_y[(size_t)e * RB + n0 - r0] = we * y0[t];
         if (act1) s_y[(size_t)e * RB + n0 + 1 - r0] = we * y1[t];
       }
@@ -1550,8 +1552,10 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, int
   const int GE = groups / GR, gr = grp % GR, ge = grp / GR;
   const int RB = 2 * GR, r0 = blockIdx.x * RB;
   float* s_y = reinterpret_cast<float*>(lds);                                          // [n][RB]
-  int* s_id = reinterpret_cast<int*>(lds + al16(4 * (size_t)n * RB));                  // [n]
-  uint16_t* s_h = reinterpret_cast<uint16_t*>(lds + al16(4 * (size_t)n * RB) + al16(4 * (size_t)n));  // [n][I]
+  int* s_id = reinterpret_cast<int*>(lds + al16(4 * (size_t)n * RB));                  // [n] routed ids
+  int* s_ent = s_id + al16(4 * (size_t)n) / 4;                                         // [n] entry by sorted position
+  float* s_w = reinterpret_cast<float*>(s_ent + al16(4 * (size_t)n) / 4);              // [n] router weights
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(s_w + al16(4 * (size_t)n) / 4);           // [n][I]
   const int32_t* hdr = a.work + a.o.hdr;
   const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
   const int n_items = hdr[hdr_gemv(a.MW, 1)];               // wave 0's GEMV items start at 0
@@ -1568,7 +1572,16 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, int
   DownRows rA, rB;
   if (i0 < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d0.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
   if (i1 < n_items) fetch_down_rows<FMT>(a, a.slots + (size_t)d1.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rB);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) s_id[i] = a.ids[i];
+  // the routed ids, the sorted entry order (the step's valid entries, at most
+  // n; positions past them are read but never used) and the router weights
+  const int32_t* ents = a.work + a.o.entries;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int id = a.ids[i], en = ents[i];
+    const float w = a.topk_w[i];
+    s_id[i] = id;
+    s_ent[i] = en;
+    s_w[i] = w;
+  }
   if constexpr (STAGE) {
     const uint4* hw = reinterpret_cast<const uint4*>(a.h);
     copy_words_to_lds(reinterpret_cast<uint4*>(s_h), n * I / 8, [=](int i) { return hw + i; });
@@ -1576,14 +1589,14 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, int
   __syncthreads();
   const uint16_t* hbase = STAGE ? s_h : a.h;
   while (i0 < n_items) {
-    down_rows_item<FMT, MB>(a, d0, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
+    down_rows_item<FMT, MB>(a, d0, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0, s_ent, s_w);
     i0 += 2 * step;
     if (i0 < n_items) {
       d0 = desc[i0];
       fetch_down_rows<FMT>(a, a.slots + (size_t)d0.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
     }
     if (i1 >= n_items) break;
-    down_rows_item<FMT, MB>(a, d1, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0);
+    down_rows_item<FMT, MB>(a, d1, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0, s_ent, s_w);
     i1 += 2 * step;
     if (i1 < n_items) {
       d1 = desc[i1];
@@ -1790,7 +1803,7 @@ void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, i
   const int grid_x = ceil_div(a.H, RB);
   const int items = std::min(n, a.E);
   const int nw = std::max(1, std::min(std::min(8, ceil_div(items, GE)), std::max(1, 2048 / grid_x)));
-  const size_t head = al16(4 * (size_t)n * RB) + al16(4 * (size_t)n);
+  const size_t head = al16(4 * (size_t)n * RB) + 3 * al16(4 * (size_t)n);
   const size_t staged = head + (size_t)n * a.I * 2;
   const dim3 grid(grid_x), block(64 * nw);
   if (staged <= 64 * 1024) {
