@@ -893,12 +893,35 @@ __device__ __forceinline__ void dot_row(const uint4 (&w)[kMaxChunksInFlight], in
   }
 }
 
-// Sum over the LG lanes of a group (xor butterfly; every lane gets the total).
+// The value of lane (this lane xor m) for m = 1, 2, 4, 8 by DPP lane moves
+// (quad_perm 1,0,3,2; quad_perm 2,3,0,1; row_half_mirror, which reads lane xor
+// 7 within 8, then quad_perm 3,2,1,0; row_ror:8 within a row of 16), m = 16 by
+// ds_swizzle (xor 16 within 32) and m = 32 through ds_bpermute.
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  const int x = __float_as_int(v);
+  switch (m) {
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    case 4: {
+      const int h = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, false));
+    }
+    case 8: return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+    case 16: return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+    default: return __shfl_xor(v, m, 64);
+  }
+}
+
+// Sum over the LG lanes of a group (xor butterfly, partners LG/2, ..., 2, 1;
+// every lane gets the same total).  The masks are uniform, so the branches
+// on them are scalar.
 template <int MB>
 __device__ __forceinline__ void group_reduce(float (&acc)[MB], int LG) {
-  for (int off = LG >> 1; off > 0; off >>= 1) {
 #pragma unroll
-    for (int t = 0; t < MB; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
+  for (int off = 32; off > 0; off >>= 1) {
+    if (off >= LG) continue;
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[t] += lane_xor(acc[t], off);
   }
 }
 
