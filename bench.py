@@ -70,8 +70,6 @@ def parse():
     ap.add_argument("--repeats", type=int, default=2, help="timed repetitions (best and median reported)")
     ap.add_argument("--eager", action="store_true",
                     help="profiling: run device-planned steps without the hipGraph (per-dispatch counters)")
-    ap.add_argument("--layers", type=int, default=None,
-                    help="profiling: fewer MoE layers (never used for the reported number)")
     ap.add_argument("--sweep", action="store_true",
                     help="concurrency sweep: decode tok/s for every batch in --sweep-batches at every K in "
                          "--sweep-resident (the workload's format and routing), one JSON line per point")
@@ -106,8 +104,6 @@ def main():
     steps = args.steps or base.steps
     warmup = max(0, args.warmup)
     over = {"steps": max(steps, warmup, base.steps)}
-    if args.layers:
-        over["layers"] = args.layers
     wl = synth.workload(args.workload, **over)
     dev = "cuda:0"
     torch.cuda.init()
