@@ -135,3 +135,33 @@ def test_suggest_k_matches_sizing_rule_and_docs_example():
             assert abs(got - want) <= 1 and got == min(128, int(budget // (copied * 48)))
     with pytest.raises(pe.PEError):
         pe.pe_suggest_k("bf16", 2048, 768, 48, 128, 8, 1e9)       # fewer than top_k slots
+
+
+def _header_text():
+    src = open(os.path.join(ROOT, "include", "pe.h")).read()
+    return re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+
+
+def test_binding_constants_match_the_header():
+    defs = dict(re.findall(r"^#define\s+(PE_\w+)\s+(-?\d+)u?\s*$", _header_text(), flags=re.M))
+    names = [n for n in defs if n.startswith(("PE_OK", "PE_ERR_", "PE_W_", "PE_FLAG_"))]
+    assert len(names) >= 15
+    for n in names:
+        assert getattr(pe, n) == int(defs[n]), n
+    stages = sorted((int(v), n) for n, v in defs.items() if n.startswith("PE_STAGE_"))
+    assert [n[len("PE_STAGE_"):].lower() for _, n in stages] == list(pe.STAGES)
+    assert int(defs["PE_NUM_STAGES"]) == len(pe.STAGES)
+
+
+def _struct_fields(name):
+    body = re.search(r"typedef struct \{(.*?)\}\s*" + name + r";", _header_text(), flags=re.S).group(1)
+    return re.findall(r"^\s*(int|unsigned|uint64_t)\s+(\w+);", body, flags=re.M)
+
+
+def test_binding_structs_match_the_header():
+    ct = {"int": "c_int", "unsigned": "c_uint", "uint64_t": "c_uint64"}
+    from host_paged_expert_amd import _binding
+    for name, cls in (("pe_config", _binding.pe_config), ("pe_stats", _binding.pe_stats)):
+        want = [(f, ct[t]) for t, f in _struct_fields(name)]
+        got = [(f, t.__name__) for f, t in cls._fields_]
+        assert got == want, name
