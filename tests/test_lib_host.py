@@ -154,14 +154,16 @@ def test_binding_constants_match_the_header():
 
 
 def _struct_fields(name):
-    body = re.search(r"typedef struct \{(.*?)\}\s*" + name + r";", _header_text(), flags=re.S).group(1)
+    body = re.search(r"typedef struct \{((?:(?!typedef struct).)*?)\}\s*" + name + r";", _header_text(),
+                     flags=re.S).group(1)
     return re.findall(r"^\s*(int|unsigned|uint64_t)\s+(\w+);", body, flags=re.M)
 
 
 def test_binding_structs_match_the_header():
-    ct = {"int": "c_int", "unsigned": "c_uint", "uint64_t": "c_uint64"}
+    import ctypes
     from host_paged_expert_amd import _binding
+    ct = {"int": ctypes.c_int, "unsigned": ctypes.c_uint, "uint64_t": ctypes.c_uint64}
     for name, cls in (("pe_config", _binding.pe_config), ("pe_stats", _binding.pe_stats)):
         want = [(f, ct[t]) for t, f in _struct_fields(name)]
-        got = [(f, t.__name__) for f, t in cls._fields_]
-        assert got == want, name
+        assert len(want) >= 9, name
+        assert list(cls._fields_) == want, name
