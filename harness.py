@@ -23,11 +23,14 @@ def host_threads() -> int:
     return max(1, min(16, n))
 
 
-def make_moe(wl, flags=0, max_tokens=None, device=0):
+def make_moe(wl, flags=0, max_tokens=None, device=0, plan_log_steps=0):
+    """A PagedMoE context for the workload; plan_log_steps > 0 turns on the plan log."""
     if max_tokens is None:
         max_tokens = max(wl.batch, wl.prefill_tokens, 1)
+    if plan_log_steps:
+        flags |= pe.PE_FLAG_PLAN_LOG
     return pe.PagedMoE(wl.layers, wl.experts, wl.top_k, wl.resident, wl.hidden, wl.inter, max_tokens,
-                       wl.wtype, device, flags)
+                       wl.wtype, device, flags, plan_log_steps)
 
 
 def load_store(moe, wl, threads=None, layers=None, experts=None, progress=None):
@@ -75,8 +78,10 @@ class DecodeRunner:
     `capture` is set, one step through every layer is captured once as a
     hipGraph and replayed; the graph picks its step's inputs from x_all /
     ids_all / w_all on the device with a step counter that it advances itself.
-    Otherwise pe_forward runs eagerly per layer.  The latest step's output is
-    in `out` [L, B, H].  `rewind()` makes the next step step 0 again.
+    Otherwise pe_forward runs eagerly per layer, called straight through the
+    C ABI with addresses worked out once (the tensors are checked once, here).
+    The latest step's output is in `out` [L, B, H].  `rewind()` makes the next
+    step step 0 again.
     """
 
     def __init__(self, moe, wl, x_all, ids_all, w_all, out, stream, capture=True):
@@ -87,6 +92,16 @@ class DecodeRunner:
         self.s = 0
         self.sidx = torch.zeros(1, dtype=torch.long, device=out.device)
         self.graph = None
+        S, L, B = ids_all.shape[0], wl.layers, wl.batch
+        assert tuple(x_all.shape) == (S, B, wl.hidden) and tuple(ids_all.shape) == (S, L, B, wl.top_k)
+        assert tuple(w_all.shape) == (S, L, B, wl.top_k) and tuple(out.shape) == (L, B, wl.hidden)
+        moe._check_step(x_all.view(S * B, wl.hidden), ids_all.view(S * L * B, wl.top_k),
+                        w_all.view(S * L * B, wl.top_k), out.view(L * B, wl.hidden), B)
+        self._xs, self._ids, self._ws = x_all.data_ptr(), ids_all.data_ptr(), w_all.data_ptr()
+        self._out = out.data_ptr()
+        self._sx, self._sid = B * wl.hidden * 2, B * wl.top_k * 4       # bytes per step / layer
+        self._handle = stream.cuda_stream
+        self.S = S
         if self.captured:
             side = torch.cuda.Stream(device=out.device)
             side.wait_stream(stream)
@@ -105,15 +120,21 @@ class DecodeRunner:
             self.graph = g
 
     def run(self, n):
+        if n < 0 or self.s + n > self.S:
+            raise IndexError("steps %d..%d outside the %d-step input window" % (self.s, self.s + n - 1, self.S))
         if self.captured:
             for _ in range(n):
                 self.graph.replay()
         else:
+            fwd, ctx, L, B, h = pe.lib().pe_forward, self.moe.ctx, self.wl.layers, self.wl.batch, self._handle
             for i in range(n):
                 s = self.s + i
-                for l in range(self.wl.layers):
-                    self.moe.forward(l, self.x_all[s], self.ids_all[s, l], self.w_all[s, l], self.out[l],
-                                     stream=self.stream)
+                x = self._xs + s * self._sx
+                for l in range(L):
+                    at = (s * L + l) * self._sid
+                    rc = fwd(ctx, l, x, self._ids + at, self._ws + at, B, self._out + l * self._sx, h)
+                    if rc != pe.PE_OK:
+                        raise pe.PEError(rc, pe.pe_last_error())
         self.s += n
 
     def rewind(self):

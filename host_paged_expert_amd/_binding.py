@@ -8,6 +8,8 @@ raise PEError with the library's message.
 import ctypes
 import os
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpe.so")
 
@@ -30,13 +32,14 @@ WTYPES = {"bf16": PE_W_BF16, "fp8": PE_W_FP8_B128, "int4": PE_W_INT4_G128, "int8
 PE_FLAG_PAGEIN_DMA = 1
 PE_FLAG_FORCE_HOST_PLAN = 2
 PE_FLAG_UNPAGED = 4
+PE_FLAG_PLAN_LOG = 8
 
 
 class pe_config(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int), ("num_experts", ctypes.c_int), ("top_k", ctypes.c_int),
                 ("num_resident", ctypes.c_int), ("hidden", ctypes.c_int), ("inter", ctypes.c_int),
                 ("max_tokens", ctypes.c_int), ("device", ctypes.c_int), ("wtype", ctypes.c_int),
-                ("flags", ctypes.c_uint)]
+                ("flags", ctypes.c_uint), ("plan_log_steps", ctypes.c_int)]
 
 
 class pe_stats(ctypes.Structure):
@@ -68,6 +71,8 @@ SIGNATURES = {
     "pe_get_lru_state": (_i, [_vp, _i, _vp, _vp, _vp, _vp]),
     "pe_get_plan": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pe_get_slot_map": (_i, [_vp, _i, _vp, _i, _vp]),
+    "pe_plan_log_record_words": (_i, [_vp]),
+    "pe_get_plan_log": (_i, [_vp, _i, _vp, _i, _vp, _vp]),
     "pe_get_stats": (_i, [_vp, ctypes.POINTER(pe_stats)]),
     "pe_reset_stats": (_i, [_vp]),
     "pe_link_probe": (_i, [_vp, _sz, _i, _i, ctypes.POINTER(ctypes.c_double), _vp]),
@@ -125,9 +130,9 @@ def _stream(s):
 # ---------------------------------------------------------------- entry points
 
 def pe_create(num_layers, num_experts, top_k, num_resident, hidden, inter, max_tokens, wtype="bf16",
-              device=0, flags=0):
+              device=0, flags=0, plan_log_steps=0):
     cfg = pe_config(num_layers, num_experts, top_k, num_resident, hidden, inter, max_tokens, device,
-                    WTYPES[wtype] if isinstance(wtype, str) else wtype, flags)
+                    WTYPES[wtype] if isinstance(wtype, str) else wtype, flags, plan_log_steps)
     out = ctypes.c_void_p()
     _check(lib().pe_create(ctypes.byref(cfg), ctypes.byref(out)))
     return out.value
@@ -210,6 +215,42 @@ def pe_get_slot_map(ctx, layer, T, top_k, stream=None):
     out = np.empty(T * top_k, np.int32)
     _check(lib().pe_get_slot_map(ctx, layer, out.ctypes.data, T, _stream(stream)))
     return out
+
+
+def pe_plan_log_record_words(ctx):
+    v = lib().pe_plan_log_record_words(ctx)
+    if v < 0:
+        _check(v)
+    return v
+
+
+def pe_get_plan_log(ctx, layer, max_records, stream=None):
+    """The layer's most recent plan-log records, oldest first, as an int32
+    array [n, record_words] (layout in include/pe.h)."""
+    import numpy as np
+    rw = pe_plan_log_record_words(ctx)
+    buf = np.zeros((max(max_records, 1), rw), np.int32)
+    n = ctypes.c_int()
+    _check(lib().pe_get_plan_log(ctx, layer, buf.ctypes.data, max_records, ctypes.byref(n), _stream(stream)))
+    return buf[:n.value]
+
+
+def parse_plan_record(rec, K, max_waves, max_entries):
+    """Split one plan-log record into its fields (layout in include/pe.h)."""
+    MW = max_waves
+    o = 4
+    nw = int(rec[o]); o += 1
+    counts = rec[o:o + MW]; o += MW
+    ex = rec[o:o + MW * K].reshape(MW, K); o += MW * K
+    sl = rec[o:o + MW * K].reshape(MW, K); o += MW * K
+    ev = rec[o:o + MW * K].reshape(MW, K); o += MW * K
+    T = int(rec[1])
+    slot_of = rec[o:o + max_entries]; o += max_entries
+    waves = [{"count": int(counts[w]), "experts": ex[w, :counts[w]].copy(), "slots": sl[w, :counts[w]].copy(),
+              "evicted": ev[w, :counts[w]].copy()} for w in range(nw)]
+    return {"seq": int(rec[0]), "T": T, "tick": int(rec[2]) & 0xFFFFFFFF, "n_waves": nw, "waves": waves,
+            "slot_of": slot_of.copy(), "slot_expert": rec[o:o + K].copy(),
+            "last_use": rec[o + K:o + 2 * K].astype(np.int64) & 0xFFFFFFFF}
 
 
 def pe_get_stats(ctx):

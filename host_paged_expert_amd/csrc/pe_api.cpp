@@ -108,7 +108,6 @@ struct pe_ctx {
   BlobLayout b{};
   bool unpaged = false;
   int mfma_min = pe::kNoMfma;         // = d.mfma_min
-  int stream_wgs = kStreamWgs;        // copier workgroups of a device-planned step
   uint8_t* host_store = nullptr;       // page-locked, mapped: [L][E][stride]
   uint8_t* host_store_dev = nullptr;   // its device-visible address
   uint8_t* slots = nullptr;            // device: [L][K][stride]
@@ -117,11 +116,21 @@ struct pe_ctx {
   uint16_t* h = nullptr;               // device: [max_entries][I] bf16
   float* merged = nullptr;             // device: [max_entries][H] fp32
   unsigned long long* stats = nullptr; // device: [ST_COUNT]
-  int32_t* st_ids = nullptr;           // pinned staging: [max_entries]
-  int32_t* st_blk = nullptr;           // pinned: [L][layer_words], the host mirror of each layer's block and
-                                       // work lists (a host-planned step uploads both in one copy)
-  std::vector<char> mirror_ok;         // per layer: st_blk holds the device block's LRU state
+  // Page-locked, mapped, coherent host staging of host-planned steps: the routed
+  // ids and the host mirror of each layer's block and work lists.  A step's
+  // first launch writes the ids and the block's LRU state into them through
+  // their device addresses; the host plans in the mirror, and one more launch
+  // reads the block and work lists back from it.
+  int32_t* st_ids = nullptr;           // [max_entries]
+  int32_t* st_blk = nullptr;           // [L][layer_words]
+  int32_t* st_ids_dev = nullptr;       // device-visible addresses of the two
+  int32_t* st_blk_dev = nullptr;
   pe::HostPlanSummary* sum = nullptr;
+  // plan log (PE_FLAG_PLAN_LOG): per layer a ring of log_cap records
+  pe::PlanLogLayout pl{};
+  int log_cap = 0;
+  int32_t* plan_log = nullptr;         // device: [L][log_cap][pl.total]
+  uint32_t* log_seq = nullptr;         // device: [L] steps logged per layer
   unsigned long long host_counts[pe::ST_COUNT] = {};
   // Second stream (default priority): runs the experts that were already
   // resident while the page-in is in flight; forked and joined with events.
@@ -146,7 +155,7 @@ void free_ctx(pe_ctx* c) {
   if (c->st_ids) (void)hipHostFree(c->st_ids);
   if (c->st_blk) (void)hipHostFree(c->st_blk);
   for (void* p : {(void*)c->slots, (void*)c->blocks, (void*)c->h, (void*)c->merged,
-                  (void*)c->stats})
+                  (void*)c->stats, (void*)c->plan_log, (void*)c->log_seq})
     if (p) (void)hipFree(p);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
@@ -162,7 +171,14 @@ int use_device(const pe_ctx* c) {
   return PE_OK;
 }
 
-pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const float* w, int part = 0) {
+// Where a step's activations go.
+struct Act {
+  uint16_t* h;
+  float* merged;
+};
+
+pe::ExpertArgs expert_args(pe_ctx* c, const Act& act, int layer, int wave, const void* x, const float* w,
+                           int part = 0) {
   pe::ExpertArgs a{};
   a.part = part;
   a.slots = c->slots + (size_t)layer * c->d.K * c->b.stride;
@@ -174,8 +190,8 @@ pe::ExpertArgs expert_args(pe_ctx* c, int layer, int wave, const void* x, const 
   a.wave = wave;
   a.x = static_cast<const uint16_t*>(x);
   a.topk_w = w;
-  a.h = c->h;
-  a.merged = c->merged;
+  a.h = act.h;
+  a.merged = act.merged;
   a.H = c->d.H; a.I = c->d.I; a.k = c->d.k;
   a.lean = 0;
   a.mfma_min = c->mfma_min;
@@ -211,14 +227,14 @@ int drain_timing(pe_ctx* c, bool wait) {
   return PE_OK;
 }
 
-// Brackets one stage's launches with events when timing is on.
+// Brackets one stage's launches with events when timing is on (and `on`).
 struct StageTimer {
   pe_ctx* c;
   int stage;
   hipStream_t s;
   hipEvent_t a = nullptr;
-  StageTimer(pe_ctx* c_, int stage_, hipStream_t s_) : c(c_), stage(stage_), s(s_) {
-    if (!c->timing) return;
+  StageTimer(pe_ctx* c_, int stage_, hipStream_t s_, bool on = true) : c(c_), stage(stage_), s(s_) {
+    if (!c->timing || !on) return;
     a = take_event(c);
     if (a && hipEventRecord(a, s) != hipSuccess) a = nullptr;
   }
@@ -235,26 +251,33 @@ struct StageTimer {
 // Expert kernels (gate/up then down; GEMV items, then MFMA tiles) of one part
 // of one wave.  `items`/`tiles` bound the launches' grids; `max_m` bounds the
 // GEMV experts' token counts.
-void run_experts(pe_ctx* c, int layer, int wave, int part, const void* x, const float* w, int items, int max_m,
-                 int tiles, hipStream_t s) {
-  pe::ExpertArgs a = expert_args(c, layer, wave, x, w, part);
+void run_experts(pe_ctx* c, const Act& act, bool tm_on, int layer, int wave, int part, const void* x,
+                 const float* w, int items, int max_m, int tiles, hipStream_t s) {
+  pe::ExpertArgs a = expert_args(c, act, layer, wave, x, w, part);
   if (items > 0) {
     {
-      StageTimer tm(c, PE_STAGE_GATE_UP, s);
+      StageTimer tm(c, PE_STAGE_GATE_UP, s, tm_on);
       pe::launch_gemv_gate_up(c->cfg.wtype, a, items, max_m, s);
     }
-    StageTimer tm(c, PE_STAGE_DOWN, s);
+    StageTimer tm(c, PE_STAGE_DOWN, s, tm_on);
     pe::launch_gemv_down(c->cfg.wtype, a, items, max_m, s);
   }
   if (tiles > 0) {
     {
-      StageTimer tm(c, PE_STAGE_GATE_UP, s);
+      StageTimer tm(c, PE_STAGE_GATE_UP, s, tm_on);
       pe::launch_mfma_gate_up(c->cfg.wtype, a, tiles, s);
     }
-    StageTimer tm(c, PE_STAGE_DOWN, s);
+    StageTimer tm(c, PE_STAGE_DOWN, s, tm_on);
     pe::launch_mfma_down(c->cfg.wtype, a, tiles, s);
   }
 }
+
+// The LDS a one-wave down projection + top-k sum launch (launch_down_sum) takes
+// for n routed entries at most (row blocks of up to 16 rows: per entry 16 fp32
+// results plus its id, sorted position and router weight).  Steps whose
+// launch would need more than one workgroup may take run the down kernel into
+// the merged buffer and the separate top-k sum instead: the same arithmetic.
+bool down_sum_fits(int n) { return (size_t)n * 76 + 64 <= 64 * 1024; }
 
 }  // namespace
 
@@ -335,8 +358,11 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   if (g.wtype < PE_W_BF16 || g.wtype > PE_W_MXFP4_B32)
     return fail(PE_ERR_INVALID_ARG, "unknown weight type %d", g.wtype);
   if (int rc = check_multiples(g.wtype, g.hidden, g.inter)) return rc;
-  if (g.flags & ~(PE_FLAG_PAGEIN_DMA | PE_FLAG_FORCE_HOST_PLAN | PE_FLAG_UNPAGED))
+  if (g.flags & ~(PE_FLAG_PAGEIN_DMA | PE_FLAG_FORCE_HOST_PLAN | PE_FLAG_UNPAGED | PE_FLAG_PLAN_LOG))
     return fail(PE_ERR_INVALID_ARG, "unknown flags 0x%x", g.flags);
+  const bool plan_log = (g.flags & PE_FLAG_PLAN_LOG) != 0;
+  if (plan_log && (g.plan_log_steps < 1 || g.plan_log_steps > (1 << 24)))
+    return fail(PE_ERR_INVALID_ARG, "PE_FLAG_PLAN_LOG needs plan_log_steps in [1, 2^24]");
   if ((long long)g.max_tokens * g.top_k > (1 << 24))
     return fail(PE_ERR_UNSUPPORTED, "max_tokens * top_k too large");
   int ndev = 0;
@@ -355,8 +381,9 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   blob_layout(g.wtype, g.hidden, g.inter, &c->b);
   // The MFMA kernels stage K in blocks of 128 and tile weight rows by 64.
   c->mfma_min = (g.hidden % 128 == 0 && g.inter % 128 == 0) ? pe::kMfmaMinTokens : pe::kNoMfma;
-  if (const char* v = getenv("PE_STREAM_WGS")) c->stream_wgs = std::max(1, atoi(v));
   c->d.mfma_min = c->mfma_min;
+  c->pl = pe::make_plan_log_layout(c->d, c->ll);
+  c->log_cap = plan_log ? g.plan_log_steps : 0;
   c->sum = new pe::HostPlanSummary;
   int rc = use_device(c);
   if (rc) { free_ctx(c); return rc; }
@@ -383,8 +410,11 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
       {reinterpret_cast<void**>(&c->h), (size_t)d.max_entries * d.I * 2},
       {reinterpret_cast<void**>(&c->merged), (size_t)d.max_entries * d.H * 4},
       {reinterpret_cast<void**>(&c->stats), pe::ST_COUNT * 8},
+      {reinterpret_cast<void**>(&c->plan_log), (size_t)d.L * c->log_cap * c->pl.total * 4},
+      {reinterpret_cast<void**>(&c->log_seq), (size_t)d.L * 4},
   };
   for (auto& a : dev) {
+    if (a.bytes == 0) continue;
     if (hipMalloc(a.p, a.bytes) != hipSuccess) {
       *a.p = nullptr;
       (void)hipGetLastError();
@@ -395,15 +425,28 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   struct { int32_t** p; size_t words; } pin[] = {
       {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, (size_t)d.L * c->layer_words}};
   for (auto& a : pin) {
-    if (hipHostMalloc(reinterpret_cast<void**>(a.p), a.words * 4, hipHostMallocDefault) != hipSuccess) {
+    if (hipHostMalloc(reinterpret_cast<void**>(a.p), a.words * 4, hipHostMallocMapped | hipHostMallocCoherent) !=
+        hipSuccess) {
       *a.p = nullptr;
       (void)hipGetLastError();
       free_ctx(c);
       return fail(PE_ERR_OOM_HOST_PIN, "cannot pin staging buffers");
     }
   }
+  {
+    void* a = nullptr;
+    void* b = nullptr;
+    if (hipHostGetDevicePointer(&a, c->st_ids, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&b, c->st_blk, 0) != hipSuccess) {
+      free_ctx(c);
+      return fail(PE_ERR_HIP, "hipHostGetDevicePointer failed for the staging buffers");
+    }
+    c->st_ids_dev = static_cast<int32_t*>(a);
+    c->st_blk_dev = static_cast<int32_t*>(b);
+  }
   if (hipMemset(c->stats, 0, pe::ST_COUNT * 8) != hipSuccess ||
-      hipMemset(c->blocks, 0, (size_t)d.L * c->layer_words * 4) != hipSuccess) {
+      hipMemset(c->blocks, 0, (size_t)d.L * c->layer_words * 4) != hipSuccess ||
+      (c->log_seq && hipMemset(c->log_seq, 0, (size_t)d.L * 4) != hipSuccess)) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "initialising device buffers failed");
   }
@@ -413,12 +456,12 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "creating the side stream and its events failed");
   }
-  c->mirror_ok.assign(d.L, 0);
   pe::launch_reset_lru(c->blocks, c->layer_words, 0, d.L, c->o, d.E, d.K, unpaged, nullptr);
   if (hipDeviceSynchronize() != hipSuccess) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "resetting the LRU state failed: %s", hipGetErrorString(hipGetLastError()));
   }
+
   *out = c;
   return PE_OK;
 }
@@ -467,22 +510,26 @@ int pe_reset_lru(pe_ctx* c, int layer, void* stream) {
   int rc = use_device(c);
   if (rc) return rc;
   const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->d.L : layer + 1;
-  for (int l = l0; l < l1; ++l) c->mirror_ok[l] = 0;
   pe::launch_reset_lru(c->blocks, c->layer_words, l0, l1, c->o, c->d.E, c->d.K, c->unpaged,
                        static_cast<hipStream_t>(stream));
   PE_HIP(hipGetLastError());
   return PE_OK;
 }
 
-int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, const float* topk_w, int T,
-               void* out, void* stream) {
-  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
-  if (layer < 0 || layer >= c->d.L) return fail(PE_ERR_INVALID_ARG, "layer %d out of range", layer);
-  if (T < 0 || T > c->d.max_tokens) return fail(PE_ERR_INVALID_ARG, "T=%d outside [0, %d]", T, c->d.max_tokens);
-  if (T == 0) return PE_OK;
-  if (!x || !topk_ids || !topk_w || !out) return fail(PE_ERR_INVALID_ARG, "NULL tensor pointer");
-  int rc = use_device(c);
-  if (rc) return rc;
+namespace {
+
+// Append the record of the step that just ended to the layer's plan log.
+void log_step(pe_ctx* c, const int32_t* blk, int layer, int T, hipStream_t s) {
+  if (!c->log_cap) return;
+  pe::launch_plan_log(blk, c->o, c->d.K, (int)c->ll.n_waves, (int)c->pl.plan_words, T,
+                      c->plan_log + (size_t)layer * c->log_cap * c->pl.total, c->log_cap, (int)c->pl.total,
+                      c->log_seq + layer, s);
+}
+
+// One forward step of one layer (pe_forward and pe_forward_static): `act` holds
+// the step's activation buffers; the stage timers record events only if `tm_on`.
+int forward_impl(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, const float* topk_w, int T,
+                 void* out, void* stream, const Act& act, bool tm_on) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const pe::Dims& d = c->d;
   const int n = T * d.k;
@@ -499,7 +546,6 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   const int mfma_min = T >= c->mfma_min ? c->mfma_min : pe::kNoMfma;
 
   if (device_plan) {
-    c->mirror_ok[layer] = 0;     // the device updates this layer's LRU state
     // One wave, on the caller's stream only (a second stream would put graph
     // branches on other hardware queues, whose cross-queue dependencies cost more
     // than they hide).  No host synchronisation: capturable.
@@ -512,7 +558,7 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       // projection of the experts already resident.  Launch B: every expert's
       // down projection and the fixed-order top-k sum, which also makes the new
       // state copy current.
-      pe::ExpertArgs a = expert_args(c, layer, 0, x, topk_w, 1);
+      pe::ExpertArgs a = expert_args(c, act, layer, 0, x, topk_w, 1);
       a.lean = 1;
       a.ids = topk_ids;
       a.T = T;
@@ -520,18 +566,19 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       a.blk = blk;
       a.mfma_min = mfma_min;
       {
-        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+        StageTimer tm(c, PE_STAGE_PAGE_IN, s, tm_on);
         pe::launch_step_a(c->cfg.wtype, blk, topk_ids, n, d, c->o, mfma_min, work_l, c->stats, host_l,
-                          slots_l, c->b.stride, c->b.copied, c->stream_wgs, a, items, T, s);
+                          slots_l, c->b.stride, c->b.copied, kStreamWgs, a, items, T, s);
       }
-      pe::ExpertArgs all = expert_args(c, layer, 0, x, topk_w, 0);
+      pe::ExpertArgs all = expert_args(c, act, layer, 0, x, topk_w, 0);
       all.ids = topk_ids;
       all.T = T;
       all.E = d.E;
       {
-        StageTimer tm(c, PE_STAGE_DOWN, s);
+        StageTimer tm(c, PE_STAGE_DOWN, s, tm_on);
         pe::launch_down_sum(c->cfg.wtype, all, T, static_cast<uint16_t*>(out), blk + c->ll.cur, s);
       }
+      log_step(c, blk, layer, T, s);
       PE_HIP(hipGetLastError());
       return PE_OK;
     }
@@ -540,16 +587,17 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
     // Surplus MFMA workgroups exit on the device tile count.
     const int tiles = mfma_min != pe::kNoMfma ? pe::ceil_div(n, pe::kTileM) + items : 0;
     {
-      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+      StageTimer tm(c, PE_STAGE_PAGE_IN, s, tm_on);
       pe::launch_plan_page_in(blk, topk_ids, n, d, c->o, mfma_min, work_l, c->stats, host_l, slots_l,
                               c->b.stride, c->b.copied, !c->unpaged, kPageInGrid, s);
     }
-    run_experts(c, layer, 0, 0, x, topk_w, items, T, tiles, s);
+    run_experts(c, act, tm_on, layer, 0, 0, x, topk_w, items, T, tiles, s);
     {
-      StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
-      pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out),
+      StageTimer tm(c, PE_STAGE_TOPK_SUM, s, tm_on);
+      pe::launch_topk_sum(act.merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out),
                           blk + c->ll.cur, s);
     }
+    log_step(c, blk, layer, T, s);
     PE_HIP(hipGetLastError());
     return PE_OK;
   }
@@ -559,25 +607,27 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   if (cap != hipStreamCaptureStatusNone)
     return fail(PE_ERR_NOT_CAPTURABLE, "T*top_k=%d > K=%d needs host planning, which cannot be captured", n, d.K);
 
-  // Host-planned step: read the ids back, and the layer's LRU state unless the
-  // host's mirror of it is current (a host-planned step was the last to change
-  // it); that is the one synchronisation.  Plan every wave on the host, upload
-  // the block (state, plans, slot map) and the work lists, then run the waves in
-  // order.
+  // Host-planned step.  One launch writes the routed ids and the layer's LRU
+  // state (both state copies and the current-copy index, whoever changed them
+  // last: a device-planned step, a replayed graph or a reset) into page-locked
+  // host memory; that is the one synchronisation.  The host plans every wave in
+  // its mirror of the block, one launch reads the block (state, plans, slot map)
+  // and the work lists back into device memory, and the waves run in order.
   int32_t* mirror = c->st_blk + (size_t)layer * c->layer_words;
-  PE_HIP(hipMemcpyAsync(c->st_ids, topk_ids, (size_t)n * 4, hipMemcpyDeviceToHost, s));
-  if (!c->mirror_ok[layer])
-    PE_HIP(hipMemcpyAsync(mirror, blk, c->ll.state_prefix * 4, hipMemcpyDeviceToHost, s));
+  int32_t* mirror_dev = c->st_blk_dev + (size_t)layer * c->layer_words;
+  pe::launch_gather_state(blk, (int)c->ll.state_prefix, topk_ids, n, mirror_dev, c->st_ids_dev, s);
+  PE_HIP(hipGetLastError());
   PE_HIP(hipStreamSynchronize(s));
-  c->mirror_ok[layer] = 0;
   pe::HostPlanSummary& sm = *c->sum;
   pe::Dims dp = d;
   dp.mfma_min = mfma_min;
   if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, mirror, mirror + c->ll.total, &sm) != 0)
     return fail(PE_ERR_INVALID_ARG, "step needs more waves than the context holds");
-  // the block (state, plans, slot map) and the work lists that follow it, in one copy
-  PE_HIP(hipMemcpyAsync(blk, mirror, (c->ll.total + c->wl.entries + n) * 4, hipMemcpyHostToDevice, s));
-  c->mirror_ok[layer] = 1;
+  {
+    const size_t bytes = align_up((c->ll.total + c->wl.entries + (size_t)n) * 4, 16);
+    const int grid = (int)std::min<size_t>(16, std::max<size_t>(1, bytes / 8192));
+    pe::launch_copy(blk, mirror_dev, bytes, grid, s);
+  }
   const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
   bool summed = false;     // the top-k sum already ran with the last down projection
   for (int w = 0; w < sm.n_waves; ++w) {
@@ -588,15 +638,15 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       // GEMV experts only: one launch pages in the missing experts with their
       // gate/up projection fused in while the resident ones run theirs, then
       // one launch runs the wave's down projection.
-      pe::ExpertArgs a = expert_args(c, layer, w, x, topk_w, 1);
+      pe::ExpertArgs a = expert_args(c, act, layer, w, x, topk_w, 1);
       {
-        StageTimer tm(c, PE_STAGE_PAGE_IN, s);
-        pe::launch_wave_a(c->cfg.wtype, a, g_hit, sm.max_gemv_tokens, c->stream_wgs, host_l, c->b.stride,
+        StageTimer tm(c, PE_STAGE_PAGE_IN, s, tm_on);
+        pe::launch_wave_a(c->cfg.wtype, a, g_hit, sm.max_gemv_tokens, kStreamWgs, host_l, c->b.stride,
                           c->b.copied, s);
       }
       a.part = 0;
-      StageTimer tm(c, PE_STAGE_DOWN, s);
-      if (sm.n_waves == 1 && mfma_min == pe::kNoMfma) {
+      StageTimer tm(c, PE_STAGE_DOWN, s, tm_on);
+      if (sm.n_waves == 1 && mfma_min == pe::kNoMfma && down_sum_fits(n)) {
         // one wave of few tokens: its down projection and the top-k sum in one
         // launch, as in a device-planned step (the same arithmetic as the
         // down kernel followed by the sum over the merged buffer)
@@ -614,11 +664,11 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
     if (fork) {
       PE_HIP(hipEventRecord(c->ev_fork, s));
       PE_HIP(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-      run_experts(c, layer, w, 1, x, topk_w, g_hit, sm.max_gemv_tokens, t_hit, c->side);
+      run_experts(c, act, tm_on, layer, w, 1, x, topk_w, g_hit, sm.max_gemv_tokens, t_hit, c->side);
       PE_HIP(hipEventRecord(c->ev_join, c->side));
     }
     if (!c->unpaged && cnt > 0) {
-      StageTimer tm(c, PE_STAGE_PAGE_IN, s);
+      StageTimer tm(c, PE_STAGE_PAGE_IN, s, tm_on);
       if (dma) {
         const int32_t* pe_ = mirror + c->ll.plan_expert + (size_t)w * d.K;
         const int32_t* ps_ = mirror + c->ll.plan_slot + (size_t)w * d.K;
@@ -631,16 +681,17 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
       }
     }
     if (fork) {
-      run_experts(c, layer, w, 2, x, topk_w, g_all - g_hit, sm.max_gemv_tokens, t_all - t_hit, s);
+      run_experts(c, act, tm_on, layer, w, 2, x, topk_w, g_all - g_hit, sm.max_gemv_tokens, t_all - t_hit, s);
       PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));    // before the next wave may evict these slots
     } else {
-      run_experts(c, layer, w, 0, x, topk_w, g_all, sm.max_gemv_tokens, t_all, s);
+      run_experts(c, act, tm_on, layer, w, 0, x, topk_w, g_all, sm.max_gemv_tokens, t_all, s);
     }
   }
   if (!summed) {
-    StageTimer tm(c, PE_STAGE_TOPK_SUM, s);
-    pe::launch_topk_sum(c->merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), nullptr, s);
+    StageTimer tm(c, PE_STAGE_TOPK_SUM, s, tm_on);
+    pe::launch_topk_sum(act.merged, topk_ids, T, d.k, d.E, d.H, static_cast<uint16_t*>(out), nullptr, s);
   }
+  log_step(c, blk, layer, T, s);
   PE_HIP(hipGetLastError());
   c->host_counts[pe::ST_STEPS] += 1;
   c->host_counts[pe::ST_HOST_PLANNED] += 1;
@@ -651,6 +702,27 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   c->host_counts[pe::ST_BAD_IDS] += sm.bad_ids;
   return PE_OK;
 }
+
+// Argument checks shared by pe_forward and pe_forward_static; 1 if T = 0 (no-op).
+int check_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, const float* topk_w, int T,
+                  void* out) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (layer < 0 || layer >= c->d.L) return fail(PE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (T < 0 || T > c->d.max_tokens) return fail(PE_ERR_INVALID_ARG, "T=%d outside [0, %d]", T, c->d.max_tokens);
+  if (T == 0) return 1;
+  if (!x || !topk_ids || !topk_w || !out) return fail(PE_ERR_INVALID_ARG, "NULL tensor pointer");
+  return use_device(c);
+}
+
+}  // namespace
+
+int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, const float* topk_w, int T,
+               void* out, void* stream) {
+  const int rc = check_forward(c, layer, x, topk_ids, topk_w, T, out);
+  if (rc) return rc < 0 ? rc : PE_OK;
+  return forward_impl(c, layer, x, topk_ids, topk_w, T, out, stream, Act{c->h, c->merged}, true);
+}
+
 
 int pe_max_captured_batch(const pe_ctx* c) {
   if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
@@ -706,6 +778,38 @@ int pe_get_slot_map(pe_ctx* c, int layer, int32_t* slot_of, int T, void* stream)
   PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   PE_HIP(hipMemcpy(slot_of, c->blocks + (size_t)layer * c->layer_words + c->ll.slot_of, (size_t)T * c->d.k * 4,
                    hipMemcpyDeviceToHost));
+  return PE_OK;
+}
+
+int pe_plan_log_record_words(const pe_ctx* c) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  return (int)c->pl.total;
+}
+
+int pe_get_plan_log(pe_ctx* c, int layer, int32_t* records, int max_records, int* n_records, void* stream) {
+  if (!c || !records || !n_records) return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  if (!c->log_cap) return fail(PE_ERR_INVALID_ARG, "the context keeps no plan log (create it with PE_FLAG_PLAN_LOG)");
+  if (layer < 0 || layer >= c->d.L || max_records < 0)
+    return fail(PE_ERR_INVALID_ARG, "layer %d / max_records %d out of range", layer, max_records);
+  int rc = use_device(c);
+  if (rc) return rc;
+  PE_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  uint32_t seq = 0;
+  PE_HIP(hipMemcpy(&seq, c->log_seq + layer, 4, hipMemcpyDeviceToHost));
+  const uint32_t cap = (uint32_t)c->log_cap;
+  const uint32_t n = std::min(std::min(seq, cap), (uint32_t)max_records);
+  const size_t rw = c->pl.total;
+  const int32_t* ring = c->plan_log + (size_t)layer * cap * rw;
+  // records seq - n .. seq - 1 sit at ring positions (seq - n + i) % cap: at most two runs
+  uint32_t done = 0;
+  while (done < n) {
+    const uint32_t pos = (seq - n + done) % cap;
+    const uint32_t run = std::min(n - done, cap - pos);
+    PE_HIP(hipMemcpy(records + (size_t)done * rw, ring + (size_t)pos * rw, (size_t)run * rw * 4,
+                     hipMemcpyDeviceToHost));
+    done += run;
+  }
+  *n_records = (int)n;
   return PE_OK;
 }
 

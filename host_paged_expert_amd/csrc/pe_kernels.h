@@ -104,4 +104,18 @@ void launch_topk_sum(const float* merged, const int32_t* ids, int T, int k, int 
 void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const Offsets& o,
                       int E, int K, bool identity, hipStream_t s);
 
+// Host-planned step, before the host plans: copy the layer block's first
+// `state_words` words (current-copy index and both LRU-state copies) to
+// `host_blk` and the n routed ids to `host_ids`, both page-locked host memory
+// written through its mapped device address (one launch, no copy engine).
+void launch_gather_state(const int32_t* blk, int state_words, const int32_t* ids, int n, int32_t* host_blk,
+                         int32_t* host_ids, hipStream_t s);
+
+// Append one record (PlanLogLayout) of the step that just ended to the layer's
+// plan-log ring: `ring` holds `cap` records of `rec_words` words; *seq counts
+// the layer's logged steps and is advanced.  Reads the layer block's plan area
+// (`plan_words` words from word `plan0`) and its current LRU-state copy.
+void launch_plan_log(const int32_t* blk, const Offsets& o, int K, int plan0, int plan_words, int T,
+                     int32_t* ring, int cap, int rec_words, uint32_t* seq, hipStream_t s);
+
 }  // namespace pe

@@ -2284,4 +2284,53 @@ void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const
   reset_lru_kernel<<<l1 - l0, 256, 0, s>>>(blocks, layer_words, l0, o, E, K, identity ? 1 : 0);
 }
 
+// ------------------------------------------------------------------ host-planned step: read-back
+
+__global__ __launch_bounds__(256) void gather_state_kernel(const int32_t* __restrict__ blk, int state_words,
+                                                           const int32_t* __restrict__ ids, int n,
+                                                           int32_t* __restrict__ host_blk,
+                                                           int32_t* __restrict__ host_ids) {
+  for (int i = threadIdx.x; i < state_words; i += blockDim.x) host_blk[i] = blk[i];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) host_ids[i] = ids[i];
+}
+
+void launch_gather_state(const int32_t* blk, int state_words, const int32_t* ids, int n, int32_t* host_blk,
+                         int32_t* host_ids, hipStream_t s) {
+  gather_state_kernel<<<1, 256, 0, s>>>(blk, state_words, ids, n, host_blk, host_ids);
+}
+
+// ------------------------------------------------------------------ plan log
+
+// One workgroup: the record of the step that just ended goes to ring slot
+// seq % cap.  Runs after every kernel of the step, so the block's current
+// state copy is the state after the step.
+__global__ __launch_bounds__(256) void plan_log_kernel(const int32_t* __restrict__ blk, Offsets o, int K,
+                                                       int plan0, int plan_words, int T,
+                                                       int32_t* __restrict__ ring, int cap, int rec_words,
+                                                       uint32_t* __restrict__ seq) {
+  const uint32_t q = *seq;
+  int32_t* rec = ring + (size_t)(q % (uint32_t)cap) * rec_words;
+  const int32_t* st = blk + o.state0 + (blk[o.cur] & 1) * o.state_stride;
+  const int p_se = 4 + plan_words, p_lu = p_se + K;
+  if (threadIdx.x == 0) {
+    rec[0] = (int32_t)q;
+    rec[1] = T;
+    rec[2] = st[o.tick];
+    rec[3] = 0;
+  }
+  for (int i = threadIdx.x; i < plan_words; i += blockDim.x) rec[4 + i] = blk[plan0 + i];
+  for (int j = threadIdx.x; j < K; j += blockDim.x) {
+    rec[p_se + j] = st[o.slot_expert + j];
+    rec[p_lu + j] = st[o.last_use + j];
+  }
+  for (int i = p_lu + K + threadIdx.x; i < rec_words; i += blockDim.x) rec[i] = 0;
+  __syncthreads();     // every thread has read *seq
+  if (threadIdx.x == 0) *seq = q + 1;
+}
+
+void launch_plan_log(const int32_t* blk, const Offsets& o, int K, int plan0, int plan_words, int T,
+                     int32_t* ring, int cap, int rec_words, uint32_t* seq, hipStream_t s) {
+  plan_log_kernel<<<1, 256, 0, s>>>(blk, o, K, plan0, plan_words, T, ring, cap, rec_words, seq);
+}
+
 }  // namespace pe

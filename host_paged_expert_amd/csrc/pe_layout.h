@@ -93,6 +93,35 @@ inline LayerLayout make_layer_layout(const Dims& d) {
   return l;
 }
 
+// One plan-log record (int32 words): what one step of one layer decided.
+//   [0] seq        the layer's step number since the context was created (from 0)
+//   [1] T          tokens of the step
+//   [2] tick       the layer's tick after the step
+//   [3] 0
+//   [4 ...]        the block's plan area as the step left it, word for word:
+//                  n_waves, count[MW], experts[MW*K], slots[MW*K], evicted[MW*K]
+//                  (wave-major, entries r < count[w] valid), slot_of[max_entries]
+//                  (first T*k valid)
+//   then           slot_expert[K] and last_use[K] after the step
+// padded to a multiple of 16 words.
+struct PlanLogLayout {
+  size_t plan;          // first word of the copied plan area
+  size_t plan_words;    // words of the plan area (ll.slot_of + max_entries - ll.n_waves)
+  size_t slot_expert;   // [K]
+  size_t last_use;      // [K]
+  size_t total;         // words per record
+};
+
+inline PlanLogLayout make_plan_log_layout(const Dims& d, const LayerLayout& ll) {
+  PlanLogLayout p{};
+  p.plan = 4;
+  p.plan_words = ll.slot_of + (size_t)d.max_entries - ll.n_waves;
+  p.slot_expert = p.plan + p.plan_words;
+  p.last_use = p.slot_expert + (size_t)d.K;
+  p.total = (p.last_use + (size_t)d.K + 15) / 16 * 16;
+  return p;
+}
+
 // Step work arena (int32 words), shared by all layers (steps run in stream order).
 // "Used" experts are those with at least one valid entry; they are numbered u in
 // wave order and, inside a wave, by ascending expert id.  Entries of used expert

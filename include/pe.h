@@ -1,18 +1,19 @@
 /*
  * pe.h — paged-expert MoE layer for one AMD Instinct MI355X (gfx950).
  *
- * The method (SGLang "Paged Experts" documentation page, sections "The K-slot
- * table and the host store", "A step: waves, page-in, merge", "Captured
- * decode"): each MoE layer keeps K of its E routed experts in a K-slot table
- * in GPU memory and all E experts in page-locked host memory.  Each forward
- * step of a layer splits the distinct routed experts into waves of at most K
- * (already-resident experts first), makes each wave resident by evicting the
- * least recently used experts outside the wave and copying in the missing
- * ones, runs the SwiGLU expert FFN over the wave's own entries (each
- * (token, expert) output scaled by the entry's router weight, no top-k sum
- * yet), keeps every entry once (per block of output rows in LDS on a
- * device-planned step, in a merged buffer on a host-planned one), and finally
- * applies one fixed-order top-k sum.  The output equals the unpaged layer's.
+ * What is computed (SGLang "Paged Experts" documentation page, sections "The
+ * K-slot table and the host store", "A step: waves, page-in, merge", steps
+ * 1-4, and "Captured decode"): every expert of every MoE layer lives in a
+ * page-locked host store, and only K of a layer's E experts occupy its GPU
+ * slot table at a time.  A forward step gathers the experts its tokens route
+ * to, processes them in groups of at most K (those already in a slot go
+ * first), and before each group runs, fills the group's missing experts into
+ * slots whose occupants the group does not use, oldest use first.  The
+ * SwiGLU FFN then runs per (token, expert) entry, scaled by the entry's
+ * router weight; the entries are kept apart (per block of output rows in LDS
+ * on a device-planned step, in a merged buffer on a host-planned one) until
+ * one top-k sum in a fixed order makes each token's output.  That output is
+ * the unpaged layer's.
  *
  * Conventions for every entry point:
  *   - Return 0 (PE_OK) on success or a negative PE_ERR_* code; no exception
@@ -61,6 +62,9 @@ extern "C" {
 #define PE_FLAG_FORCE_HOST_PLAN 2u  /* plan every step on the host                */
 #define PE_FLAG_UNPAGED         4u  /* reference mode: K = E, slot e holds expert e
                                        for good, no host store, no paging         */
+#define PE_FLAG_PLAN_LOG        8u  /* keep a per-layer device ring of every step's
+                                       plan (see pe_get_plan_log); needs
+                                       plan_log_steps >= 1                        */
 
 typedef struct pe_ctx pe_ctx;
 
@@ -77,6 +81,8 @@ typedef struct {
   int device;         /* HIP device ordinal                                  */
   int wtype;          /* PE_W_*                                              */
   unsigned flags;     /* PE_FLAG_*                                           */
+  int plan_log_steps; /* records per layer in the plan log (PE_FLAG_PLAN_LOG
+                         only; ignored otherwise)                            */
 } pe_config;
 
 /* Counters since creation (or the last pe_reset_stats). */
@@ -95,18 +101,20 @@ typedef struct {
 /* Create a context: validates the configuration (K >= top_k as the docs'
  * "Usage" section requires, K <= E, format-dependent divisibility), allocates
  * the page-locked mapped host store (L*E expert blobs; hipHostMalloc with
- * hipHostMallocMapped), the device slot tables (L*K blobs), the per-layer LRU
- * state (reset to empty), plan buffers and scratch sized by max_tokens.  On
- * failure nothing is leaked and *out is NULL. */
+ * hipHostMallocMapped; docs, "The K-slot table and the host store"), the
+ * device slot tables (L*K blobs), the per-layer LRU state (reset to empty),
+ * plan buffers, the plan log if asked for, and scratch sized by max_tokens.
+ * On failure nothing is leaked and *out is NULL. */
 int pe_create(const pe_config* cfg, pe_ctx** out);
 
 /* Free everything pe_create allocated.  The caller must make sure no work
  * enqueued on the context is still running.  NULL is ignored. */
 void pe_destroy(pe_ctx* ctx);
 
-/* Write one expert's weights into its host-store row (docs page: the weight
- * loader writes a one-row view of the host store; host rows have the layout
- * the GPU slots have).  All pointers are host memory, row-major:
+/* Write one expert's weights into its host-store row (docs page, "The K-slot
+ * table and the host store": the weight loader writes a one-row view of the
+ * host store, and host rows have the layout the GPU slots have).  All
+ * pointers are host memory, row-major:
  *   PE_W_BF16:      w13 bf16 [2I, H] (gate rows 0..I-1, up rows I..2I-1),
  *                   w2 bf16 [H, I]; s13 = s2 = NULL.
  *   PE_W_FP8_B128:  w13 u8 e4m3fn [2I, H], w2 u8 [H, I], s13 fp32
@@ -116,6 +124,12 @@ void pe_destroy(pe_ctx* ctx);
  *                   [H, I/128]; weight = (nibble - 8) * s.
  *   PE_W_INT8_G128: w13 u8 [2I, H], w2 u8 [H, I], s13 fp16 [2I, H/128],
  *                   s2 fp16 [H, I/128]; weight = (byte - 128) * s.
+ *   PE_W_MXFP4_B32: w13 u8 [2I, H/2], w2 u8 [H, I/2] (OCP E2M1 codes, element
+ *                   2c the low nibble of byte c), s13 u8 [2I, H/32], s2 u8
+ *                   [H, I/32] (OCP E8M0 scale bytes, one per row and 32
+ *                   inputs); weight = e2m1(code) * 2^(scale - 127).
+ * The blob holds W13 | W2 | S13 | S2 in this order, each part starting on a
+ * 256-byte boundary; pe_expert_bytes gives its size.
  * The data is copied; the caller keeps ownership.  With PE_FLAG_UNPAGED the
  * blob goes straight to device slot `expert` (synchronous copy).  An expert
  * that is resident when it is reloaded keeps its old slot contents until it
@@ -133,18 +147,25 @@ int pe_load_expert(pe_ctx* ctx, int layer, int expert,
  * If T*k <= K (and PE_FLAG_FORCE_HOST_PLAN is off) the step is one wave
  * planned on the device with no host synchronisation ("Captured decode" on
  * the docs page), so the call may be captured into a hipGraph.  Otherwise
- * the host reads the ids back, and the layer's LRU state unless a host-planned
- * step was the last to change it (one stream synchronisation), plans the
- * waves and enqueues them; under stream capture that path returns
- * PE_ERR_NOT_CAPTURABLE without enqueuing anything.
+ * one launch writes the ids and the layer's LRU state into page-locked host
+ * memory, the stream is synchronised once, the host plans the waves ("A
+ * step: waves, page-in, merge", steps 1-2) and enqueues them; under stream
+ * capture that path returns PE_ERR_NOT_CAPTURABLE without enqueuing
+ * anything.  Both paths read and update one LRU state per layer, whatever
+ * changed it last (an eager step, a replayed graph, a reset).
  * Entries whose id is outside [0, E) contribute 0 and are counted in
  * pe_stats.bad_ids. */
 int pe_forward(pe_ctx* ctx, int layer, const void* x, const int32_t* topk_ids,
                const float* topk_w, int T, void* out, void* stream);
 
 /* Empty the slot table of `layer` (-1: every layer): no expert resident,
- * every slot's last use 0, tick 1.  With PE_FLAG_UNPAGED the identity map is
- * restored instead.  Enqueued on `stream`. */
+ * every slot's last use 0, tick 1 -- the state of a fresh table, which the
+ * pages leave unspecified (read here as empty, with no expert preloaded).
+ * Used to start a measurement window cold and after reloading experts.
+ * With PE_FLAG_UNPAGED the identity map is restored instead.  Enqueued on
+ * `stream`; device-planned and host-planned steps both see the reset (they
+ * share one LRU state per layer, docs "Captured decode").  The plan log is
+ * not cleared. */
 int pe_reset_lru(pe_ctx* ctx, int layer, void* stream);
 
 /* ---- sizes and introspection (host calls) ------------------------------ */
@@ -169,24 +190,51 @@ int pe_max_captured_batch(const pe_ctx* ctx);
 /* Most waves one step can need: ceil(min(max_tokens*k, E) / K). */
 int pe_max_waves(const pe_ctx* ctx);
 
-/* Copy the LRU state of `layer` to host arrays (slot_expert [K] int32, -1 =
- * empty; last_use [K]; *tick).  Synchronises `stream`.  Any pointer may be
- * NULL. */
+/* Copy the LRU state of `layer` (docs, "A step: waves, page-in, merge", step
+ * 2, read as: the expert in each slot, the tick of the wave that last used
+ * each slot, and the layer's next tick) to host arrays (slot_expert [K]
+ * int32, -1 = empty; last_use [K]; *tick).  Synchronises `stream`.  Any
+ * pointer may be NULL. */
 int pe_get_lru_state(pe_ctx* ctx, int layer, int32_t* slot_expert, uint32_t* last_use,
                      uint32_t* tick, void* stream);
 
-/* The plan of wave `wave` of the most recent step of `layer`: *count page-ins,
- * experts[r] copied into slots[r] evicting evicted[r] (-1 = slot was empty),
- * r < *count (arrays of K entries), and *n_waves of that step.  Synchronises
- * `stream`.  Pointers may be NULL. */
+/* The plan of wave `wave` of the most recent step of `layer` (the plan the
+ * docs' "Captured decode" planner writes to device buffers: experts, slots,
+ * count): *count page-ins, experts[r] copied into slots[r] evicting
+ * evicted[r] (-1 = slot was empty), r < *count (arrays of K entries), and
+ * *n_waves of that step.  Synchronises `stream`.  Pointers may be NULL. */
 int pe_get_plan(pe_ctx* ctx, int layer, int wave, int32_t* count, int32_t* experts,
                 int32_t* slots, int32_t* evicted, int32_t* n_waves, void* stream);
 
-/* Slot each routed entry of the most recent step of `layer` ran in
- * (slot_of [T*k], -1 for an invalid id), T of that step.  Synchronises. */
+/* Slot each routed entry of the most recent step of `layer` ran in (the
+ * slot remap of docs, "A step: waves, page-in, merge", step 3; slot_of
+ * [T*k], -1 for an invalid id), T of that step.  Synchronises. */
 int pe_get_slot_map(pe_ctx* ctx, int layer, int32_t* slot_of, int T, void* stream);
 
-/* Counters (synchronises the device to read the device-side ones). */
+/* Plan log (PE_FLAG_PLAN_LOG): every step of a layer, device-planned or not,
+ * captured in a graph or not, appends one record of int32 words to the
+ * layer's ring of plan_log_steps records, written on the device after the
+ * step's kernels (a replayed graph logs every replay).  Record layout, with
+ * MW = pe_max_waves and N = max_tokens * top_k:
+ *   [0] step number of the layer since pe_create (0, 1, ...), [1] T,
+ *   [2] the layer's tick after the step, [3] 0,
+ *   [4] n_waves, then count[MW], experts[MW*K], slots[MW*K], evicted[MW*K]
+ *       (wave w's page-ins r < count[w] at [w*K + r]; entries past n_waves
+ *       or count[w] are stale), then slot_of[N] (first T*k valid),
+ *   then slot_expert[K] and last_use[K] after the step,
+ *   padded to pe_plan_log_record_words words.
+ * pe_plan_log_record_words returns that size (or < 0). */
+int pe_plan_log_record_words(const pe_ctx* ctx);
+
+/* Copy the most recent min(steps logged, plan_log_steps, max_records) records
+ * of `layer`, oldest first, to `records` (max_records * record words int32,
+ * host); *n_records gets the count.  Synchronises `stream`.  Returns
+ * PE_ERR_INVALID_ARG without PE_FLAG_PLAN_LOG. */
+int pe_get_plan_log(pe_ctx* ctx, int layer, int32_t* records, int max_records, int* n_records, void* stream);
+
+/* Counters of the docs' "Captured decode" dispatch and of the pages'
+ * byte accounting (page-ins times blob bytes; synchronises the device to read
+ * the device-side ones). */
 int pe_get_stats(pe_ctx* ctx, pe_stats* out);
 int pe_reset_stats(pe_ctx* ctx);
 

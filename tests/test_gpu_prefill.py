@@ -15,7 +15,7 @@ from oracle.lru import LayerLRU
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 2e-2}
+TOL = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 1e-2}
 
 
 def _expert_fn(wl, layer):
