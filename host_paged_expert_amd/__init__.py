@@ -10,9 +10,9 @@ from ._binding import (  # noqa: F401
     PE_OK, PE_ERR_INVALID_ARG, PE_ERR_UNSUPPORTED, PE_ERR_OOM_HOST_PIN, PE_ERR_OOM_DEVICE, PE_ERR_HIP,
     PE_ERR_NOT_CAPTURABLE, PE_W_BF16, PE_W_FP8_B128, PE_W_INT4_G128, PE_W_INT8_G128, PE_W_MXFP4_B32,
     WTYPES,
-    PE_FLAG_PAGEIN_DMA, PE_FLAG_FORCE_HOST_PLAN, PE_FLAG_UNPAGED, PE_FLAG_PLAN_LOG,
+    PE_FLAG_PAGEIN_DMA, PE_FLAG_FORCE_HOST_PLAN, PE_FLAG_UNPAGED, PE_FLAG_PLAN_LOG, PE_STATIC_SCRATCH_BYTES,
     SIGNATURES,
-    pe_create, pe_destroy, pe_load_expert, pe_forward, pe_forward_rc, pe_reset_lru,
+    pe_create, pe_destroy, pe_load_expert, pe_forward, pe_forward_rc, pe_forward_static, pe_reset_lru,
     pe_expert_bytes, pe_plan_log_record_words, pe_get_plan_log, parse_plan_record,
     pe_suggest_k, pe_max_captured_batch, pe_max_waves, pe_get_lru_state, pe_get_plan, pe_get_slot_map, pe_get_stats,
     pe_reset_stats, pe_link_probe, pe_plan_host, pe_strerror, pe_last_error,
@@ -69,6 +69,11 @@ class PagedMoE:
         T = x.shape[0] if T is None else T
         self._check_step(x, topk_ids, topk_w, out, T)
         return pe_forward(self.ctx, layer, x, topk_ids, topk_w, T, out, stream)
+
+    def forward_static(self, layer, x, topk_ids, topk_w, out, stream=None, T=None):
+        T = x.shape[0] if T is None else T
+        self._check_step(x, topk_ids, topk_w, out, T)
+        return pe_forward_static(self.ctx, layer, x, topk_ids, topk_w, T, out, stream)
 
     def plan_log(self, layer, max_records=None, stream=None):
         """Parsed plan-log records of `layer`, oldest first."""

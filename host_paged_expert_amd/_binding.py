@@ -33,6 +33,7 @@ PE_FLAG_PAGEIN_DMA = 1
 PE_FLAG_FORCE_HOST_PLAN = 2
 PE_FLAG_UNPAGED = 4
 PE_FLAG_PLAN_LOG = 8
+PE_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class pe_config(ctypes.Structure):
@@ -73,6 +74,7 @@ SIGNATURES = {
     "pe_get_slot_map": (_i, [_vp, _i, _vp, _i, _vp]),
     "pe_plan_log_record_words": (_i, [_vp]),
     "pe_get_plan_log": (_i, [_vp, _i, _vp, _i, _vp, _vp]),
+    "pe_forward_static": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "pe_get_stats": (_i, [_vp, ctypes.POINTER(pe_stats)]),
     "pe_reset_stats": (_i, [_vp]),
     "pe_link_probe": (_i, [_vp, _sz, _i, _i, ctypes.POINTER(ctypes.c_double), _vp]),
@@ -154,6 +156,11 @@ def pe_forward(ctx, layer, x, topk_ids, topk_w, T, out, stream=None):
 def pe_forward_rc(ctx, layer, x, topk_ids, topk_w, T, out, stream=None):
     """pe_forward returning the status code instead of raising."""
     return lib().pe_forward(ctx, layer, _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, _ptr(out), _stream(stream))
+
+
+def pe_forward_static(ctx, layer, x, topk_ids, topk_w, T, out, stream=None):
+    return _check(lib().pe_forward_static(ctx, layer, _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, _ptr(out),
+                                          _stream(stream)))
 
 
 def pe_reset_lru(ctx, layer=-1, stream=None):

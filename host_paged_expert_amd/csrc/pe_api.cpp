@@ -97,6 +97,8 @@ constexpr int kPageInGrid = 128;
 // blocks of every format at hidden 2048 / inter 768: 192, 96 and 48).
 constexpr int kStreamWgs = 96;
 
+static_assert(pe::kStaticScratchBytes == PE_STATIC_SCRATCH_BYTES, "the fixed scratch size is stated in pe.h");
+
 }  // namespace
 
 struct pe_ctx {
@@ -171,7 +173,7 @@ int use_device(const pe_ctx* c) {
   return PE_OK;
 }
 
-// Where a step's activations go.
+// Where a step's activations go: the context's buffers, or the fixed scratch area.
 struct Act {
   uint16_t* h;
   float* merged;
@@ -461,7 +463,12 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     free_ctx(c);
     return fail(PE_ERR_HIP, "resetting the LRU state failed: %s", hipGetErrorString(hipGetLastError()));
   }
-
+  // The fixed scratch area of pe_forward_static: its address on this device,
+  // looked up once per device while the device is current.
+  if (!pe::static_scratch(g.device)) {
+    free_ctx(c);
+    return fail(PE_ERR_HIP, "hipGetSymbolAddress failed for the fixed scratch area");
+  }
   *out = c;
   return PE_OK;
 }
@@ -723,6 +730,25 @@ int pe_forward(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, con
   return forward_impl(c, layer, x, topk_ids, topk_w, T, out, stream, Act{c->h, c->merged}, true);
 }
 
+int pe_forward_static(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, const float* topk_w, int T,
+                      void* out, void* stream) {
+  const int rc = check_forward(c, layer, x, topk_ids, topk_w, T, out);
+  if (rc) return rc < 0 ? rc : PE_OK;
+  // h [n][I] bf16, then the merged buffer [n][H] fp32, 256-byte aligned
+  const size_t n = (size_t)T * c->d.k;
+  const size_t h_bytes = align_up(n * c->d.I * 2, 256);
+  const size_t need = h_bytes + n * c->d.H * 4;
+  if (need > pe::kStaticScratchBytes)
+    return fail(PE_ERR_INVALID_ARG,
+                "pe_forward_static: %zu entries need %zu bytes of scratch, more than the fixed %zu "
+                "(%zu entries fit at this hidden and inter size)",
+                n, need, pe::kStaticScratchBytes,
+                (size_t)((pe::kStaticScratchBytes - 256) / (2 * (size_t)c->d.I + 4 * (size_t)c->d.H)));
+  char* base = static_cast<char*>(pe::static_scratch(c->cfg.device));
+  if (!base) return fail(PE_ERR_HIP, "the fixed scratch area has no address on device %d", c->cfg.device);
+  const Act act{reinterpret_cast<uint16_t*>(base), reinterpret_cast<float*>(base + h_bytes)};
+  return forward_impl(c, layer, x, topk_ids, topk_w, T, out, stream, act, false);
+}
 
 int pe_max_captured_batch(const pe_ctx* c) {
   if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");

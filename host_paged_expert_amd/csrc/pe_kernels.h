@@ -118,4 +118,10 @@ void launch_gather_state(const int32_t* blk, int state_words, const int32_t* ids
 void launch_plan_log(const int32_t* blk, const Offsets& o, int K, int plan0, int plan_words, int T,
                      int32_t* ring, int cap, int rec_words, uint32_t* seq, hipStream_t s);
 
+// The library's fixed device scratch area (no allocation): its size, and its
+// address on the current device (looked up once per device with
+// hipGetSymbolAddress; NULL if the lookup failed).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+void* static_scratch(int device);
+
 }  // namespace pe

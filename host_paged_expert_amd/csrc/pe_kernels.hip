@@ -2333,4 +2333,33 @@ void launch_plan_log(const int32_t* blk, const Offsets& o, int K, int plan0, int
   plan_log_kernel<<<1, 256, 0, s>>>(blk, o, K, plan0, plan_words, T, ring, cap, rec_words, seq);
 }
 
+// ------------------------------------------------------------------ fixed scratch area
+
+// The activations of pe_forward_static (h, then the merged buffer) live here
+// instead of in the context's allocations.  Each device the library runs on
+// holds its own copy until the process ends.  Host code never passes this name
+// to a kernel: in host code it is only a stand-in for the symbol, and the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+void* static_scratch(int device) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(device);
+  if (it != addr.end()) return it->second;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != device) {
+    (void)hipGetLastError();
+    return nullptr;      // the caller makes `device` current first
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  addr[device] = ptr;
+  return ptr;
+}
+
 }  // namespace pe

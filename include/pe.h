@@ -276,6 +276,24 @@ int pe_plan_host(int num_experts, int num_resident, int top_k, int T, const int3
 int pe_set_timing(pe_ctx* ctx, int enable);
 int pe_get_timing(pe_ctx* ctx, uint64_t* launches, double* total_ms);
 
+/* ---- a variant for callers that cannot allocate ---------------------------
+ *
+ * For code that must not call hipMalloc (under hipGraph capture, in tight
+ * serving loops, in harnesses that forbid it): pe_forward with the step's
+ * activations (the bf16 gate/up results and the fp32 merged entries) in a
+ * fixed device scratch area the library holds from load time, of
+ * PE_STATIC_SCRATCH_BYTES per GPU, instead of the context's buffers.  It
+ * allocates nothing.  A step needs (T*top_k*inter*2 rounded up to 256) +
+ * T*top_k*hidden*4 bytes; a larger step is rejected with PE_ERR_INVALID_ARG
+ * and enqueues nothing.  Everything else (arguments, results, capture rules,
+ * host-planned steps) is pe_forward's; stage timing is not recorded.  Every
+ * call on one GPU shares that GPU's area, whatever the context: calls that
+ * overlap in time on one GPU (two streams, two threads) race and give wrong
+ * results.  Nothing in the area needs to start at zero. */
+#define PE_STATIC_SCRATCH_BYTES (16u << 20)
+int pe_forward_static(pe_ctx* ctx, int layer, const void* x, const int32_t* topk_ids,
+                      const float* topk_w, int T, void* out, void* stream);
+
 const char* pe_strerror(int status);
 const char* pe_last_error(void);
 
