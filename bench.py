@@ -75,6 +75,9 @@ def parse():
                          "--sweep-resident (the workload's format and routing), one JSON line per point")
     ap.add_argument("--sweep-batches", default="1,2,3,4,5,6,7,8")
     ap.add_argument("--sweep-resident", default="24,40")
+    ap.add_argument("--warm-prefill", action="store_true",
+                    help="prefill workloads: also time the chunk with every expert resident (K = E, no page-in), "
+                         "which exposes the MFMA expert kernels")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="profiling: first run one plain device-to-device copy of this many MiB, "
                          "a known-size kernel to scale memory counters by")
@@ -335,7 +338,67 @@ def main():
         result["cpu_baseline"], result["sample_parity"] = cpu_baseline(wl, routing, steps, sample_steps, samples,
                                                                        M, D, has_prefill, args.cpu_budget)
     m.close()
+    if has_prefill and args.warm_prefill:
+        del m, runner
+        torch.cuda.empty_cache()
+        result["prefill_warm"] = warm_prefill(wl, xp, idsp, wp, outp, stream)
     print(json.dumps(result), flush=True)
+
+
+MFMA_BF16_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+
+
+def warm_prefill(wl, xp, idsp, wp, outp, stream):
+    """The prefill chunk with every expert resident: an unpaged context (K = E,
+    slot e holds expert e, no page-in), so the step is planning, the MFMA (and
+    GEMV) expert kernels and the top-k sum.  Each expert kernel is set against
+    its own roofline, the larger of its MFMA time at the bf16 peak and its HBM
+    time for the weights it reads once (D experts' gate/up or down weights)."""
+    import torch
+
+    import harness
+    import host_paged_expert_amd as pe
+
+    L = wl.layers
+    m = harness.make_moe(wl, flags=pe.PE_FLAG_UNPAGED, max_tokens=wl.prefill_tokens)
+    harness.load_store(m, wl, progress=L * wl.experts // 4)
+    log("warm prefill: unpaged context loaded")
+
+    def chunk():
+        for l in range(L):
+            m.forward(l, xp, idsp[l], wp[l], outp[l], stream=stream)
+    chunk()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        chunk()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    m.reset_stats()
+    m.set_timing(1)
+    chunk()
+    tm = m.timing()
+    m.set_timing(0)
+    st = m.stats()
+    m.close()
+    H, I = wl.hidden, wl.inter
+    w13, w2, s13, s2 = part_bytes(wl.wtype, H, I)
+    ent, D = st["entries"], st["distinct"]
+    out = {"ms": round(min(times), 2), "tok_s": round(wl.prefill_tokens / (min(times) / 1e3), 1), "distinct": D}
+    for name, flops, wbytes in (("gate_up", ent * 2.0 * 2 * H * I, D * (w13 + s13)),
+                                ("down", ent * 2.0 * H * I, D * (w2 + s2))):
+        n, ms = tm[name]
+        roof_ms = max(flops / MFMA_BF16_PEAK, wbytes / (HBM_PEAK_GBS * 1e9)) * 1e3
+        out[name] = {"launches": n, "ms": round(ms, 3), "tflops": round(flops / (ms / 1e3) / 1e12, 1) if ms else None,
+                     "roof_ms": round(roof_ms, 3), "frac": round(roof_ms / ms, 4) if ms else None,
+                     "bound": "mfma" if flops / MFMA_BF16_PEAK > wbytes / (HBM_PEAK_GBS * 1e9) else "hbm"}
+    log("warm prefill: %.1f ms for %d tokens; gate/up %.1f ms (%.3f of its roofline), down %.1f ms (%.3f)" % (
+        out["ms"], wl.prefill_tokens, out["gate_up"]["ms"], out["gate_up"]["frac"] or 0, out["down"]["ms"],
+        out["down"]["frac"] or 0))
+    return out
 
 
 def sweep(args):
@@ -407,11 +470,59 @@ def sweep(args):
                    "roofline_path": {"model": "D*S/HBM + M*S/link", "link_gbs": round(link, 2),
                                      "roof_tok_s": round(steps * B / t_roof, 2),
                                      "frac": round(value / (steps * B / t_roof), 4)}}
-            log("sweep: K=%d batch %d (%s): %.1f tok/s, %.3f of roofline, %d waves" % (
-                K, B, res["config"]["path"], value, res["roofline_path"]["frac"], st["waves"]))
+            res["sample_parity"] = sweep_parity(m, wl, routing, runner, cold, st)
+            log("sweep: K=%d batch %d (%s): %.1f tok/s, %.3f of roofline, %d waves, parity %s" % (
+                K, B, res["config"]["path"], value, res["roofline_path"]["frac"], st["waves"],
+                "ok" if res["sample_parity"]["ok"] else "FAILED"))
             print(json.dumps(res), flush=True)
             del runner
         m.close()
+
+
+def sweep_parity(m, wl, routing, runner, cold, st):
+    """One sweep point checked against the oracle: the window's page-in,
+    distinct and wave counts against the LRU simulator, and the outputs of the
+    first and last layer at the first and last step (from one more pass over
+    the window, from an empty table) against the fp32 unpaged layer."""
+    import numpy as np
+    import torch
+
+    import harness
+    import synth
+    from oracle import formats, moe
+    from oracle.lru import LayerLRU
+
+    L, S = wl.layers, wl.steps
+    misses = distinct = waves = 0
+    for l in range(L):
+        sim = LayerLRU(wl.experts, wl.resident)
+        for s in range(S):
+            ids = routing["decode_ids"][s, l].ravel()
+            w = sim.step(ids)
+            misses += sum(v.count for v in w)
+            waves += len(w)
+            distinct += len(set(ids.tolist()))
+    counts_ok = (misses, distinct, waves) == (st["page_ins"], st["distinct"], st["waves"])
+    pick = sorted({0, S - 1})
+    cold()
+    got = {}
+    for s in range(S):
+        runner.run(1)
+        if s in pick:
+            got[s] = harness.bf16_bits(runner.out)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for s in pick:
+        x = formats.bf16_to_f32(synth.hidden_states(wl, s, wl.batch))
+        for l in sorted({0, L - 1}):
+            ids, w = routing["decode_ids"][s, l], routing["decode_w"][s, l]
+            canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(ids)}
+            ref = moe.moe_layer(x, ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+            g = harness.bf16_to_f32(got[s][l])
+            worst = max(worst, float(np.abs(g - ref).max() / np.abs(ref).max()))
+    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 1e-2}[wl.wtype]
+    return {"pairs": len(pick) * len({0, L - 1}), "steps": pick, "max_rel_err": worst, "tol": tol,
+            "counts_match_simulator": counts_ok, "ok": bool(counts_ok and worst <= tol)}
 
 
 def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=False, budget_s=20.0):
@@ -468,18 +579,46 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
                 worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
         log("oracle: %d (step, layer) pairs, %.1fs of oracle time" % (len(done), t_moe))
     pool.shutdown()
-    pre_worst = None
+    # one thread: the first (step, layer) pairs again, BLAS limited to one thread,
+    # for about a quarter of the budget
+    t_one, one = 0.0, 0
+    with threadpoolctl.threadpool_limits(1):
+        for (s, l) in done:
+            if t_one >= budget_s / 4:
+                break
+            canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(routing["decode_ids"][s, l])}
+            t1 = time.perf_counter()
+            moe.moe_layer(xs[s], routing["decode_ids"][s, l], routing["decode_w"][s, l],
+                          lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+            t_one += time.perf_counter() - t1
+            one += 1
+    log("oracle, one thread: %d (step, layer) pairs in %.2fs" % (one, t_one))
+    pre_worst, pre_cpu = None, None
     if has_prefill and "prefill" in samples:
+        # the whole prefill chunk through as many layers as the budget allows
+        # (the first and the last at least), timed; expert tensors untimed
         xp = formats.bf16_to_f32(synth.hidden_states(wl, -1, wl.prefill_tokens))
-        pre_worst = 0.0
-        for l in (0, L - 1):
+        pre_worst, t_pre, pre_layers = 0.0, 0.0, []
+        order = [0, L - 1] + [l for l in range(1, L - 1)]
+        pool = ThreadPoolExecutor(harness.host_threads())
+        for l in order:
+            if len(pre_layers) >= 2 and t_pre >= budget_s:
+                break
             ids, w = routing["prefill_ids"][l], routing["prefill_w"][l]
-            canon = {int(e): synth.expert_tensors(wl, l, int(e)) for e in np.unique(ids)}
+            used = [int(e) for e in np.unique(ids)]
+            canon = dict(zip(used, pool.map(lambda e: synth.expert_tensors(wl, l, e), used)))
+            t1 = time.perf_counter()
             ref = moe.moe_layer(xp, ids, w, lambda e: formats.dequant_expert(wl.wtype, *canon[e]))
+            t_pre += time.perf_counter() - t1
+            pre_layers.append(l)
             got = harness.bf16_to_f32(samples["prefill"][l])
             pre_worst = max(pre_worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
-            log("oracle prefill layer %d done" % l)
-        log("oracle prefill layers 0 and %d: max rel err %.2e" % (L - 1, pre_worst))
+            log("oracle prefill layer %d: %.1fs of oracle time so far" % (l, t_pre))
+        pool.shutdown()
+        log("oracle prefill, %d layers: max rel err %.2e" % (len(pre_layers), pre_worst))
+        pre_cpu = {"value": round(wl.prefill_tokens / (t_pre / len(pre_layers) * L), 3), "unit": "tok/s",
+                   "sample": "the whole %d-token prefill chunk through layers %s (of %d), fp32 unpaged oracle" % (
+                       wl.prefill_tokens, pre_layers, L)}
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     tokens = B * len(done) / L                      # a token passes all L layers
     t_total = t_moe + t_sim * (len(done) / L) / steps
@@ -488,13 +627,18 @@ def cpu_baseline(wl, routing, steps, sample_steps, samples, M, D, has_prefill=Fa
     cpu = {"value": round(tokens / t_total, 5) if t_total > 0 else None, "unit": "tok/s", "cores": threads,
            "kind": "oracle",
            "sample": "%d (step, layer) pairs from decode steps %s (batch %d) through the fp32 unpaged oracle, "
-                     "plus the LRU simulator over all %d steps x %d layers; host %s, %d cpus" % (
-                         len(done), sample_steps, B, steps, L, cpu_model(), os.cpu_count())}
+                     "plus the LRU simulator over all %d steps x %d layers; host %s, %d cpus, BLAS on %d threads"
+                     % (len(done), sample_steps, B, steps, L, cpu_model(), os.cpu_count(), threads),
+           "single_thread": {"value": round(B * one / L / t_one, 5) if t_one > 0 else None, "unit": "tok/s",
+                             "cores": 1, "sample": "the first %d of those (step, layer) pairs, BLAS on one thread"
+                             % one}}
+    if pre_cpu:
+        cpu["prefill"] = pre_cpu
     parity = {"pairs": len(done), "max_rel_err": worst, "tol": tol,
               "ok": bool(worst <= tol and (pre_worst is None or pre_worst <= tol)) if samples else None,
               "plans_match_simulator": plan_ok}
     if pre_worst is not None:
-        parity["prefill_layers"] = [0, L - 1]
+        parity["prefill_layers"] = pre_layers
         parity["prefill_max_rel_err"] = pre_worst
     return cpu, parity
 

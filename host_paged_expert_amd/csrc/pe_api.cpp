@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -127,6 +128,12 @@ struct pe_ctx {
   int32_t* st_blk = nullptr;           // [L][layer_words]
   int32_t* st_ids_dev = nullptr;       // device-visible addresses of the two
   int32_t* st_blk_dev = nullptr;
+  // The read-back's completion word (page-locked, mapped, coherent): the launch
+  // stores the step's sequence number there once its writes are visible, and
+  // the host polls it instead of synchronising the stream.
+  uint32_t* st_flag = nullptr;
+  uint32_t* st_flag_dev = nullptr;
+  uint32_t gather_seq = 0;
   pe::HostPlanSummary* sum = nullptr;
   // plan log (PE_FLAG_PLAN_LOG): per layer a ring of log_cap records
   pe::PlanLogLayout pl{};
@@ -156,6 +163,7 @@ void free_ctx(pe_ctx* c) {
   if (c->host_store) (void)hipHostFree(c->host_store);
   if (c->st_ids) (void)hipHostFree(c->st_ids);
   if (c->st_blk) (void)hipHostFree(c->st_blk);
+  if (c->st_flag) (void)hipHostFree(c->st_flag);
   for (void* p : {(void*)c->slots, (void*)c->blocks, (void*)c->h, (void*)c->merged,
                   (void*)c->stats, (void*)c->plan_log, (void*)c->log_seq})
     if (p) (void)hipFree(p);
@@ -425,7 +433,8 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
     }
   }
   struct { int32_t** p; size_t words; } pin[] = {
-      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, (size_t)d.L * c->layer_words}};
+      {&c->st_ids, (size_t)d.max_entries}, {&c->st_blk, (size_t)d.L * c->layer_words},
+      {reinterpret_cast<int32_t**>(&c->st_flag), 64}};
   for (auto& a : pin) {
     if (hipHostMalloc(reinterpret_cast<void**>(a.p), a.words * 4, hipHostMallocMapped | hipHostMallocCoherent) !=
         hipSuccess) {
@@ -438,13 +447,17 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   {
     void* a = nullptr;
     void* b = nullptr;
+    void* f = nullptr;
     if (hipHostGetDevicePointer(&a, c->st_ids, 0) != hipSuccess ||
-        hipHostGetDevicePointer(&b, c->st_blk, 0) != hipSuccess) {
+        hipHostGetDevicePointer(&b, c->st_blk, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&f, c->st_flag, 0) != hipSuccess) {
       free_ctx(c);
       return fail(PE_ERR_HIP, "hipHostGetDevicePointer failed for the staging buffers");
     }
     c->st_ids_dev = static_cast<int32_t*>(a);
     c->st_blk_dev = static_cast<int32_t*>(b);
+    c->st_flag_dev = static_cast<uint32_t*>(f);
+    *c->st_flag = 0;
   }
   if (hipMemset(c->stats, 0, pe::ST_COUNT * 8) != hipSuccess ||
       hipMemset(c->blocks, 0, (size_t)d.L * c->layer_words * 4) != hipSuccess ||
@@ -524,6 +537,19 @@ int pe_reset_lru(pe_ctx* c, int layer, void* stream) {
 }
 
 namespace {
+
+// Poll the read-back's completion word until it holds `want`, for at most about
+// 200 ms (a step's read-back normally lands within microseconds); false if it
+// did not.
+bool poll_flag(const uint32_t* flag, uint32_t want) {
+  if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == want) return true;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (unsigned i = 1;; ++i) {
+    if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == want) return true;
+    __builtin_ia32_pause();
+    if ((i & 1023) == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(200)) return false;
+  }
+}
 
 // Append the record of the step that just ended to the layer's plan log.
 void log_step(pe_ctx* c, const int32_t* blk, int layer, int T, hipStream_t s) {
@@ -622,20 +648,34 @@ int forward_impl(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, c
   // and the work lists back into device memory, and the waves run in order.
   int32_t* mirror = c->st_blk + (size_t)layer * c->layer_words;
   int32_t* mirror_dev = c->st_blk_dev + (size_t)layer * c->layer_words;
-  pe::launch_gather_state(blk, (int)c->ll.state_prefix, topk_ids, n, mirror_dev, c->st_ids_dev, s);
+  if (++c->gather_seq == 0) c->gather_seq = 1;     // 0 is the word's initial value
+  const uint32_t want = c->gather_seq;
+  pe::launch_gather_state(blk, (int)c->ll.state_prefix, topk_ids, n, mirror_dev, c->st_ids_dev, c->st_flag_dev,
+                          want, s);
   PE_HIP(hipGetLastError());
-  PE_HIP(hipStreamSynchronize(s));
+  if (!poll_flag(c->st_flag, want)) {
+    // not seen within the polling budget: wait for the stream the ordinary way
+    PE_HIP(hipStreamSynchronize(s));
+    if (__atomic_load_n(c->st_flag, __ATOMIC_ACQUIRE) != want)
+      return fail(PE_ERR_HIP, "the routed ids and LRU state were not read back (step %u)", want);
+  }
   pe::HostPlanSummary& sm = *c->sum;
   pe::Dims dp = d;
   dp.mfma_min = mfma_min;
   if (pe::host_plan_step(dp, c->ll, c->wl, c->st_ids, n, mirror, mirror + c->ll.total, &sm) != 0)
     return fail(PE_ERR_INVALID_ARG, "step needs more waves than the context holds");
-  {
-    const size_t bytes = align_up((c->ll.total + c->wl.entries + (size_t)n) * 4, 16);
-    const int grid = (int)std::min<size_t>(16, std::max<size_t>(1, bytes / 8192));
-    pe::launch_copy(blk, mirror_dev, bytes, grid, s);
-  }
+  // The plan (the block with state, plans and slot map, and the work lists that
+  // follow it) goes to device memory in one copy.  When the first wave is a
+  // streamed GEMV wave, that wave's launch makes the copy with one extra
+  // workgroup and reads its own work lists from the host's copy: one launch
+  // fewer between the host's plan and the GPU's work.
   const bool dma = (c->cfg.flags & PE_FLAG_PAGEIN_DMA) != 0;
+  const size_t up_bytes = align_up((c->ll.total + c->wl.entries + (size_t)n) * 4, 16);
+  const bool fold = sm.n_waves > 0 && !c->unpaged && !dma && sm.tiles[0] == 0;
+  if (!fold) {
+    const int grid = (int)std::min<size_t>(16, std::max<size_t>(1, up_bytes / 8192));
+    pe::launch_copy(blk, mirror_dev, up_bytes, grid, s);
+  }
   bool summed = false;     // the top-k sum already ran with the last down projection
   for (int w = 0; w < sm.n_waves; ++w) {
     const int cnt = mirror[c->ll.plan_count + w];
@@ -646,12 +686,20 @@ int forward_impl(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, c
       // gate/up projection fused in while the resident ones run theirs, then
       // one launch runs the wave's down projection.
       pe::ExpertArgs a = expert_args(c, act, layer, w, x, topk_w, 1);
+      const bool up = fold && w == 0;
+      if (up) {
+        a.work = mirror_dev + c->ll.total;
+        a.hdr_known = 1;
+        a.g0 = 0;
+        a.gsplit = g_hit;
+        a.g1 = g_all;
+      }
       {
         StageTimer tm(c, PE_STAGE_PAGE_IN, s, tm_on);
         pe::launch_wave_a(c->cfg.wtype, a, g_hit, sm.max_gemv_tokens, kStreamWgs, host_l, c->b.stride,
-                          c->b.copied, s);
+                          c->b.copied, up ? mirror_dev : nullptr, up ? blk : nullptr, up ? up_bytes : 0, s);
       }
-      a.part = 0;
+      a = expert_args(c, act, layer, w, x, topk_w, 0);     // device work lists from here on
       StageTimer tm(c, PE_STAGE_DOWN, s, tm_on);
       if (sm.n_waves == 1 && mfma_min == pe::kNoMfma && down_sum_fits(n)) {
         // one wave of few tokens: its down projection and the top-k sum in one

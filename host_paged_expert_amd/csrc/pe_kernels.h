@@ -37,6 +37,10 @@ struct ExpertArgs {
   // expert from the routed ids and the current LRU-state copy instead of the
   // published work lists, so it can run alongside the planning + page-in kernel.
   int lean;
+  // hdr_known = 1: this launch's GEMV ranges of the wave (start, end of the
+  // experts resident before the wave, end) are g0 / gsplit / g1 instead of the
+  // work arena's header (which may be in host memory)
+  int hdr_known, g0, gsplit, g1;
   int mfma_min;
   const int32_t* ids;         // [T*k] routed ids
   int T, E;
@@ -82,13 +86,17 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
                    int max_m, hipStream_t s);
 void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s);
 
-// Host-planned wave with no MFMA tiles (work lists uploaded, `a` = the wave,
-// part 1): `P` workgroups page in the wave's missing experts from the mapped
-// host rows with their gate/up projection computed on the way; the others run
-// the gate/up projection of its `hit_items` resident experts.  Follow with
+// Host-planned wave with no MFMA tiles (`a` = the wave, part 1): `P` workgroups
+// page in the wave's missing experts from the mapped host rows with their
+// gate/up projection computed on the way; the others run the gate/up
+// projection of its `hit_items` resident experts.  With up_bytes > 0, one more
+// workgroup copies `up_bytes` from the mapped host address `up_src` (the host's
+// plan) to `up_dst` (the layer block and work lists in device memory), and
+// `a.work` may point at the host's copy of the work lists.  Follow with
 // launch_gemv_down over all of the wave's GEMV items (part 0).
 void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int P, const uint8_t* host_rows,
-                   size_t stride, size_t copy_bytes, hipStream_t s);
+                   size_t stride, size_t copy_bytes, const void* up_src, void* up_dst, size_t up_bytes,
+                   hipStream_t s);
 
 // MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
 // tokens).  Need H and I multiples of 128.
@@ -106,10 +114,12 @@ void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const
 
 // Host-planned step, before the host plans: copy the layer block's first
 // `state_words` words (current-copy index and both LRU-state copies) to
-// `host_blk` and the n routed ids to `host_ids`, both page-locked host memory
-// written through its mapped device address (one launch, no copy engine).
+// `host_blk` and the n routed ids to `host_ids`, both page-locked coherent host
+// memory written through its mapped device address (one launch, no copy
+// engine), then store `seq` to the host word `flag` once those writes are
+// visible to the host.
 void launch_gather_state(const int32_t* blk, int state_words, const int32_t* ids, int n, int32_t* host_blk,
-                         int32_t* host_ids, hipStream_t s);
+                         int32_t* host_ids, uint32_t* flag, uint32_t seq, hipStream_t s);
 
 // Append one record (PlanLogLayout) of the step that just ended to the layer's
 // plan-log ring: `ring` holds `cap` records of `rec_words` words; *seq counts

@@ -395,7 +395,7 @@ __device__ int plan_page_in_block(const PlanArgs& p, int block, int ncopy, char*
       if (c < mfma_min) {
         const int g = miss ? g_hit + s_pref(4, e) : s_pref(3, e);
         gemv_u[g] = u;
-        reinterpret_cast<int4*>(work + o.gemv_desc)[g] = make_int4(j, s_pref(2, e), c, u);
+        reinterpret_cast<int4*>(work + o.gemv_desc)[g] = make_int4(j, s_pref(2, e), c, e);
       } else {
         int t0 = miss ? t_hit + s_pref(6, e) : s_pref(5, e);
         for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
@@ -1045,9 +1045,14 @@ __device__ bool lean_hit_item(const ExpertArgs& a, int item, GemvItem& it, char*
 
 __device__ __forceinline__ bool gemv_item(const ExpertArgs& a, int item, GemvItem& it, char* lds) {
   if (a.lean) return lean_hit_item(a, item, it, lds);
-  const int32_t* hdr = a.work + a.o.hdr;
   int g0, g1;
-  part_range(a, hdr[hdr_gemv(a.MW, a.wave)], hdr[hdr_gemv_split(a.MW, a.wave)], hdr[hdr_gemv(a.MW, a.wave + 1)], g0, g1);
+  if (a.hdr_known) {
+    part_range(a, a.g0, a.gsplit, a.g1, g0, g1);
+  } else {
+    const int32_t* hdr = a.work + a.o.hdr;
+    part_range(a, hdr[hdr_gemv(a.MW, a.wave)], hdr[hdr_gemv_split(a.MW, a.wave)], hdr[hdr_gemv(a.MW, a.wave + 1)], g0,
+               g1);
+  }
   if (item >= g1 - g0) return false;
   const int4 dsc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc)[g0 + item];
   it.slot = dsc.x;
@@ -1099,6 +1104,7 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
   const int R0 = bx * nr * rows_per_block, R1 = min(I, R0 + nr * rows_per_block);
   const int SW = scale_stage_words<FMT>(nr * rows_per_block, H);
   char* s_sc = lds + gemv_lds_head(a) + al16((size_t)MB * H * 2);
+  int* s_e8 = reinterpret_cast<int*>(s_sc + 32 * (size_t)SW);     // the token batch's entries
   ScaleSpan gs{0, 0}, us{0, 0};
   if constexpr (FMT != PE_W_BF16) {
     gs = scale_span<FMT>(R0, R1, H);
@@ -1115,6 +1121,9 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
       load_row(W13 + (size_t)(I + i0) * n_ch, n_ch, lig, LG, wu);
     }
     if (tb > 0) __syncthreads();     // the previous batch's token vectors are consumed
+    // the batch's entries (the work lists may be in host memory: one read each)
+    if ((int)threadIdx.x < mb) s_e8[threadIdx.x] = ent[tb + threadIdx.x];
+    __syncthreads();
     // the batch's token vectors, and with the first batch the scales
     const int n16 = H / 8, xw = mb * n16, sw = tb == 0 ? gs.words + us.words : 0;
     copy_words_to_lds(
@@ -1122,7 +1131,7 @@ __device__ void gate_up_block(const ExpertArgs& a, int bx, int by, int LG, int r
         [=](int i) -> const uint4* {
           if (i < xw) {
             const int t = i / n16;
-            return reinterpret_cast<const uint4*>(x + (size_t)(ent[tb + t] / k) * H) + (i - t * n16);
+            return reinterpret_cast<const uint4*>(x + (size_t)(s_e8[t] / k) * H) + (i - t * n16);
           }
           const int j = i - xw;
           return j < gs.words ? reinterpret_cast<const uint4*>(S13b + gs.begin) + j
@@ -1271,6 +1280,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(ExpertArgs a, G
 // 4096 (int4 / int8: rows_per_block * hidden / 128 fp16, at most 512; MXFP4:
 // rows_per_block * hidden / 32 bytes, at most 1024; FP8: one 128-row block row).
 constexpr size_t kStreamScaleLds = 2048;
+// LDS for one token batch's entries (at most 8), staged by every GEMV gate/up
+// block before it reads the batch's token vectors.
+constexpr size_t kEntStage = 32;
 
 // Gate/up row block gi of a missing expert, paged in and projected in one pass:
 // rows i of the block (gemv_gate_up_kernel's geometry) are read from the mapped
@@ -1284,7 +1296,7 @@ constexpr size_t kStreamScaleLds = 2048;
 template <int FMT, int MB>
 __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, const uint8_t* __restrict__ src,
                                     uint8_t* __restrict__ dst, int gi, const int* ent, int m, int off,
-                                    uint16_t* xs, char* s_sc) {
+                                    uint16_t* xs, char* s_sc, int* s_e8) {
   constexpr int VPC = Fmt<FMT>::VPC;
   const int H = a.H, I = a.I, n_ch = H / VPC, LG = g.LG;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1320,7 +1332,9 @@ __device__ void stream_gate_up_rows(const ExpertArgs& a, const GemvGeom& g, cons
     uint4 wg = make_uint4(0, 0, 0, 0), wu = wg;
     if (active && c < n_ch) { wg = sg[c]; wu = su[c]; }     // in flight during the staging
     __syncthreads();
-    stage_rows(xs, a.x, H, ent + tb, mb, a.k);
+    if ((int)threadIdx.x < mb) s_e8[threadIdx.x] = ent[tb + threadIdx.x];    // the entries may be in host memory
+    __syncthreads();
+    stage_rows(xs, a.x, H, s_e8, mb, a.k);
     if (FMT != PE_W_BF16 && tb == 0) {
       const uint16_t* hs = reinterpret_cast<const uint16_t*>(src + a.off_s13);
       uint16_t* ds = reinterpret_cast<uint16_t*>(dst + a.off_s13);
@@ -1383,6 +1397,7 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
   int* s_ent = reinterpret_cast<int*>(lds + plan_b);                                    // [n]
   char* s_sc = lds + plan_b + al16(4 * (size_t)p.n);                                    // scales
   uint16_t* xs = reinterpret_cast<uint16_t*>(s_sc + kStreamScaleLds);                   // [MB][H]
+  int* s_e8 = reinterpret_cast<int*>(s_sc + kStreamScaleLds + al16((size_t)MB * a.H * 2));   // [MB]
   for (int r = 0; r < n_miss; ++r) {
     int gi = ((w - (r * g.gx) % P) % P + P) % P;     // this workgroup's first block of expert r
     if (gi >= g.gx) continue;
@@ -1396,7 +1411,7 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
     const int m = L.cnt[e], off = L.off[r];
     const uint8_t* src = p.host_rows + (size_t)e * p.stride;
     uint8_t* dst = p.slots + (size_t)L.victim[r] * p.stride;
-    for (; gi < g.gx; gi += P) stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, s_ent, m, off, xs, s_sc);
+    for (; gi < g.gx; gi += P) stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, s_ent, m, off, xs, s_sc, s_e8);
     __syncthreads();     // s_ent is rebuilt for the next expert
   }
   for (int r = 0; r < n_miss; ++r)
@@ -1405,42 +1420,61 @@ __device__ void stream_in(const PlanArgs& p, const ExpertArgs& a, const GemvGeom
 }
 
 // Host-planned wave with no MFMA tiles, launch A: workgroups [0, P) page in the
-// wave's missing experts (its GEMV items past the hit split, descriptors from
-// the uploaded work lists), computing their gate/up projection from the rows as
-// they arrive (stream_gate_up_rows), then copy the rest of each blob; the others
-// run the gate/up projection of the wave's experts that were already resident
-// (`a.part` = 1).  The wave's down projection follows as its own launch.
+// wave's missing experts (its GEMV items past the hit split), computing their
+// gate/up projection from the rows as they arrive (stream_gate_up_rows), then
+// copy the rest of each blob; the next ceil(gx / nr) x hit items run the
+// gate/up projection of the wave's experts that were already resident
+// (`a.part` = 1), nr row blocks each.  If `up_bytes` is not 0, one more
+// workgroup copies the host's plan (layer block and work lists, `up_bytes`
+// from the mapped host mirror `up_src`) into device memory at `up_dst`, while
+// the others read their work lists from the mirror itself (`a.work`, with the
+// wave's GEMV ranges in `a.g0 / a.gsplit / a.g1`): the step's first wave then
+// needs no launch of its own for the upload.  The wave's down projection
+// follows as its own launch.
 template <int FMT, int MB>
-__global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, GemvGeom g, int P,
+__global__ __launch_bounds__(kGemvThreads) void wave_a_kernel(ExpertArgs a, GemvGeom g, int P, int nr,
                                                               const uint8_t* __restrict__ host_rows,
-                                                              size_t stride, size_t copy_bytes) {
+                                                              size_t stride, size_t copy_bytes,
+                                                              const uint4* __restrict__ up_src,
+                                                              uint4* __restrict__ up_dst, size_t up_bytes) {
   extern __shared__ __align__(16) char lds[];
+  if (up_bytes && blockIdx.x == gridDim.x - 1) {
+    copy_chunks(up_dst, up_src, up_bytes / 16, threadIdx.x, blockDim.x);
+    return;
+  }
   if ((int)blockIdx.x >= P) {
+    const int gxn = (g.gx + nr - 1) / nr;
     const int b = blockIdx.x - P;
-    gate_up_block<FMT, MB>(a, b % g.gx, b / g.gx, g.LG, g.rows_per_block, lds);
+    gate_up_block<FMT, MB>(a, b % gxn, b / gxn, g.LG, g.rows_per_block, lds, nr);
     return;
   }
   const int w = blockIdx.x;
-  const int32_t* hdr = a.work + a.o.hdr;
-  const int split = hdr[hdr_gemv_split(a.MW, a.wave)], g1 = hdr[hdr_gemv(a.MW, a.wave + 1)];
+  int split, g1;
+  if (a.hdr_known) {
+    split = a.gsplit;
+    g1 = a.g1;
+  } else {
+    const int32_t* hdr = a.work + a.o.hdr;
+    split = hdr[hdr_gemv_split(a.MW, a.wave)];
+    g1 = hdr[hdr_gemv(a.MW, a.wave + 1)];
+  }
   const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
   char* s_sc = lds;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + kStreamScaleLds);
+  int* s_e8 = reinterpret_cast<int*>(lds + kStreamScaleLds + al16((size_t)MB * a.H * 2));
   const int n_miss = g1 - split;
   for (int r = 0; r < n_miss; ++r) {
     int gi = ((w - (r * g.gx) % P) % P + P) % P;
     if (gi >= g.gx) continue;
-    const int4 d = desc[split + r];
-    const int e = a.work[a.o.used_expert + d.w];
-    const uint8_t* src = host_rows + (size_t)e * stride;
+    const int4 d = desc[split + r];     // {slot, first sorted position, entries, expert}
+    const uint8_t* src = host_rows + (size_t)d.w * stride;
     uint8_t* dst = const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride;
     for (; gi < g.gx; gi += P)
-      stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, a.work + a.o.entries + d.y, d.z, d.y, xs, s_sc);
+      stream_gate_up_rows<FMT, MB>(a, g, src, dst, gi, a.work + a.o.entries + d.y, d.z, d.y, xs, s_sc, s_e8);
   }
   for (int r = 0; r < n_miss; ++r) {
     const int4 d = desc[split + r];
-    const int e = a.work[a.o.used_expert + d.w];
-    copy_blob_rest(a, host_rows + (size_t)e * stride, const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride,
+    copy_blob_rest(a, host_rows + (size_t)d.w * stride, const_cast<uint8_t*>(a.slots) + (size_t)d.x * a.slot_stride,
                    copy_bytes, (size_t)w * blockDim.x + threadIdx.x, (size_t)P * blockDim.x);
   }
 }
@@ -1755,7 +1789,7 @@ void launch_gemv_gate_up(int wtype, const ExpertArgs& a, int items, int max_m, h
   if (items <= 0) return;
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t lds = lean_head(a) + gemv_stage(wtype, mb, a.H, g.rows_per_block, 2);
+  const size_t lds = lean_head(a) + gemv_stage(wtype, mb, a.H, g.rows_per_block, 2) + kEntStage;
   const dim3 grid(g.gx, items);
   PE_DISPATCH(wtype, mb, (gemv_gate_up_kernel<F_, M_><<<grid, kGemvThreads, lds, s>>>(a, g)));
 }
@@ -1776,11 +1810,12 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
   const PlanArgs p = plan_args(blk, ids, n, d, o, mfma_min, work, stats, host_rows, slots, stride, copy_bytes, true);
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t copier = copier_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds + (size_t)mb * a.H * 2;
+  const size_t copier = copier_lds_bytes(d.E, d.K, n) + al16(4 * (size_t)n) + kStreamScaleLds +
+                        al16((size_t)mb * a.H * 2) + kEntStage;
   const size_t fixed = std::max(copier, plan_lds_bytes(d.E, d.K, n));
   // LDS for nr row blocks per gate/up workgroup (their scales grow with nr)
   auto lds_for = [&](int nr) {
-    return std::max(fixed, lean_head(a) + gemv_stage(wtype, mb, a.H, nr * g.rows_per_block, 2));
+    return std::max(fixed, lean_head(a) + gemv_stage(wtype, mb, a.H, nr * g.rows_per_block, 2) + kEntStage);
   };
   // Row blocks per gate/up workgroup: the fewest that leave every workgroup of
   // the launch resident at once (a second dispatch round would start its
@@ -1802,12 +1837,35 @@ void launch_step_a(int wtype, int32_t* blk, const int32_t* ids, int n, const Dim
 }
 
 void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int P, const uint8_t* host_rows,
-                   size_t stride, size_t copy_bytes, hipStream_t s) {
+                   size_t stride, size_t copy_bytes, const void* up_src, void* up_dst, size_t up_bytes,
+                   hipStream_t s) {
   const int mb = pick_mb(max_m);
   const GemvGeom g = gate_up_geom(wtype, a);
-  const size_t lds = std::max(kStreamScaleLds + (size_t)mb * a.H * 2, gemv_stage(wtype, mb, a.H, g.rows_per_block, 2));
-  const int blocks = P + g.gx * hit_items;
-  PE_DISPATCH(wtype, mb, (wave_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(a, g, P, host_rows, stride, copy_bytes)));
+  const size_t copier = kStreamScaleLds + al16((size_t)mb * a.H * 2) + kEntStage;
+  auto lds_for = [&](int nr) {
+    return std::max(copier, gemv_stage(wtype, mb, a.H, nr * g.rows_per_block, 2) + kEntStage);
+  };
+  // Row blocks per gate/up workgroup: the fewest that leave every workgroup of
+  // the launch resident at once, as in launch_step_a.
+  auto resident_at = [&](int nr) {
+    int r = 0;
+    PE_DISPATCH(wtype, mb, (r = resident_blocks(reinterpret_cast<const void*>(&wave_a_kernel<F_, M_>), lds_for(nr))));
+    return r;
+  };
+  const int extra = up_bytes ? 1 : 0;
+  int nr = 1;
+  if (hit_items > 0) {
+    if (resident_at(1) <= 0) {
+      nr = 2;
+    } else {
+      while (nr < g.gx && P + extra + ceil_div(g.gx, nr) * hit_items > resident_at(nr)) ++nr;
+    }
+  }
+  const size_t lds = lds_for(nr);
+  const int blocks = P + ceil_div(g.gx, nr) * hit_items + extra;
+  PE_DISPATCH(wtype, mb, (wave_a_kernel<F_, M_><<<blocks, kGemvThreads, lds, s>>>(
+                             a, g, P, nr, host_rows, stride, copy_bytes, static_cast<const uint4*>(up_src),
+                             static_cast<uint4*>(up_dst), up_bytes)));
 }
 
 void launch_down_sum(int wtype, const ExpertArgs& a, int max_m, uint16_t* out, int32_t* flip, hipStream_t s) {
@@ -2286,17 +2344,24 @@ void launch_reset_lru(int32_t* blocks, size_t layer_words, int l0, int l1, const
 
 // ------------------------------------------------------------------ host-planned step: read-back
 
+// Every thread makes its own stores visible to the host (system-scope fence)
+// before the barrier, so once thread 0 has published `seq` the host can read
+// everything the workgroup wrote.
 __global__ __launch_bounds__(256) void gather_state_kernel(const int32_t* __restrict__ blk, int state_words,
                                                            const int32_t* __restrict__ ids, int n,
                                                            int32_t* __restrict__ host_blk,
-                                                           int32_t* __restrict__ host_ids) {
+                                                           int32_t* __restrict__ host_ids, uint32_t* flag,
+                                                           uint32_t seq) {
   for (int i = threadIdx.x; i < state_words; i += blockDim.x) host_blk[i] = blk[i];
   for (int i = threadIdx.x; i < n; i += blockDim.x) host_ids[i] = ids[i];
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 void launch_gather_state(const int32_t* blk, int state_words, const int32_t* ids, int n, int32_t* host_blk,
-                         int32_t* host_ids, hipStream_t s) {
-  gather_state_kernel<<<1, 256, 0, s>>>(blk, state_words, ids, n, host_blk, host_ids);
+                         int32_t* host_ids, uint32_t* flag, uint32_t seq, hipStream_t s) {
+  gather_state_kernel<<<1, 256, 0, s>>>(blk, state_words, ids, n, host_blk, host_ids, flag, seq);
 }
 
 // ------------------------------------------------------------------ plan log

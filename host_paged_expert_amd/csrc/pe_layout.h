@@ -133,7 +133,7 @@ struct WorkLayout {
   size_t used_off;      // [E+1]
   size_t gemv_u;        // [E]          used experts on the GEMV kernels, per wave
   size_t gemv_desc;     // [E][4]       the same GEMV items as {slot, first sorted position,
-                        //              entry count, used-expert index}, 16-byte aligned
+                        //              entry count, expert id}, 16-byte aligned
   size_t tile_u;        // [max_tiles]  MFMA tiles: used expert
   size_t tile_row;      // [max_tiles]  MFMA tiles: first row inside the expert
   size_t entries;       // [max_entries] entry index t*k+j at each sorted position

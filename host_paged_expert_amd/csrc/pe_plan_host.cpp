@@ -121,7 +121,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
         if (was_hit[e] != (pass == 0)) continue;
         if (cnt[e] < d.mfma_min) {
           int32_t* dsc = gemv_desc + 4 * (size_t)ng;
-          dsc[0] = used_slot[uu]; dsc[1] = used_off[uu]; dsc[2] = cnt[e]; dsc[3] = uu;
+          dsc[0] = used_slot[uu]; dsc[1] = used_off[uu]; dsc[2] = cnt[e]; dsc[3] = e;
           gemv_u[ng++] = uu;
           max_gemv = std::max(max_gemv, cnt[e]);
         } else {
