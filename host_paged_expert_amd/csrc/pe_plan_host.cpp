@@ -1,11 +1,11 @@
 // Host wave planner of libpe: the multi-wave step of one layer.
 //
-// SGLang "Paged Experts" docs page, "A step: waves, page-in, merge", steps 1-2:
-// the distinct experts a step routes to are split into waves of at most K,
-// already-resident experts first; each wave makes its experts resident,
-// evicting the least recently used experts outside the wave, and copies only
-// the missing ones.  "Captured decode": steps that do not fit one wave are
-// planned on the host, sharing the LRU state with device-planned steps.
+// SGLang "Paged Experts" docs page, "A step: waves, page-in, merge", steps 1-2,
+// and "Captured decode" (which steps the host plans, and that it shares the
+// layer's LRU state with the device planner).  For one step of one layer: the
+// routed experts are grouped into waves of at most K, those holding a slot
+// first; per wave, each expert without a slot takes the slot of an expert the
+// wave does not use, least recently used first, and only those are copied in.
 //
 // Readings where the page is silent (the device planner makes the same ones):
 // resident-first order with ascending ids inside each part; waves are

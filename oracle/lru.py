@@ -1,12 +1,14 @@
 """Per-layer LRU / wave simulator.  TEST INFRASTRUCTURE (oracle).
 
-Follows steps 1-2 of "A step: waves, page-in, merge" on the SGLang Paged
-Experts docs page: the distinct experts a step routes to are split into
-waves of at most K, already-resident experts first; each wave makes its
-experts resident, evicting the least recently used experts outside the wave,
-and copies only the missing ones.  Each MoE layer has its own K-slot table
-("The K-slot table and the host store"); captured and uncaptured steps share
-one LRU state ("Captured decode").
+Implements steps 1-2 of "A step: waves, page-in, merge" on the SGLang Paged
+Experts docs page.  Given the experts one forward step of one layer routes
+to, it forms groups ("waves") of at most K of them, the ones already holding
+a slot placed first; before a wave runs, every expert of the wave that holds
+no slot is given one, taken from an expert the wave does not use, the one
+whose last use lies furthest back first; only those experts are copied from
+the host.  There is one K-slot table per MoE layer ("The K-slot table and the
+host store"), and one LRU state per layer whether the step was captured or
+not ("Captured decode").
 
 Readings where the page is silent:
 - distinct experts are ordered resident-first, each part by ascending id;
