@@ -389,8 +389,9 @@ int pe_create(const pe_config* cfg, pe_ctx** out) {
   c->layer_words = c->ll.total + c->wl.total;     // both multiples of 64 words
   c->o = pe::make_offsets(c->ll, c->wl);
   blob_layout(g.wtype, g.hidden, g.inter, &c->b);
-  // The MFMA kernels stage K in blocks of 128 and tile weight rows by 64.
-  c->mfma_min = (g.hidden % 128 == 0 && g.inter % 128 == 0) ? pe::kMfmaMinTokens : pe::kNoMfma;
+  // The MFMA kernels stage K in blocks of 64 (bf16, MXFP4) or 128 (scaled formats).
+  const int mm = pe::mfma_multiple(g.wtype);
+  c->mfma_min = (g.hidden % mm == 0 && g.inter % mm == 0) ? pe::kMfmaMinTokens : pe::kNoMfma;
   c->d.mfma_min = c->mfma_min;
   c->pl = pe::make_plan_log_layout(c->d, c->ll);
   c->log_cap = plan_log ? g.plan_log_steps : 0;

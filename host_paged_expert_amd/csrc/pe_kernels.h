@@ -99,9 +99,12 @@ void launch_wave_a(int wtype, const ExpertArgs& a, int hit_items, int max_m, int
                    hipStream_t s);
 
 // MFMA grouped-GEMM expert kernels for the tiles of one wave (experts with many
-// tokens).  Need H and I multiples of 128.
+// tokens).  Need H and I multiples of mfma_multiple(wtype): 64 for bf16 and
+// MXFP4 (32x32 MFMA kernels, K staged 64 wide), 128 for the block- and
+// group-scaled formats (one scale per 128-wide K block).
 void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);
 void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s);
+int mfma_multiple(int wtype);
 
 // out[t] = bf16(sum_j merged[t,j]) over valid entries, j in order; if `flip` is
 // set, it toggles that word (the layer's current LRU-state copy).

@@ -2280,25 +2280,270 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
     }
 }
 
+// ---- 32x32 MFMA kernels for the formats without per-block scales (bf16, MXFP4)
+//
+// v_mfma_f32_32x32x16_bf16 does twice the multiply-adds of the 16x16x32 form
+// for the same two 16-byte operand reads per lane, and every wavefront here
+// covers all 128 token rows of the tile against 32 (gate/up: 32 gate and the
+// matching 32 up rows) or 64 (down) weight rows, so each staged K block feeds
+// 8 MFMAs per 6 LDS operand reads.  K is staged 64 wide (rows padded to 72
+// bf16: conflict-free 16-byte reads), so any H and I that are multiples of 64
+// take these kernels (gpt-oss-20b's 2880 included); weight rows past the
+// matrix are zero-filled and their outputs dropped.  Operand layout of the
+// 32x32x16 form: lane l holds A[m = l % 32][k = 8 (l / 32) .. +8] and
+// B[k = 8 (l / 32) .. +8][n = l % 32]; result register i of lane l is
+// D[m = 8 (i / 4) + 4 (l / 32) + i % 4][n = l % 32].  The next K block is loaded
+// into registers while the current one's MFMAs run.
+namespace {
+constexpr int kKB2 = 64;
+constexpr int kRow2 = kKB2 + 8;
+constexpr int kNG2 = 128;        // gate/up: intermediate rows per block (32 per wavefront)
+constexpr int kND2 = 256;        // down: output rows per block (64 per wavefront)
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+template <int FMT> constexpr int kCpr2 = kKB2 / Fmt<FMT>::VPC;    // 16-byte chunks per row per K block
+}  // namespace
+
+template <int FMT>
+constexpr bool kMfma32 = FMT == PE_W_BF16 || FMT == PE_W_MXFP4_B32;
+
+// Chunks q of one K block of weight rows [row0, row0 + NR) (rows >= nrows
+// zero): thread-strided, chunk i = threadIdx.x + q * 256 is row i / CPR,
+// chunk i % CPR.  MXFP4 takes each chunk's E8M0 scale too.
+template <int FMT, int NR>
+__device__ __forceinline__ void load_w2(uint4 (&v)[NR * kCpr2<FMT> / kMfmaThreads], float (&sc)[NR * kCpr2<FMT> / kMfmaThreads],
+                                        const uint8_t* __restrict__ W, const uint8_t* __restrict__ S, int C,
+                                        int row0, int nrows, int kb) {
+  constexpr int VPC = Fmt<FMT>::VPC, CPR = kCpr2<FMT>, NQ = NR * CPR / kMfmaThreads;
+  const size_t row_chunks = (size_t)(C / VPC);
+  const uint4* base = reinterpret_cast<const uint4*>(W);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int i = threadIdx.x + q * kMfmaThreads;
+    const int r = i / CPR, c = i - r * CPR;
+    const bool ok = row0 + r < nrows;
+    v[q] = ok ? base[(size_t)(row0 + r) * row_chunks + (size_t)kb * CPR + c] : make_uint4(0, 0, 0, 0);
+    sc[q] = 1.0f;
+    if constexpr (FMT == PE_W_MXFP4_B32)
+      if (ok) sc[q] = chunk_scale<FMT>(nullptr, S + row_scale_off<FMT>(row0 + r, C), (kb * CPR + c) * VPC);
+  }
+}
+
+template <int FMT, int NR>
+__device__ __forceinline__ void store_w2(const uint4 (&v)[NR * kCpr2<FMT> / kMfmaThreads],
+                                         const float (&sc)[NR * kCpr2<FMT> / kMfmaThreads], uint16_t* sB) {
+  constexpr int VPC = Fmt<FMT>::VPC, CPR = kCpr2<FMT>, NQ = NR * CPR / kMfmaThreads;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int i = threadIdx.x + q * kMfmaThreads;
+    const int r = i / CPR, c = i - r * CPR;
+    decode_chunk_to_lds<FMT>(v[q], sB + r * kRow2 + c * VPC, sc[q]);
+  }
+}
+
+// Gate/up + SwiGLU: one token tile x 128 intermediate rows (the item mfma_item
+// gives this workgroup); wavefront wv takes rows n0 + 32 wv .. + 32.
+template <int FMT>
+__global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_gate_up_kernel(ExpertArgs a) {
+  __shared__ __align__(16) uint16_t sA[kTileM * kRow2];
+  __shared__ __align__(16) uint16_t sG[kNG2 * kRow2];
+  __shared__ __align__(16) uint16_t sU[kNG2 * kRow2];
+  __shared__ int sTok[kTileM];
+  constexpr int NQ = kNG2 * kCpr2<FMT> / kMfmaThreads;
+  constexpr int AQ = kTileM * (kKB2 / 8) / kMfmaThreads;
+  const int32_t* hdr = a.work + a.o.hdr;
+  int t0, t1;
+  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
+  int tile_idx, nblk;
+  mfma_item(tile_idx, nblk);
+  const int tile = t0 + tile_idx;
+  if (tile >= t1) return;
+  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
+  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
+  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  const int H = a.H, I = a.I;
+  const int n0 = nblk * kNG2;
+  const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
+  const uint8_t* W13 = blob + a.off_w13;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  if (threadIdx.x < kTileM)
+    sTok[threadIdx.x] = (int)threadIdx.x < rows ? a.work[a.o.entries + off + row0 + threadIdx.x] / a.k : -1;
+  f32x16_t accg[4], accu[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { accg[mb][i] = 0.f; accu[mb][i] = 0.f; }
+  uint4 va[AQ], vg[NQ], vu[NQ];
+  float sg_[NQ], su_[NQ];
+  __syncthreads();     // sTok
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB2 / 8), c = i - r * (kKB2 / 8);
+      const int tok = sTok[r];
+      va[q] = tok >= 0 ? reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + kb * kKB2)[c] : make_uint4(0, 0, 0, 0);
+    }
+    // gate rows [n0, n0 + 128) of the first I rows, up rows I + [n0, n0 + 128)
+    load_w2<FMT, kNG2>(vg, sg_, W13, blob + a.off_s13, H, n0, I, kb);
+    load_w2<FMT, kNG2>(vu, su_, W13 + (size_t)I * (H / Fmt<FMT>::VPC) * 16, blob + a.off_s13 + row_scale_off<FMT>(I, H),
+                       H, n0, I, kb);
+  };
+  const int nK = H / kKB2;
+  load_block(0);
+  for (int kb = 0; kb < nK; ++kb) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB2 / 8), c = i - r * (kKB2 / 8);
+      *reinterpret_cast<uint4*>(sA + r * kRow2 + c * 8) = va[q];
+    }
+    store_w2<FMT, kNG2>(vg, sg_, sG);
+    store_w2<FMT, kNG2>(vu, su_, sU);
+    __syncthreads();
+    if (kb + 1 < nK) load_block(kb + 1);
+#pragma unroll
+    for (int ks = 0; ks < kKB2 / 16; ++ks) {
+      const int kc = ks * 16 + 8 * lh;
+      const bf16x8_t bg = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sG + (32 * wv + l32) * kRow2 + kc));
+      const bf16x8_t bu = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sU + (32 * wv + l32) * kRow2 + kc));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (32 * mb + l32) * kRow2 + kc));
+        accg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bg, accg[mb], 0, 0, 0);
+        accu[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bu, accu[mb], 0, 0, 0);
+      }
+    }
+  }
+  const int ncol = n0 + 32 * wv + l32;     // this lane's intermediate row
+  if (ncol >= I) return;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * mb + 8 * (i / 4) + 4 * lh + (i % 4);
+      if (r < rows) a.h[(size_t)(off + row0 + r) * I + ncol] = f32_to_bf16(silu_f(accg[mb][i]) * accu[mb][i]);
+    }
+}
+
+// Down projection x router weight: one token tile x 256 output rows; wavefront
+// wv takes rows n0 + 64 wv .. + 64 (two 32-row MFMA blocks).
+template <int FMT>
+__global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_down_kernel(ExpertArgs a) {
+  __shared__ __align__(16) uint16_t sA[kTileM * kRow2];
+  __shared__ __align__(16) uint16_t sB[kND2 * kRow2];
+  constexpr int NQ = kND2 * kCpr2<FMT> / kMfmaThreads;
+  constexpr int AQ = kTileM * (kKB2 / 8) / kMfmaThreads;
+  const int32_t* hdr = a.work + a.o.hdr;
+  int t0, t1;
+  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
+  int tile_idx, nblk;
+  mfma_item(tile_idx, nblk);
+  const int tile = t0 + tile_idx;
+  if (tile >= t1) return;
+  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
+  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
+  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  const int H = a.H, I = a.I;
+  const int n0 = nblk * kND2;
+  const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+  uint4 va[AQ], vb[NQ];
+  float sb_[NQ];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB2 / 8), c = i - r * (kKB2 / 8);
+      va[q] = r < rows ? reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB2)[c]
+                       : make_uint4(0, 0, 0, 0);
+    }
+    load_w2<FMT, kND2>(vb, sb_, blob + a.off_w2, blob + a.off_s2, I, n0, H, kb);
+  };
+  const int nK = I / kKB2;
+  load_block(0);
+  for (int kb = 0; kb < nK; ++kb) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int i = threadIdx.x + q * kMfmaThreads;
+      const int r = i / (kKB2 / 8), c = i - r * (kKB2 / 8);
+      *reinterpret_cast<uint4*>(sA + r * kRow2 + c * 8) = va[q];
+    }
+    store_w2<FMT, kND2>(vb, sb_, sB);
+    __syncthreads();
+    if (kb + 1 < nK) load_block(kb + 1);
+#pragma unroll
+    for (int ks = 0; ks < kKB2 / 16; ++ks) {
+      const int kc = ks * 16 + 8 * lh;
+      bf16x8_t bv[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bv[nb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sB + (64 * wv + 32 * nb + l32) * kRow2 + kc));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + (32 * mb + l32) * kRow2 + kc));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+  }
+  const int32_t* ent = a.work + a.o.entries + off + row0;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int ncol = n0 + 64 * wv + 32 * nb + l32;
+    if (ncol >= H) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mb + 8 * (i / 4) + 4 * lh + (i % 4);
+        if (r < rows) {
+          const int e = ent[r];
+          a.merged[(size_t)e * H + ncol] = a.topk_w[e] * acc[mb][nb][i];
+        }
+      }
+  }
+}
+
 void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) {
   if (tiles <= 0) return;
+  if (wtype == PE_W_BF16 || wtype == PE_W_MXFP4_B32) {
+    const dim3 grid(ceil_div(a.I, kNG2), tiles);
+    if (wtype == PE_W_BF16) mfma32_gate_up_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
+    else mfma32_gate_up_kernel<PE_W_MXFP4_B32><<<grid, kMfmaThreads, 0, s>>>(a);
+    return;
+  }
   dim3 grid(a.I / kNT, tiles);
-  if (wtype == PE_W_BF16) mfma_gate_up_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
-  else if (wtype == PE_W_FP8_B128) mfma_gate_up_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
+  if (wtype == PE_W_FP8_B128) mfma_gate_up_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_INT8_G128) mfma_gate_up_kernel<PE_W_INT8_G128><<<grid, kMfmaThreads, 0, s>>>(a);
-  else if (wtype == PE_W_MXFP4_B32) mfma_gate_up_kernel<PE_W_MXFP4_B32><<<grid, kMfmaThreads, 0, s>>>(a);
   else mfma_gate_up_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
 }
 
 void launch_mfma_down(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) {
   if (tiles <= 0) return;
+  if (wtype == PE_W_BF16 || wtype == PE_W_MXFP4_B32) {
+    const dim3 grid(ceil_div(a.H, kND2), tiles);
+    if (wtype == PE_W_BF16) mfma32_down_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
+    else mfma32_down_kernel<PE_W_MXFP4_B32><<<grid, kMfmaThreads, 0, s>>>(a);
+    return;
+  }
   dim3 grid(a.H / kNT, tiles);
-  if (wtype == PE_W_BF16) mfma_down_kernel<PE_W_BF16><<<grid, kMfmaThreads, 0, s>>>(a);
-  else if (wtype == PE_W_FP8_B128) mfma_down_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
+  if (wtype == PE_W_FP8_B128) mfma_down_kernel<PE_W_FP8_B128><<<grid, kMfmaThreads, 0, s>>>(a);
   else if (wtype == PE_W_INT8_G128) mfma_down_kernel<PE_W_INT8_G128><<<grid, kMfmaThreads, 0, s>>>(a);
-  else if (wtype == PE_W_MXFP4_B32) mfma_down_kernel<PE_W_MXFP4_B32><<<grid, kMfmaThreads, 0, s>>>(a);
   else mfma_down_kernel<PE_W_INT4_G128><<<grid, kMfmaThreads, 0, s>>>(a);
 }
+
+int mfma_multiple(int wtype) { return wtype == PE_W_BF16 || wtype == PE_W_MXFP4_B32 ? kKB2 : kKB; }
 
 // ------------------------------------------------------------------ top-k sum
 

@@ -134,3 +134,37 @@ def test_device_planned_step_with_a_many_token_expert(wtype):
     torch.cuda.synchronize()
     assert np.array_equal(harness.bf16_bits(out), got_dev)
     m.close()
+
+
+@pytest.mark.parametrize("wtype,H,I", [("bf16", 320, 192), ("mxfp4", 320, 448)])
+def test_prefill_mfma_at_multiples_of_64(wtype, H, I):
+    """bf16 and MXFP4 take the 32x32 MFMA kernels whenever H and I are multiples
+    of 64: K is staged 64 wide, and the last block of weight rows lies partly
+    outside the matrix (gate/up blocks of 128 rows: I = 192 is 128 + 64; down
+    blocks of 256 rows: H = 320 is 256 + 64)."""
+    wl = synth.workload("prefill_bf16_k92", layers=2, experts=16, top_k=4, resident=6, hidden=H, inter=I,
+                        wtype=wtype, prefill_tokens=100, steps=3)
+    print("case prefill %s H=%d I=%d" % (wtype, H, I), flush=True)
+    r = synth.routing_for(wl)
+    counts = np.bincount(r["prefill_ids"][0].ravel(), minlength=16)
+    assert counts.max() >= 16
+    (p_out, d_out), st = _prefill_run(wl)
+    (u_out, ud_out), _ = _prefill_run(wl, flags=pe.PE_FLAG_UNPAGED, check=False)
+    assert np.array_equal(p_out, u_out) and np.array_equal(d_out, ud_out)
+
+
+def test_prefill_mxfp4_gpt_oss_expert_shape():
+    """MXFP4 at gpt-oss-20b's expert shape (H = I = 2880, 32 experts, top-4): a
+    256-token chunk, host-planned in waves of K = 16, whose experts (about 32
+    entries each) take the MFMA kernels (2880 = 45 K blocks of 64; weight-row
+    blocks end partly outside the matrix), then decode steps; against the
+    oracle, the simulator and an unpaged run."""
+    wl = synth.workload("prefill_bf16_k92", layers=1, experts=32, top_k=4, resident=16, hidden=2880, inter=2880,
+                        wtype="mxfp4", prefill_tokens=256, steps=2)
+    print("case prefill mxfp4 2880", flush=True)
+    r = synth.routing_for(wl)
+    assert np.bincount(r["prefill_ids"][0].ravel(), minlength=32).max() >= 16
+    (p_out, d_out), st = _prefill_run(wl)
+    assert st["waves"] >= 2 + wl.steps
+    (u_out, ud_out), _ = _prefill_run(wl, flags=pe.PE_FLAG_UNPAGED, check=False)
+    assert np.array_equal(p_out, u_out) and np.array_equal(d_out, ud_out)
