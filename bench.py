@@ -78,6 +78,10 @@ def parse():
     ap.add_argument("--warm-prefill", action="store_true",
                     help="prefill workloads: also time the chunk with every expert resident (K = E, no page-in), "
                          "which exposes the MFMA expert kernels")
+    ap.add_argument("--others", default=None,
+                    help="comma-separated workloads measured after the main one, each on a window of "
+                         "min(steps, 128) steps with its own oracle check (default: the other configs when "
+                         "--workload is not given, none otherwise)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="profiling: first run one plain device-to-device copy of this many MiB, "
                          "a known-size kernel to scale memory counters by")
@@ -342,7 +346,165 @@ def main():
         del m, runner
         torch.cuda.empty_cache()
         result["prefill_warm"] = warm_prefill(wl, xp, idsp, wp, outp, stream)
+    others = others_for(args, sys.argv[1:])
+    if others:
+        m = runner = xp = idsp = wp = outp = x_all = ids_all = w_all = out = None
+        torch.cuda.empty_cache()
+        result["other_workloads"] = [other_workload(n, min(steps, 128), warmup, link) for n in others]
     print(json.dumps(result), flush=True)
+
+
+# Workloads the default run measures after the main one (the other configs of
+# the paged-MoE layer), each on a short window with its own oracle check.
+OTHER_WORKLOADS = ("decode_fp8_k40_b4", "decode_int4_k26_b4", "decode_int8_k40_b4", "decode_mxfp4_k16_b1",
+                   "prefill_bf16_k92")
+
+
+def others_for(args, argv):
+    """The workloads to measure after the main one: `--others` if given, else
+    OTHER_WORKLOADS when `--workload` was not given (none otherwise, so a run
+    aimed at one workload, a profile for instance, covers that one only); the
+    DMA variant measures the main workload only."""
+    if args.dma:
+        return []
+    names = args.others
+    if names is None:
+        explicit = any(a == "--workload" or a.startswith("--workload=") for a in argv)
+        names = "" if explicit else ",".join(OTHER_WORKLOADS)
+    return [n for n in names.split(",") if n and n != args.workload]
+
+
+def other_workload(name, steps, warmup, link):
+    """One more workload on a window of `steps` decode steps from an empty slot
+    table (after `warmup` untimed steps; prefill workloads time their cold
+    chunk first and then the continuation), one repetition, the path roofline
+    of the same window, and the same run's checks: page-in, distinct and wave
+    counts against the LRU simulator, and outputs of the first and last layer
+    at the first and last step (for prefill also three rows of the chunk)
+    against the fp32 unpaged oracle."""
+    import numpy as np
+    import torch
+
+    import harness
+    import synth
+    import host_paged_expert_amd as pe
+    from oracle import formats, moe
+    from oracle.lru import LayerLRU
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    warmup = max(0, min(warmup, steps))
+    wl = synth.workload(name, steps=steps)
+    t0 = time.time()
+    m = harness.make_moe(wl)
+    harness.load_store(m, wl)
+    log("%s: context loaded in %.1fs" % (name, time.time() - t0))
+    routing = synth.routing_for(wl)
+    x, ids, w = harness.decode_inputs(wl, routing, dev)
+    L, B, H = wl.layers, wl.batch, wl.hidden
+    out = torch.empty((L, B, H), dtype=torch.bfloat16, device=dev)
+    runner = harness.DecodeRunner(m, wl, x, ids, w, out, stream)
+    prefill = wl.routing == "prefill_zipf"
+    if prefill:
+        Tp = wl.prefill_tokens
+        xp = torch.from_numpy(synth.hidden_states(wl, -1, Tp).view(np.int16)).view(torch.bfloat16).to(dev)
+        idsp = torch.from_numpy(np.ascontiguousarray(routing["prefill_ids"])).to(dev)
+        wp = torch.from_numpy(np.ascontiguousarray(routing["prefill_w"])).to(dev)
+        outp = torch.empty((L, Tp, H), dtype=torch.bfloat16, device=dev)
+
+    def cold():
+        torch.cuda.synchronize()
+        m.reset_lru(-1, stream)
+        runner.rewind()
+        torch.cuda.synchronize()
+        m.reset_stats()
+
+    def chunk():
+        for l in range(L):
+            m.forward(l, xp, idsp[l], wp[l], outp[l], stream=stream)
+
+    cold()
+    if prefill:
+        chunk()
+    runner.run(warmup)
+    cold()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    if prefill:
+        chunk()
+    ev[1].record(stream)
+    got = {}
+    for s in range(steps):
+        runner.run(1)
+        if s in (0, steps - 1):
+            got[s] = out.clone()
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    st = m.stats()
+    chunk_ms, ms = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    got = {s: harness.bf16_bits(v) for s, v in got.items()}
+    got_p = harness.bf16_bits(outp) if prefill else None
+    captured = runner.captured
+    del runner
+    m.close()
+
+    S_alg, _ = pe.pe_expert_bytes(wl.wtype, H, wl.inter)
+    misses = distinct = waves = 0
+    for l in range(L):
+        sim = LayerLRU(wl.experts, wl.resident)
+        step_ids = ([routing["prefill_ids"][l].ravel()] if prefill else []) + \
+                   [routing["decode_ids"][s, l].ravel() for s in range(steps)]
+        for v in step_ids:
+            wv = sim.step(v)
+            misses += sum(u.count for u in wv)
+            waves += len(wv)
+            distinct += len(set(v.tolist()))
+    counts_ok = (misses, distinct, waves) == (st["page_ins"], st["distinct"], st["waves"])
+    # the outputs' sample (copied out after the step that made them, outside the window's timing)
+    worst = 0.0
+    for l in sorted({0, L - 1}):
+        canon = {}
+
+        def expert(e):
+            if e not in canon:
+                canon[e] = formats.dequant_expert(wl.wtype, *synth.expert_tensors(wl, l, e))
+            return canon[e]
+        for s in sorted(got):
+            xs = formats.bf16_to_f32(synth.hidden_states(wl, s, B))
+            ref = moe.moe_layer(xs, routing["decode_ids"][s, l], routing["decode_w"][s, l], expert)
+            g = harness.bf16_to_f32(got[s][l])
+            worst = max(worst, float(np.abs(g - ref).max() / np.abs(ref).max()))
+        if prefill:
+            rows = [0, Tp // 2, Tp - 1]
+            xr = formats.bf16_to_f32(synth.hidden_states(wl, -1, Tp))[rows]
+            ref = moe.moe_layer(xr, routing["prefill_ids"][l][rows], routing["prefill_w"][l][rows], expert)
+            g = harness.bf16_to_f32(got_p[l])[rows]
+            worst = max(worst, float(np.abs(g - ref).max() / np.abs(ref).max()))
+    tol = {"bf16": 1e-2, "fp8": 1e-2, "int4": 2e-2, "int8": 1e-2, "mxfp4": 1e-2}[wl.wtype]
+    # the decode window's roofline: its share of distinct experts and page-ins
+    # (the prefill chunk's are counted apart)
+    Dd, Md = distinct, misses
+    res = {"workload": name, "path": "captured" if captured else "host-planned", "steps": steps,
+           "warmup": warmup, "dtype": DTYPES[wl.wtype], "batch": B, "resident": wl.resident}
+    if prefill:
+        sim_p = [LayerLRU(wl.experts, wl.resident) for _ in range(L)]
+        Dp = sum(len(set(routing["prefill_ids"][l].ravel().tolist())) for l in range(L))
+        Mp = sum(sum(u.count for u in sim_p[l].step(routing["prefill_ids"][l].ravel())) for l in range(L))
+        roof_p = Dp * S_alg / (HBM_PEAK_GBS * 1e9) + Mp * S_alg / (link * 1e9)
+        res["prefill"] = {"tokens": Tp, "ms": round(chunk_ms, 2), "tok_s": round(Tp / (chunk_ms / 1e3), 1),
+                          "roof_ms": round(roof_p * 1e3, 2), "frac": round(roof_p * 1e3 / chunk_ms, 4)}
+        Dd, Md = distinct - Dp, misses - Mp
+    t_roof = Dd * S_alg / (HBM_PEAK_GBS * 1e9) + Md * S_alg / (link * 1e9)
+    value = steps * B / (ms / 1e3)
+    res.update({"value": round(value, 3), "unit": "tok/s", "ms_per_step": round(ms / steps, 4),
+                "roof_tok_s": round(steps * B / t_roof, 2), "frac": round(value / (steps * B / t_roof), 4),
+                "sample_parity": {"max_rel_err": worst, "tol": tol, "counts_match_simulator": counts_ok,
+                                  "ok": bool(counts_ok and worst <= tol)}})
+    log("%s (%s): %.1f tok/s, %.3f of its path roofline%s, parity %s" % (
+        name, res["path"], value, res["frac"],
+        (", prefill chunk %.1f ms (%.3f)" % (chunk_ms, res["prefill"]["frac"])) if prefill else "",
+        "ok" if res["sample_parity"]["ok"] else "FAILED"))
+    return res
 
 
 MFMA_BF16_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s

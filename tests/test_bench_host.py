@@ -89,3 +89,23 @@ def test_committed_traffic_applies_only_to_the_sources_it_was_taken_on(tmp_path,
     t["source_sha256_16"] = "0" * 16
     (tmp_path / "profiles" / "traffic_w.json").write_text(json.dumps(t))
     assert bench.traffic_for("step_a_kernel", "w", 1000.0) is None
+
+
+def test_other_workloads_run_only_when_no_workload_is_named(monkeypatch):
+    def args_of(argv):
+        monkeypatch.setattr("sys.argv", ["bench.py"] + argv)
+        return bench.parse()
+    default = bench.others_for(args_of([]), [])
+    assert default == [n for n in bench.OTHER_WORKLOADS]
+    assert "decode_bf16_k40_b1" not in default
+    argv = ["--workload", "decode_fp8_k40_b4"]
+    assert bench.others_for(args_of(argv), argv) == []
+    argv = ["--workload=decode_bf16_k40_b1", "--steps", "16"]
+    assert bench.others_for(args_of(argv), argv) == []
+    argv = ["--others", "decode_int4_k26_b4,decode_bf16_k40_b1"]
+    assert bench.others_for(args_of(argv), argv) == ["decode_int4_k26_b4"]
+    argv = ["--dma"]
+    assert bench.others_for(args_of(argv), argv) == []
+    synth = pytest.importorskip("synth")
+    for n in bench.OTHER_WORKLOADS:
+        assert n in synth.WORKLOADS
