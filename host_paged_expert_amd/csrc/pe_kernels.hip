@@ -1921,6 +1921,22 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 }  // namespace
 
+// Entry index and router weight of each row of a down tile, staged in LDS
+// (`s_ent`, `s_w`: kTileM words each, over the last K block's operands) for
+// the epilogue, which would otherwise load both, one after the other, for
+// every output element it stores.
+__device__ __forceinline__ void stage_tile_entries(const ExpertArgs& a, const int32_t* __restrict__ ent, int rows,
+                                                   int* s_ent, float* s_w) {
+  __syncthreads();     // every wavefront is done with the operands in this LDS area
+  if ((int)threadIdx.x < kTileM) {
+    const int r = threadIdx.x;
+    const int e = r < rows ? ent[r] : 0;
+    s_ent[r] = e;
+    s_w[r] = r < rows ? a.topk_w[e] : 0.f;
+  }
+  __syncthreads();
+}
+
 // The (tile, column block) item of this workgroup.  Workgroups are dispatched
 // round-robin over the 8 XCDs (each with its own L2) in linear block order; the
 // items are given out so that every XCD takes a contiguous run of them, tile by
@@ -2267,16 +2283,15 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[h][i] = __builtin_fmaf(sc, p[h][i], acc[h][i]);
   }
-  const int32_t* ent = a.work + a.o.entries + off + row0;
+  int* s_ent = reinterpret_cast<int*>(sA);
+  float* s_w = reinterpret_cast<float*>(sA) + kTileM;
+  stage_tile_entries(a, a.work + a.o.entries + off + row0, rows, s_ent, s_w);
 #pragma unroll
   for (int h = 0; h < kMH; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * h + 4 * lk + i;
-      if (r < rows) {
-        const int e = ent[r];
-        a.merged[(size_t)e * H + ncol] = a.topk_w[e] * acc[h][i];
-      }
+      if (r < rows) a.merged[(size_t)s_ent[r] * H + ncol] = s_w[r] * acc[h][i];
     }
 }
 
@@ -2497,22 +2512,23 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_down_kernel(ExpertArgs
       }
     }
   }
-  const int32_t* ent = a.work + a.o.entries + off + row0;
+  int* s_ent = reinterpret_cast<int*>(sA);
+  float* s_w = reinterpret_cast<float*>(sA) + kTileM;
+  stage_tile_entries(a, a.work + a.o.entries + off + row0, rows, s_ent, s_w);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int ncol = n0 + 64 * wv + 32 * nb + l32;
-    if (ncol >= H) continue;
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * mb + 8 * (i / 4) + 4 * lh + (i % 4);
+      if (r >= rows) continue;
+      float* dst = a.merged + (size_t)s_ent[r] * H;
+      const float wr = s_w[r];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 32 * mb + 8 * (i / 4) + 4 * lh + (i % 4);
-        if (r < rows) {
-          const int e = ent[r];
-          a.merged[(size_t)e * H + ncol] = a.topk_w[e] * acc[mb][nb][i];
-        }
+      for (int nb = 0; nb < 2; ++nb) {
+        const int ncol = n0 + 64 * wv + 32 * nb + l32;
+        if (ncol < H) dst[ncol] = wr * acc[mb][nb][i];
       }
-  }
+    }
 }
 
 void launch_mfma_gate_up(int wtype, const ExpertArgs& a, int tiles, hipStream_t s) {
