@@ -1218,6 +1218,9 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
   const int32_t* ent = it.ent;
   for (int tb = 0; tb < it.m; tb += MB) {
     const int mb = min(MB, it.m - tb);
+    // lane lig stores token lig of the batch: its entry now, its router weight
+    // once the entry has arrived (both in flight during the dot products)
+    const int e_l = lig < mb ? ent[tb + lig] : 0;
     uint4 w0[kMaxChunksInFlight], w1[kMaxChunksInFlight];
     if (act0) load_row(r0, n_ch, lig, LG, w0);
     if (act1) load_row(r1, n_ch, lig, LG, w1);
@@ -1231,6 +1234,7 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
         [=](int i) { return i < hw ? reinterpret_cast<uint4*>(hs) + i : reinterpret_cast<uint4*>(s_sc) + (i - hw); });
     __syncthreads();
     if (!act0) continue;
+    const float w_l = lig < mb ? a.topk_w[e_l] : 0.0f;
     float y0[MB], y1[MB];
 #pragma unroll
     for (int t = 0; t < MB; ++t) { y0[t] = 0.0f; y1[t] = 0.0f; }
@@ -1249,9 +1253,8 @@ __device__ void down_block(const ExpertArgs& a, int bx, int by, int LG, int rows
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
       if (t < mb && lig == t) {
-        const int e = ent[tb + t];
-        a.merged[(size_t)e * H + n0] = a.topk_w[e] * y0[t];
-        if (act1) a.merged[(size_t)e * H + n0 + 1] = a.topk_w[e] * y1[t];
+        a.merged[(size_t)e_l * H + n0] = w_l * y0[t];
+        if (act1) a.merged[(size_t)e_l * H + n0 + 1] = w_l * y1[t];
       }
     }
   }
