@@ -258,12 +258,24 @@ struct StageTimer {
   }
 };
 
+// A host-planned wave's GEMV and MFMA ranges in the work lists (first, first
+// paged-in, end), which its launches then take as arguments instead of
+// reading the work arena's header.
+struct WaveRanges { int g0, gsplit, g1, t0, tsplit, t1; };
+
 // Expert kernels (gate/up then down; GEMV items, then MFMA tiles) of one part
 // of one wave.  `items`/`tiles` bound the launches' grids; `max_m` bounds the
-// GEMV experts' token counts.
+// GEMV experts' token counts; `wr`, if given, are the wave's ranges.
+void set_ranges(pe::ExpertArgs& a, const WaveRanges& wr) {
+  a.hdr_known = 1;
+  a.g0 = wr.g0; a.gsplit = wr.gsplit; a.g1 = wr.g1;
+  a.t0 = wr.t0; a.tsplit = wr.tsplit; a.t1 = wr.t1;
+}
+
 void run_experts(pe_ctx* c, const Act& act, bool tm_on, int layer, int wave, int part, const void* x,
-                 const float* w, int items, int max_m, int tiles, hipStream_t s) {
+                 const float* w, int items, int max_m, int tiles, hipStream_t s, const WaveRanges* wr = nullptr) {
   pe::ExpertArgs a = expert_args(c, act, layer, wave, x, w, part);
+  if (wr) set_ranges(a, *wr);
   if (items > 0) {
     {
       StageTimer tm(c, PE_STAGE_GATE_UP, s, tm_on);
@@ -678,29 +690,28 @@ int forward_impl(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, c
     pe::launch_copy(blk, mirror_dev, up_bytes, grid, s);
   }
   bool summed = false;     // the top-k sum already ran with the last down projection
+  WaveRanges wr{0, 0, 0, 0, 0, 0};
   for (int w = 0; w < sm.n_waves; ++w) {
     const int cnt = mirror[c->ll.plan_count + w];
     const int g_all = sm.gemv_items[w], g_hit = sm.gemv_hits[w];
     const int t_all = sm.tiles[w], t_hit = sm.tile_hits[w];
+    wr.g0 = wr.g1; wr.gsplit = wr.g0 + g_hit; wr.g1 = wr.g0 + g_all;
+    wr.t0 = wr.t1; wr.tsplit = wr.t0 + t_hit; wr.t1 = wr.t0 + t_all;
     if (!c->unpaged && !dma && t_all == 0) {
       // GEMV experts only: one launch pages in the missing experts with their
       // gate/up projection fused in while the resident ones run theirs, then
       // one launch runs the wave's down projection.
       pe::ExpertArgs a = expert_args(c, act, layer, w, x, topk_w, 1);
+      set_ranges(a, wr);
       const bool up = fold && w == 0;
-      if (up) {
-        a.work = mirror_dev + c->ll.total;
-        a.hdr_known = 1;
-        a.g0 = 0;
-        a.gsplit = g_hit;
-        a.g1 = g_all;
-      }
+      if (up) a.work = mirror_dev + c->ll.total;
       {
         StageTimer tm(c, PE_STAGE_PAGE_IN, s, tm_on);
         pe::launch_wave_a(c->cfg.wtype, a, g_hit, sm.max_gemv_tokens, kStreamWgs, host_l, c->b.stride,
                           c->b.copied, up ? mirror_dev : nullptr, up ? blk : nullptr, up ? up_bytes : 0, s);
       }
       a = expert_args(c, act, layer, w, x, topk_w, 0);     // device work lists from here on
+      set_ranges(a, wr);
       StageTimer tm(c, PE_STAGE_DOWN, s, tm_on);
       if (sm.n_waves == 1 && mfma_min == pe::kNoMfma && down_sum_fits(n)) {
         // one wave of few tokens: its down projection and the top-k sum in one
@@ -720,7 +731,7 @@ int forward_impl(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, c
     if (fork) {
       PE_HIP(hipEventRecord(c->ev_fork, s));
       PE_HIP(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-      run_experts(c, act, tm_on, layer, w, 1, x, topk_w, g_hit, sm.max_gemv_tokens, t_hit, c->side);
+      run_experts(c, act, tm_on, layer, w, 1, x, topk_w, g_hit, sm.max_gemv_tokens, t_hit, c->side, &wr);
       PE_HIP(hipEventRecord(c->ev_join, c->side));
     }
     if (!c->unpaged && cnt > 0) {
@@ -737,10 +748,10 @@ int forward_impl(pe_ctx* c, int layer, const void* x, const int32_t* topk_ids, c
       }
     }
     if (fork) {
-      run_experts(c, act, tm_on, layer, w, 2, x, topk_w, g_all - g_hit, sm.max_gemv_tokens, t_all - t_hit, s);
+      run_experts(c, act, tm_on, layer, w, 2, x, topk_w, g_all - g_hit, sm.max_gemv_tokens, t_all - t_hit, s, &wr);
       PE_HIP(hipStreamWaitEvent(s, c->ev_join, 0));    // before the next wave may evict these slots
     } else {
-      run_experts(c, act, tm_on, layer, w, 0, x, topk_w, g_all, sm.max_gemv_tokens, t_all, s);
+      run_experts(c, act, tm_on, layer, w, 0, x, topk_w, g_all, sm.max_gemv_tokens, t_all, s, &wr);
     }
   }
   if (!summed) {

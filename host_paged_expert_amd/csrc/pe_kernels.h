@@ -11,7 +11,7 @@ struct Offsets {
   int tick, slot_expert, expert_slot, last_use;   // inside a state copy
   int cur, state0, state_stride;                  // current copy, copies
   int n_waves, plan_count, plan_expert, plan_slot, plan_evicted, slot_of;
-  int hdr, used_expert, used_slot, used_off, gemv_u, gemv_desc, tile_u, tile_row, entries;
+  int hdr, used_expert, used_slot, used_off, gemv_u, gemv_desc, tile_desc, entries;
 };
 
 Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl);
@@ -38,9 +38,10 @@ struct ExpertArgs {
   // published work lists, so it can run alongside the planning + page-in kernel.
   int lean;
   // hdr_known = 1: this launch's GEMV ranges of the wave (start, end of the
-  // experts resident before the wave, end) are g0 / gsplit / g1 instead of the
-  // work arena's header (which may be in host memory)
-  int hdr_known, g0, gsplit, g1;
+  // experts resident before the wave, end) are g0 / gsplit / g1 and its MFMA
+  // tile ranges t0 / tsplit / t1, instead of the work arena's header (which
+  // may be in host memory, or one dependent load away)
+  int hdr_known, g0, gsplit, g1, t0, tsplit, t1;
   int mfma_min;
   const int32_t* ids;         // [T*k] routed ids
   int T, E;

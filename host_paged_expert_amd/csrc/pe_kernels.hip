@@ -35,8 +35,7 @@ Offsets make_offsets(const LayerLayout& ll, const WorkLayout& wl) {
   o.plan_evicted = (int)ll.plan_evicted; o.slot_of = (int)ll.slot_of;
   o.hdr = (int)wl.hdr; o.used_expert = (int)wl.used_expert; o.used_slot = (int)wl.used_slot;
   o.used_off = (int)wl.used_off; o.gemv_u = (int)wl.gemv_u; o.gemv_desc = (int)wl.gemv_desc;
-  o.tile_u = (int)wl.tile_u;
-  o.tile_row = (int)wl.tile_row; o.entries = (int)wl.entries;
+  o.tile_desc = (int)wl.tile_desc; o.entries = (int)wl.entries;
   return o;
 }
 
@@ -379,8 +378,7 @@ __device__ int plan_page_in_block(const PlanArgs& p, int block, int ncopy, char*
     int32_t* used_slot = work + o.used_slot;
     int32_t* used_off = work + o.used_off;
     int32_t* gemv_u = work + o.gemv_u;
-    int32_t* tile_u = work + o.tile_u;
-    int32_t* tile_row = work + o.tile_row;
+    int4* tile_desc = reinterpret_cast<int4*>(work + o.tile_desc);
     for (int e = tid; e < E; e += kPlanThreads) {
       int c = s_cnt[e];
       if (c == 0) continue;
@@ -398,7 +396,8 @@ __device__ int plan_page_in_block(const PlanArgs& p, int block, int ncopy, char*
         reinterpret_cast<int4*>(work + o.gemv_desc)[g] = make_int4(j, s_pref(2, e), c, e);
       } else {
         int t0 = miss ? t_hit + s_pref(6, e) : s_pref(5, e);
-        for (int q = 0; q * kTileM < c; ++q) { tile_u[t0 + q] = u; tile_row[t0 + q] = q * kTileM; }
+        for (int q = 0; q * kTileM < c; ++q)
+          tile_desc[t0 + q] = make_int4(j, s_pref(2, e) + q * kTileM, min(kTileM, c - q * kTileM), e);
       }
     }
     __syncthreads();
@@ -1618,7 +1617,7 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, int
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_w + al16(4 * (size_t)n) / 4);           // [n][I]
   const int32_t* hdr = a.work + a.o.hdr;
   const int4* desc = reinterpret_cast<const int4*>(a.work + a.o.gemv_desc);
-  const int n_items = hdr[hdr_gemv(a.MW, 1)];               // wave 0's GEMV items start at 0
+  const int n_items = a.hdr_known ? a.g1 : hdr[hdr_gemv(a.MW, 1)];     // wave 0's GEMV items start at 0
   const int n0 = r0 + 2 * gr;
   const bool act0 = n0 < H, act1 = n0 + 1 < H;
   // this lane group's experts i, i + NW GE, i + 2 NW GE, ... (i = wv GE + ge):
@@ -1957,6 +1956,24 @@ __device__ __forceinline__ void mfma_item(int& tile_idx, int& nblk) {
   nblk = q - tile_idx * nb;
 }
 
+// The descriptor of the wave's tile_idx-th MFMA tile of this launch's part
+// (all, resident before the wave's page-in, or paged in by it): {slot, first
+// sorted position, rows, expert id}.  False past the part's last tile.
+__device__ __forceinline__ bool mfma_tile(const ExpertArgs& a, int tile_idx, int4& td) {
+  int t0, t1;
+  if (a.hdr_known) {
+    part_range(a, a.t0, a.tsplit, a.t1, t0, t1);
+  } else {
+    const int32_t* hdr = a.work + a.o.hdr;
+    part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0,
+               t1);
+  }
+  const int tile = t0 + tile_idx;
+  if (tile >= t1) return false;
+  td = reinterpret_cast<const int4*>(a.work + a.o.tile_desc)[tile];
+  return true;
+}
+
 // Decode one 16-byte chunk of weights of format FMT into bf16 in LDS at `dst`
 // (VPC values); returns nothing, writes VPC/8 16-byte LDS words.  `sc` (MXFP4
 // only) is the chunk's block scale, applied here.
@@ -2075,16 +2092,11 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
   __shared__ __align__(16) uint16_t sG[kNT * kLdsRow];
   __shared__ __align__(16) uint16_t sU[kNT * kLdsRow];
   __shared__ int sTok[kTileM];
-  const int32_t* hdr = a.work + a.o.hdr;
-  int t0, t1;
-  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
   int tile_idx, nblk;
   mfma_item(tile_idx, nblk);
-  const int tile = t0 + tile_idx;
-  if (tile >= t1) return;
-  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
-  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
-  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  int4 td;
+  if (!mfma_tile(a, tile_idx, td)) return;
+  const int slot = td.x, pos = td.y, rows = td.z;     // the tile's sorted positions pos .. pos + rows - 1
   const int H = a.H, I = a.I;
   const int n0 = nblk * kNT;
   const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
@@ -2094,7 +2106,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ln = lane & 15, lk = lane >> 4;
   if (threadIdx.x < kTileM)
-    sTok[threadIdx.x] = threadIdx.x < rows ? a.work[a.o.entries + off + row0 + threadIdx.x] / a.k : -1;
+    sTok[threadIdx.x] = threadIdx.x < rows ? a.work[a.o.entries + pos + threadIdx.x] / a.k : -1;
   f32x4_t accg[kMH], accu[kMH];
 #pragma unroll
   for (int h = 0; h < kMH; ++h)
@@ -2189,7 +2201,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_gate_up_kernel(ExpertArgs a
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * h + 4 * lk + i;
       if (r < rows)
-        a.h[(size_t)(off + row0 + r) * I + ncol] = f32_to_bf16(silu_f(accg[h][i]) * accu[h][i]);
+        a.h[(size_t)(pos + r) * I + ncol] = f32_to_bf16(silu_f(accg[h][i]) * accu[h][i]);
     }
 }
 
@@ -2199,16 +2211,11 @@ template <int FMT>
 __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
   __shared__ __align__(16) uint16_t sA[kTileM * kLdsRow];
   __shared__ __align__(16) uint16_t sB[kNT * kLdsRow];
-  const int32_t* hdr = a.work + a.o.hdr;
-  int t0, t1;
-  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
   int tile_idx, nblk;
   mfma_item(tile_idx, nblk);
-  const int tile = t0 + tile_idx;
-  if (tile >= t1) return;
-  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
-  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
-  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  int4 td;
+  if (!mfma_tile(a, tile_idx, td)) return;
+  const int slot = td.x, pos = td.y, rows = td.z;     // the tile's sorted positions pos .. pos + rows - 1
   const int H = a.H, I = a.I;
   const int n0 = nblk * kNT;
   const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
@@ -2232,7 +2239,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
     for (int q = 0; q < kAPer; ++q) {
       const int i = threadIdx.x + q * kMfmaThreads;
       const int r = i / (kKB / 8), c = i - r * (kKB / 8);
-      va[q] = r < rows ? reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB)[c]
+      va[q] = r < rows ? reinterpret_cast<const uint4*>(a.h + (size_t)(pos + r) * I + kb * kKB)[c]
                        : make_uint4(0, 0, 0, 0);
     }
     load_weights<FMT>(vb, sb_, W2, blob + a.off_s2, I, n0, kb);
@@ -2288,7 +2295,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_down_kernel(ExpertArgs a) {
   }
   int* s_ent = reinterpret_cast<int*>(sA);
   float* s_w = reinterpret_cast<float*>(sA) + kTileM;
-  stage_tile_entries(a, a.work + a.o.entries + off + row0, rows, s_ent, s_w);
+  stage_tile_entries(a, a.work + a.o.entries + pos, rows, s_ent, s_w);
 #pragma unroll
   for (int h = 0; h < kMH; ++h)
 #pragma unroll
@@ -2368,16 +2375,11 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_gate_up_kernel(ExpertA
   __shared__ int sTok[kTileM];
   constexpr int NQ = kNG2 * kCpr2<FMT> / kMfmaThreads;
   constexpr int AQ = kTileM * (kKB2 / 8) / kMfmaThreads;
-  const int32_t* hdr = a.work + a.o.hdr;
-  int t0, t1;
-  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
   int tile_idx, nblk;
   mfma_item(tile_idx, nblk);
-  const int tile = t0 + tile_idx;
-  if (tile >= t1) return;
-  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
-  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
-  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  int4 td;
+  if (!mfma_tile(a, tile_idx, td)) return;
+  const int slot = td.x, pos = td.y, rows = td.z;     // the tile's sorted positions pos .. pos + rows - 1
   const int H = a.H, I = a.I;
   const int n0 = nblk * kNG2;
   const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
@@ -2385,7 +2387,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_gate_up_kernel(ExpertA
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
   if (threadIdx.x < kTileM)
-    sTok[threadIdx.x] = (int)threadIdx.x < rows ? a.work[a.o.entries + off + row0 + threadIdx.x] / a.k : -1;
+    sTok[threadIdx.x] = (int)threadIdx.x < rows ? a.work[a.o.entries + pos + threadIdx.x] / a.k : -1;
   f32x16_t accg[4], accu[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -2441,7 +2443,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_gate_up_kernel(ExpertA
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * mb + 8 * (i / 4) + 4 * lh + (i % 4);
-      if (r < rows) a.h[(size_t)(off + row0 + r) * I + ncol] = f32_to_bf16(silu_f(accg[mb][i]) * accu[mb][i]);
+      if (r < rows) a.h[(size_t)(pos + r) * I + ncol] = f32_to_bf16(silu_f(accg[mb][i]) * accu[mb][i]);
     }
 }
 
@@ -2453,16 +2455,11 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_down_kernel(ExpertArgs
   __shared__ __align__(16) uint16_t sB[kND2 * kRow2];
   constexpr int NQ = kND2 * kCpr2<FMT> / kMfmaThreads;
   constexpr int AQ = kTileM * (kKB2 / 8) / kMfmaThreads;
-  const int32_t* hdr = a.work + a.o.hdr;
-  int t0, t1;
-  part_range(a, hdr[hdr_tile(a.MW, a.wave)], hdr[hdr_tile_split(a.MW, a.wave)], hdr[hdr_tile(a.MW, a.wave + 1)], t0, t1);
   int tile_idx, nblk;
   mfma_item(tile_idx, nblk);
-  const int tile = t0 + tile_idx;
-  if (tile >= t1) return;
-  const int u = a.work[a.o.tile_u + tile], row0 = a.work[a.o.tile_row + tile];
-  const int slot = a.work[a.o.used_slot + u], off = a.work[a.o.used_off + u];
-  const int rows = min(kTileM, a.work[a.o.used_off + u + 1] - off - row0);
+  int4 td;
+  if (!mfma_tile(a, tile_idx, td)) return;
+  const int slot = td.x, pos = td.y, rows = td.z;     // the tile's sorted positions pos .. pos + rows - 1
   const int H = a.H, I = a.I;
   const int n0 = nblk * kND2;
   const uint8_t* blob = a.slots + (size_t)slot * a.slot_stride;
@@ -2482,7 +2479,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_down_kernel(ExpertArgs
     for (int q = 0; q < AQ; ++q) {
       const int i = threadIdx.x + q * kMfmaThreads;
       const int r = i / (kKB2 / 8), c = i - r * (kKB2 / 8);
-      va[q] = r < rows ? reinterpret_cast<const uint4*>(a.h + (size_t)(off + row0 + r) * I + kb * kKB2)[c]
+      va[q] = r < rows ? reinterpret_cast<const uint4*>(a.h + (size_t)(pos + r) * I + kb * kKB2)[c]
                        : make_uint4(0, 0, 0, 0);
     }
     load_w2<FMT, kND2>(vb, sb_, blob + a.off_w2, blob + a.off_s2, I, n0, H, kb);
@@ -2517,7 +2514,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void mfma32_down_kernel(ExpertArgs
   }
   int* s_ent = reinterpret_cast<int*>(sA);
   float* s_w = reinterpret_cast<float*>(sA) + kTileM;
-  stage_tile_entries(a, a.work + a.o.entries + off + row0, rows, s_ent, s_w);
+  stage_tile_entries(a, a.work + a.o.entries + pos, rows, s_ent, s_w);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll

@@ -134,8 +134,8 @@ struct WorkLayout {
   size_t gemv_u;        // [E]          used experts on the GEMV kernels, per wave
   size_t gemv_desc;     // [E][4]       the same GEMV items as {slot, first sorted position,
                         //              entry count, expert id}, 16-byte aligned
-  size_t tile_u;        // [max_tiles]  MFMA tiles: used expert
-  size_t tile_row;      // [max_tiles]  MFMA tiles: first row inside the expert
+  size_t tile_desc;     // [max_tiles][4] MFMA tiles as {slot, first sorted position, rows (<= kTileM),
+                        //              expert id}, 16-byte aligned
   size_t entries;       // [max_entries] entry index t*k+j at each sorted position
   size_t total;
 };
@@ -163,8 +163,7 @@ inline WorkLayout make_work_layout(const Dims& d) {
   w.gemv_u = o; o += d.E;
   o = (o + 3) / 4 * 4;
   w.gemv_desc = o; o += 4 * (size_t)d.E;
-  w.tile_u = o; o += d.max_tiles;
-  w.tile_row = o; o += d.max_tiles;
+  w.tile_desc = o; o += 4 * (size_t)d.max_tiles;
   w.entries = o; o += d.max_entries;
   w.total = (o + 63) / 64 * 64;
   return w;

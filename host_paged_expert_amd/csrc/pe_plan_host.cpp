@@ -32,17 +32,29 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
   uint32_t* last_use = reinterpret_cast<uint32_t*>(st + ll.last_use);
   int32_t* slot_of = blk + ll.slot_of;
 
-  // scratch kept per thread: a host-planned step runs on the caller's thread
-  thread_local std::vector<int> cnt, order, u_of, in_wave, seen, wave;
-  thread_local std::vector<std::pair<uint32_t, int>> cand;
-  thread_local std::vector<char> hit, was_hit;
+  // scratch kept per thread (a host-planned step runs on the caller's thread),
+  // reached once through references: the per-entry loops then touch plain arrays
+  struct Scratch {
+    std::vector<int> cnt, order, u_of, in_wave, seen, wave;
+    std::vector<std::pair<uint32_t, int>> cand;
+    std::vector<char> hit, was_hit;
+  };
+  thread_local Scratch tls;
+  Scratch& sc = tls;
+  std::vector<int>&cnt = sc.cnt, &order = sc.order, &u_of = sc.u_of, &in_wave = sc.in_wave, &seen = sc.seen,
+  &wave = sc.wave;
+  std::vector<std::pair<uint32_t, int>>& cand = sc.cand;
+  std::vector<char>&hit = sc.hit, &was_hit = sc.was_hit;
   cnt.assign(E, 0);
   int bad = 0, valid = 0;
-  for (int i = 0; i < n_entries; ++i) {
-    int e = ids[i];
-    if (e < 0 || e >= E) { ++bad; continue; }
-    ++cnt[e];
-    ++valid;
+  {
+    int* c = cnt.data();
+    for (int i = 0; i < n_entries; ++i) {
+      const int e = ids[i];
+      if ((unsigned)e >= (unsigned)E) { ++bad; continue; }
+      ++c[e];
+    }
+    valid = n_entries - bad;
   }
   order.clear();
   for (int e = 0; e < E; ++e) if (cnt[e] && expert_slot[e] >= 0) order.push_back(e);
@@ -57,8 +69,7 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
   int32_t* used_off = work + wl.used_off;
   int32_t* gemv_u = work + wl.gemv_u;
   int32_t* gemv_desc = work + wl.gemv_desc;
-  int32_t* tile_u = work + wl.tile_u;
-  int32_t* tile_row = work + wl.tile_row;
+  int32_t* tile_desc = work + wl.tile_desc;
   int32_t* entries = work + wl.entries;
 
   u_of.assign(E, -1);
@@ -125,7 +136,10 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
           gemv_u[ng++] = uu;
           max_gemv = std::max(max_gemv, cnt[e]);
         } else {
-          for (int q = 0; q < cnt[e]; q += kTileM) { tile_u[nt] = uu; tile_row[nt] = q; ++nt; }
+          for (int q = 0; q < cnt[e]; q += kTileM) {
+            int32_t* td = tile_desc + 4 * (size_t)nt++;
+            td[0] = used_slot[uu]; td[1] = used_off[uu] + q; td[2] = std::min(kTileM, cnt[e] - q); td[3] = e;
+          }
         }
       }
       if (pass == 0) {
@@ -142,14 +156,23 @@ int host_plan_step(const Dims& d, const LayerLayout& ll, const WorkLayout& wl,
     sum->tiles[w] = nt - t0;
   }
   used_off[u] = off;
-  // entries in ascending index at their expert's positions; slot map at wave time
-  seen.assign(E, 0);
-  for (int i = 0; i < n_entries; ++i) {
-    int e = ids[i];
-    if (e < 0 || e >= E) { slot_of[i] = -1; continue; }
-    int uu = u_of[e];
-    entries[used_off[uu] + seen[e]++] = i;
-    slot_of[i] = used_slot[uu];
+  // entries in ascending index at their expert's positions; slot map at wave
+  // time (per expert: its next free position and its slot, looked up once)
+  seen.assign(2 * (size_t)E, 0);
+  {
+    int* next = seen.data();          // [E] next sorted position of expert e
+    int* slot = seen.data() + E;      // [E] its slot
+    for (int e = 0; e < E; ++e) {
+      if (cnt[e] == 0) continue;
+      next[e] = used_off[u_of[e]];
+      slot[e] = used_slot[u_of[e]];
+    }
+    for (int i = 0; i < n_entries; ++i) {
+      const int e = ids[i];
+      if ((unsigned)e >= (unsigned)E) { slot_of[i] = -1; continue; }
+      entries[next[e]++] = i;
+      slot_of[i] = slot[e];
+    }
   }
   st[ll.tick] = (int32_t)tick;
   blk[ll.n_waves] = n_waves;
