@@ -50,8 +50,8 @@ WORKLOADS = {
     "decode_int8_k40_b4": Workload("decode_int8_k40_b4", 48, 128, 8, 40, 2048, 768, "int8", 4, 512,
                                    "persist_zipf", 0.7, 1.0),
     # MXFP4 experts in the shape of the blog's gpt-oss-20b runs: 24 MoE layers, 32
-    # experts, top-4, hidden and expert intermediate 2880 (not a multiple of 128,
-    # so every expert takes the GEMV kernels); K=16, batch 1.
+    # experts, top-4, hidden and expert intermediate 2880; K=16, batch 1 (every
+    # expert has one entry a step and takes the GEMV kernels).
     "decode_mxfp4_k16_b1": Workload("decode_mxfp4_k16_b1", 24, 32, 4, 16, 2880, 2880, "mxfp4", 1, 512,
                                     "persist_zipf", 0.7, 1.0),
     # bf16, K=92: a cold 2048-token prefill chunk (Zipf 0.8, 8 distinct ids per token),
