@@ -168,3 +168,51 @@ def test_prefill_mxfp4_gpt_oss_expert_shape():
     assert st["waves"] >= 2 + wl.steps
     (u_out, ud_out), _ = _prefill_run(wl, flags=pe.PE_FLAG_UNPAGED, check=False)
     assert np.array_equal(p_out, u_out) and np.array_equal(d_out, ud_out)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int4"])
+def test_mfma_tile_boundaries(wtype):
+    """Experts whose entry counts sit on the MFMA thresholds and tile edges
+    (15 and 16 entries, 127..129, 255..257, a full 300) in one host-planned step
+    of 300 tokens, over two waves (K below the distinct count): against the
+    oracle row by row, and bit-identical to an unpaged run."""
+    E, k, T, K = 24, 8, 300, 10
+    wl = synth.workload("decode_bf16_k40_b1", wtype=wtype, layers=1, experts=E, top_k=k, resident=K,
+                        hidden=256, inter=256, batch=1, steps=1)
+    counts = {0: 300, 1: 257, 2: 256, 3: 255, 4: 129, 5: 128, 6: 127, 7: 16, 8: 15}
+    rng = np.random.default_rng(7)
+    ids = np.full((T, k), -1, np.int32)
+    fill = np.zeros(T, np.int32)
+    for e, c in counts.items():             # expert e in tokens 0..c-1 (rotated so the tails differ)
+        rows = (np.arange(c) + 53 * e) % T
+        for t in rows:
+            ids[t, fill[t]] = e
+            fill[t] += 1
+    assert fill.max() <= k
+    for t in range(T):                      # the remaining positions from the other experts, no repeats
+        rest = [e for e in rng.permutation(np.arange(9, E)) if e not in ids[t]]
+        for j in range(fill[t], k):
+            ids[t, j] = rest[j - fill[t]]
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    for e, c in counts.items():
+        assert cnt[e] == c, (e, cnt[e], c)
+    x_np = synth.hidden_states(wl, 0, T)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(DEV)
+    outs = {}
+    for flags in (0, pe.PE_FLAG_UNPAGED):
+        print("case tile boundaries %s flags %d" % (wtype, flags), flush=True)
+        m = harness.make_moe(wl, flags=flags, max_tokens=T)
+        harness.load_store(m, wl)
+        out = torch.empty((T, wl.hidden), dtype=torch.bfloat16, device=DEV)
+        m.forward(0, x, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), out)
+        torch.cuda.synchronize()
+        outs[flags] = harness.bf16_bits(out)
+        if not flags:
+            waves = LayerLRU(E, K).step(ids.ravel())
+            assert len(waves) > 1 and m.plan(0, 0)["n_waves"] == len(waves)
+        m.close()
+    assert np.array_equal(outs[0], outs[pe.PE_FLAG_UNPAGED])
+    ref = moe.moe_layer(formats.bf16_to_f32(x_np), ids, w, _expert_fn(wl, 0))
+    _close(outs[0], ref, wtype, "tile boundaries")
