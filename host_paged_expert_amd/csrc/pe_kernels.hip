@@ -913,14 +913,25 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
 
 // Sum over the LG lanes of a group (xor butterfly, partners LG/2, ..., 2, 1;
 // every lane gets the same total).  The masks are uniform, so the branches
-// on them are scalar.
-template <int MB>
+// on them are scalar.  ROLL keeps the loop over the partners rolled (the same
+// operations in the same order), for callers whose registers an unrolled
+// butterfly would push into scratch.
+template <int MB, bool ROLL = false>
 __device__ __forceinline__ void group_reduce(float (&acc)[MB], int LG) {
+  if constexpr (ROLL) {
+#pragma unroll 1
+    for (int off = 32; off > 0; off >>= 1) {
+      if (off >= LG) continue;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    if (off >= LG) continue;
+      for (int t = 0; t < MB; ++t) acc[t] += lane_xor(acc[t], off);
+    }
+  } else {
 #pragma unroll
-    for (int t = 0; t < MB; ++t) acc[t] += lane_xor(acc[t], off);
+    for (int off = 32; off > 0; off >>= 1) {
+      if (off >= LG) continue;
+#pragma unroll
+      for (int t = 0; t < MB; ++t) acc[t] += lane_xor(acc[t], off);
+    }
   }
 }
 
@@ -1541,7 +1552,7 @@ __device__ __forceinline__ void fetch_down_rows(const ExpertArgs& a, const uint8
 // both staged in LDS).  `r` holds the first round of loads of token batch 0.
 // Per lane the chunks run in ascending order and the group reduces by the xor
 // butterfly, as in down_block.
-template <int FMT, int MB>
+template <int FMT, int MB, bool ROLL>
 __device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 dsc, DownRows& r, int n0,
                                                bool act0, bool act1, int lig, int LG, int n_ch,
                                                const uint16_t* hbase, float* s_y, int RB, int r0,
@@ -1570,8 +1581,8 @@ __device__ __forceinline__ void down_rows_item(const ExpertArgs& a, const int4 d
         fetch_down_rows<FMT>(a, blob, n0, act0, act1, c0 + LG * kMaxChunksInFlight, LG, n_ch, r);
       }
     }
-    group_reduce<MB>(y0, LG);
-    group_reduce<MB>(y1, LG);
+    group_reduce<MB, ROLL>(y0, LG);
+    group_reduce<MB, ROLL>(y1, LG);
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
       if (t < mb && lig == t && act0) {
@@ -1647,15 +1658,19 @@ __global__ __launch_bounds__(512) void down_sum_kernel(ExpertArgs a, int LG, int
   }
   __syncthreads();
   const uint16_t* hbase = STAGE ? s_h : a.h;
+  // int4 and MXFP4 dot products with eight tokens per item, or with h read
+  // from global memory, leave no registers for an unrolled butterfly (it
+  // spilled 0.3-0.4 KB per lane); bf16 and FP8 are faster unrolled
+  constexpr bool kRollReduce = (FMT == PE_W_INT4_G128 || FMT == PE_W_MXFP4_B32) && (MB >= 8 || !STAGE);
   while (i0 < n_items) {
-    down_rows_item<FMT, MB>(a, d0, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0, s_ent, s_w);
+    down_rows_item<FMT, MB, kRollReduce>(a, d0, rA, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0, s_ent, s_w);
     i0 += 2 * step;
     if (i0 < n_items) {
       d0 = desc[i0];
       fetch_down_rows<FMT>(a, a.slots + (size_t)d0.x * a.slot_stride, n0, act0, act1, lig, LG, n_ch, rA);
     }
     if (i1 >= n_items) break;
-    down_rows_item<FMT, MB>(a, d1, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0, s_ent, s_w);
+    down_rows_item<FMT, MB, kRollReduce>(a, d1, rB, n0, act0, act1, lig, LG, n_ch, hbase, s_y, RB, r0, s_ent, s_w);
     i1 += 2 * step;
     if (i1 < n_items) {
       d1 = desc[i1];
