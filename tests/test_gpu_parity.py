@@ -333,6 +333,66 @@ def test_expert_with_more_entries_than_a_token_batch(wtype):
         assert np.array_equal(outs[(0, ci)], outs[(pe.PE_FLAG_UNPAGED, ci)]), ci
 
 
+@pytest.mark.parametrize("wtype", ["int4", "mxfp4", "fp8", "int8"])
+def test_one_wave_host_step_with_h_outside_lds(wtype):
+    """One-wave host-planned steps (60 entries > K = 12 over at most 10 distinct
+    experts) whose h does not fit in LDS (60 x 1024 bf16 = 120 KiB), so launch B
+    reads h from global memory, and whose busiest expert has 6 tokens (8-token
+    batches): the launch B variants whose lane-group reduction is a rolled loop
+    (int4, MXFP4) or unrolled (FP8, int8).  Two steps, the first all page-ins,
+    the second 6 hits and 4 page-ins; plans and state against the simulator,
+    outputs against the oracle and bitwise against an unpaged run."""
+    T, k = 15, 4
+    wl = synth.workload("decode_bf16_k40_b1", layers=1, experts=16, top_k=k, resident=12, hidden=256, inter=1024,
+                        wtype=wtype, batch=T, steps=1)
+    print("case one-wave host step, h outside LDS, %s" % wtype, flush=True)
+    rng = np.random.default_rng(11)
+
+    def step_ids(pool, busy):
+        # `busy` in the first 6 tokens, the other k (or k - 1) ids distinct, from `pool`
+        rest = [e for e in pool if e != busy]
+        rows = []
+        for t in range(T):
+            if t < 6:
+                rows.append([busy] + [int(v) for v in rng.choice(rest, size=k - 1, replace=False)])
+            else:
+                rows.append([int(v) for v in rng.choice(rest, size=k, replace=False)])
+        return np.array(rows, np.int32)
+
+    cases = [step_ids(list(range(10)), 3), step_ids(list(range(4, 14)), 7)]
+    for c in cases:
+        assert all(len(set(r.tolist())) == k for r in c) and len(set(c.ravel().tolist())) <= 10
+        assert max(np.bincount(c.ravel())) >= 5
+    ws = [rng.random(c.shape).astype(np.float32) for c in cases]
+    x = torch.from_numpy(synth.hidden_states(wl, 0, T).view(np.int16)).view(torch.bfloat16).to(DEV)
+    xr = formats.bf16_to_f32(harness.bf16_bits(x))
+    outs = {}
+    for flags in (0, pe.PE_FLAG_UNPAGED):
+        m = harness.make_moe(wl, flags=flags)
+        harness.load_store(m, wl)
+        sim = LayerLRU(wl.experts, m.K)
+        want_page_ins = 0
+        for ci, ids_np in enumerate(cases):
+            out = torch.empty((T, wl.hidden), dtype=torch.bfloat16, device=DEV)
+            m.forward(0, x, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(ws[ci]).to(DEV), out)
+            torch.cuda.synchronize()
+            outs[(flags, ci)] = harness.bf16_bits(out)
+            if flags == 0:
+                waves = sim.step(ids_np.ravel())
+                assert len(waves) == 1
+                want_page_ins += waves[0].count
+                _check_plan(m, 0, waves, T, k, ids_np.ravel())
+                _check_state(m, 0, sim)
+                ref = moe.moe_layer(xr, ids_np, ws[ci], _expert_fn(wl, 0), num_experts=wl.experts)
+                _check_close(outs[(flags, ci)], ref, wtype, "case %d" % ci)
+        st = m.stats()
+        if flags == 0:
+            assert st["host_planned"] == 2 and st["page_ins"] == want_page_ins
+        m.close()
+    for ci in range(len(cases)):
+        assert np.array_equal(outs[(0, ci)], outs[(pe.PE_FLAG_UNPAGED, ci)]), ci
+
+
 def test_zero_tokens_is_a_noop():
     wl = synth.workload("tiny_bf16")
     m = harness.make_moe(wl)
