@@ -515,7 +515,10 @@ def warm_prefill(wl, xp, idsp, wp, outp, stream):
     slot e holds expert e, no page-in), so the step is planning, the MFMA (and
     GEMV) expert kernels and the top-k sum.  Each expert kernel is set against
     its own roofline, the larger of its MFMA time at the bf16 peak and its HBM
-    time for the weights it reads once (D experts' gate/up or down weights)."""
+    time for the bytes it must move once: gate/up reads D experts' gate/up
+    weights and the chunk's x and writes h (bf16, one row per entry); down reads
+    D experts' down weights and h and writes the merged fp32 row of every entry
+    that the top-k sum then reads."""
     import torch
 
     import harness
@@ -549,9 +552,12 @@ def warm_prefill(wl, xp, idsp, wp, outp, stream):
     H, I = wl.hidden, wl.inter
     w13, w2, s13, s2 = part_bytes(wl.wtype, H, I)
     ent, D = st["entries"], st["distinct"]
+    x_bytes = L * wl.prefill_tokens * H * 2          # the chunk's x, read once per layer
+    h_bytes = ent * I * 2                            # h: written by gate/up, read by down
+    merged_bytes = ent * H * 4                       # merged fp32 rows written by down
     out = {"ms": round(min(times), 2), "tok_s": round(wl.prefill_tokens / (min(times) / 1e3), 1), "distinct": D}
-    for name, flops, wbytes in (("gate_up", ent * 2.0 * 2 * H * I, D * (w13 + s13)),
-                                ("down", ent * 2.0 * H * I, D * (w2 + s2))):
+    for name, flops, wbytes in (("gate_up", ent * 2.0 * 2 * H * I, D * (w13 + s13) + x_bytes + h_bytes),
+                                ("down", ent * 2.0 * H * I, D * (w2 + s2) + h_bytes + merged_bytes)):
         n, ms = tm[name]
         roof_ms = max(flops / MFMA_BF16_PEAK, wbytes / (HBM_PEAK_GBS * 1e9)) * 1e3
         out[name] = {"launches": n, "ms": round(ms, 3), "tflops": round(flops / (ms / 1e3) / 1e12, 1) if ms else None,
